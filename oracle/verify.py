@@ -1,0 +1,250 @@
+"""Token verification, float64 (oracle side).
+
+Sources (SpecInfer summary, page 1):
+  * "Token Verification: Greedy Decoding (VerifyGreedy)": walk down from the
+    root; while some child v of u carries the LLM's predicted token O(u),
+    append it and move to v; at the first miss append O(u) and stop.
+  * "Token Verification: Stochastic Decoding and Multi-Step Speculative
+    Sampling (VerifyStochastic)": at node u, pick an untested child s uniformly
+    at random, accept it with probability min(1, P_LLM(x_s|u) / P_SSM_s(x_s|u));
+    on rejection replace P_LLM(.|u) by norm(max(0, P_LLM(.|u) - P_SSM_s(.|u)))
+    and drop s from the untested set; once every child is rejected, sample the
+    next token from the current P_LLM(.|u).  The same page's comparison with
+    naive sampling (Theorem 4.3) defines the naive verifier.
+  * Wiki concept page "Speculative decoding", section "Implementation sketch":
+    when the walk ends at a leaf by acceptance, the bonus token comes from the
+    leaf's own target distribution; the normaliser after a rejection can be 0
+    (guard).
+
+Readings where the pages are silent:
+  * target distributions are softmax(logits) at temperature 1;
+  * O(u) is the lowest index among maximal raw fp32 logits; among children
+    with the same token the lowest node index wins;
+  * the random child is the idx-th untested child in ascending node order,
+    idx = (top 24 bits of word 0) * m >> 24; the accept uniform is in (0, 1];
+  * q(x) = 0 gives ratio +inf when p(x) > 0 and 0 otherwise;
+  * a zero normaliser after a rejection leaves the distribution unchanged;
+  * the final sample is the smallest x whose cumulative mass reaches
+    u * sum(p) (falling back to the last x with p(x) > 0 if rounding leaves
+    the total short).
+
+Rows: target_logits[b][0] is the root's context, row 1 + i node i's context.
+Outputs per request: accepted node ids (list), bonus token, number of ratio
+tests ("rounds"), status, and a trace of decision margins used to count near
+ties (|u - ratio| for every ratio test; the distance of u*sum(p) to the two
+cumulative sums bracketing the sampled token for the final sample).
+"""
+import math
+
+import numpy as np
+
+from . import philox
+from .status import ST_OK, ST_BAD_TOKEN, ST_BAD_QROW, ST_NONFINITE
+from .tree import children_of
+
+
+# ----------------------------------------------------------------------------
+# Target distributions
+# ----------------------------------------------------------------------------
+def softmax_row(logits_row):
+    """P_LLM(.|u) = softmax of one fp32 logits row, float64, temperature 1."""
+    l = np.asarray(logits_row, dtype=np.float32).astype(np.float64)
+    m = l.max()
+    e = np.exp(l - m)
+    return e / e.sum()
+
+
+def argmax_row(logits_row):
+    """O(u): the first index of the maximal raw fp32 logit."""
+    return int(np.argmax(np.asarray(logits_row, dtype=np.float32)))
+
+
+def _request_checks(logits_b, token_b, V, q_row_b=None, R=None):
+    """Status of one request after the data checks, in the fixed order:
+    tokens in [0, V), then draft-row indices in [0, R), then finite logits."""
+    if any(not (0 <= int(t) < V) for t in token_b):
+        return ST_BAD_TOKEN
+    if q_row_b is not None and any(not (0 <= int(r) < R) for r in q_row_b):
+        return ST_BAD_QROW
+    if not np.all(np.isfinite(np.asarray(logits_b, dtype=np.float32))):
+        return ST_NONFINITE
+    return ST_OK
+
+
+# ----------------------------------------------------------------------------
+# VerifyGreedy
+# ----------------------------------------------------------------------------
+def verify_greedy_one(parent, token, logits):
+    """Greedy walk for one request (assumes valid inputs).
+
+    Returns (accepted node ids, bonus token)."""
+    accepted = []
+    u = -1
+    while True:
+        o = argmax_row(logits[u + 1])
+        nxt = None
+        for c in children_of(parent, u):
+            if int(token[c]) == o:
+                nxt = c
+                break
+        if nxt is None:
+            return accepted, o
+        accepted.append(nxt)
+        u = nxt
+
+
+def verify_greedy(parent, token, target_logits, status):
+    """Batched VerifyGreedy.  Returns dict of accepted [B][N] (-1 padded),
+    num_accepted [B], bonus [B], status [B]."""
+    B, N = token.shape
+    V = target_logits.shape[2]
+    acc = np.full((B, N), -1, dtype=np.int64)
+    num = np.full(B, -1, dtype=np.int64)
+    bonus = np.full(B, -1, dtype=np.int64)
+    st = [int(s) for s in status]
+    for b in range(B):
+        if st[b] == ST_OK:
+            st[b] = _request_checks(target_logits[b], token[b], V)
+        if st[b] != ST_OK:
+            continue
+        path, bn = verify_greedy_one(parent[b], token[b], target_logits[b])
+        acc[b, : len(path)] = path
+        num[b] = len(path)
+        bonus[b] = bn
+    return dict(accepted=acc, num_accepted=num, bonus=bonus, status=np.array(st))
+
+
+# ----------------------------------------------------------------------------
+# VerifyStochastic: multi-step speculative sampling
+# ----------------------------------------------------------------------------
+def ratio_of(p_x, q_x):
+    """P_LLM(x) / P_SSM(x) with the q(x) = 0 reading."""
+    if q_x > 0.0:
+        return p_x / q_x
+    return math.inf if p_x > 0.0 else 0.0
+
+
+def residual(p_cur, q):
+    """Distribution after rejecting a child proposed from q:
+    norm(max(0, p_cur - q)); unchanged if the normaliser is 0.
+    Returns (new distribution, normaliser)."""
+    r = np.maximum(0.0, p_cur - q)
+    z = r.sum()
+    if z > 0.0:
+        return r / z, z
+    return p_cur, z
+
+
+def sample_from(p_cur, u):
+    """Smallest x with sum_{y<=x} p_cur(y) >= u * sum(p_cur).
+
+    Returns (x, margin), margin = distance of the threshold to the nearer of the
+    two cumulative sums bracketing x, relative to sum(p_cur)."""
+    c = np.cumsum(p_cur)
+    total = c[-1]
+    t = u * total
+    idx = np.nonzero(c >= t)[0]
+    if len(idx):
+        x = int(idx[0])
+    else:
+        x = int(np.nonzero(p_cur > 0)[0][-1])
+    lo = c[x - 1] if x > 0 else 0.0
+    margin = min(abs(t - lo), abs(c[x] - t)) / total if total > 0 else 0.0
+    return x, margin
+
+
+def select_child(untested, word0):
+    """The random untested child: idx-th in ascending node order."""
+    idx = philox.pick_index(word0, len(untested))
+    return untested[idx]
+
+
+def mss_one(b, parent, token, logits, ssm, q_row, seed, offset):
+    """Multi-step speculative sampling for request b (assumes the data checks
+    passed).  Returns (accepted, bonus, rounds, status, trace)."""
+    accepted = []
+    trace = []
+    rounds = 0
+    u = -1
+    p_cur = softmax_row(logits[0])
+    while True:
+        untested = children_of(parent, u)
+        slot = u + 1
+        j = 0
+        moved = False
+        while untested:
+            w = philox.words(seed, offset, b, slot, j)
+            s = select_child(untested, w[0])
+            x = int(token[s])
+            qrow = np.asarray(ssm[q_row[s]], dtype=np.float32).astype(np.float64)
+            q_x = qrow[x]
+            if not math.isfinite(q_x) or q_x < 0.0:
+                return accepted, -1, rounds, ST_NONFINITE, trace
+            ratio = ratio_of(p_cur[x], q_x)
+            u1 = philox.unit_open0(w[1])
+            rounds += 1
+            trace.append(("ratio", abs(u1 - ratio) if math.isfinite(ratio) else math.inf))
+            if u1 <= ratio:
+                accepted.append(s)
+                u = s
+                p_cur = softmax_row(logits[s + 1])
+                moved = True
+                break
+            p_new, z = residual(p_cur, qrow)
+            if not math.isfinite(z):
+                return accepted, -1, rounds, ST_NONFINITE, trace
+            if z == 0.0:
+                trace.append(("zero_residual", 0.0))
+            p_cur = p_new
+            untested = [c for c in untested if c != s]
+            j += 1
+        if moved:
+            continue
+        # every child rejected, or a leaf reached by acceptance
+        w = philox.words(seed, offset, b, slot, 0)
+        x, margin = sample_from(p_cur, philox.unit_open0(w[2]))
+        trace.append(("sample", margin))
+        return accepted, x, rounds, ST_OK, trace
+
+
+def verify_mss(parent, token, target_logits, ssm_probs, q_row, status, seed, offset=0,
+               requests=None):
+    """Batched MSS verification.  Returns dict of accepted [B][N] (-1 padded),
+    num_accepted [B], bonus [B], rounds [B], status [B] and traces (list per
+    request).  `requests` restricts the work to a subset (others stay -1)."""
+    B, N = token.shape
+    V = target_logits.shape[2]
+    R = ssm_probs.shape[1]
+    acc = np.full((B, N), -1, dtype=np.int64)
+    num = np.full(B, -1, dtype=np.int64)
+    bonus = np.full(B, -1, dtype=np.int64)
+    rounds = np.full(B, -1, dtype=np.int64)
+    st = [int(s) for s in status]
+    traces = [[] for _ in range(B)]
+    for b in (range(B) if requests is None else requests):
+        if st[b] == ST_OK:
+            st[b] = _request_checks(target_logits[b], token[b], V, q_row[b], R)
+        if st[b] != ST_OK:
+            continue
+        path, bn, rd, s_b, tr = mss_one(b, parent[b], token[b], target_logits[b], ssm_probs[b],
+                                        q_row[b], seed, offset)
+        traces[b] = tr
+        st[b] = s_b
+        if s_b != ST_OK:
+            continue
+        acc[b, : len(path)] = path
+        num[b] = len(path)
+        bonus[b] = bn
+        rounds[b] = rd
+    return dict(accepted=acc, num_accepted=num, bonus=bonus, rounds=rounds,
+                status=np.array(st), traces=traces)
+
+
+# ----------------------------------------------------------------------------
+# Naive sampling verification (Theorem 4.3's comparator)
+# ----------------------------------------------------------------------------
+def naive_reject_prob(p, child_tokens):
+    """Naive verifier: draw x ~ P_LLM and accept iff x is a child token, so it
+    rejects with probability 1 - (mass of the distinct child tokens)."""
+    toks = sorted(set(int(t) for t in child_tokens))
+    return 1.0 - float(sum(p[t] for t in toks))
