@@ -1,0 +1,221 @@
+"""Benchmark of one tree-verification step on one MI355X.
+
+A step is the whole verification path over one batch of synthetic input:
+tree_build_mask -> tree_attn_verify -> tree_verify_greedy -> tree_verify_mss
+-> kv_commit_accepted.  The default workload is the LLaMA-7B-shaped layer
+(bf16, 8 requests x 32 heads x 128 dims, 1024-token prefixes, a 46-node
+expansion tree <2,2,2,1,1,1,1>, fp32 logits over a 32000-token vocabulary).
+
+Inputs stay resident in HBM.  Because one step's data (~250 MB) would fit in
+the 256 MB Infinity Cache, the timed loop rotates over several copies of the
+inputs whose total exceeds twice that cache, so each step reads from HBM.
+
+Prints ONE JSON line (rank 0, N = 1): throughput in verified tree tokens/s
+(B * N tree nodes per step), the roofline of the dominant kernel (attention,
+HBM-bound) from HIP events recorded on the launch stream, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tree tokens/s + achieved HBM GB/s (% peak), tree_attn + MSS verify"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (2 = LLaMA-7B layer)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU sample time")
+    return ap.parse_args()
+
+
+def attn_bytes(w):
+    """Algorithmic HBM bytes of one tree_attn_verify launch: every prefix and
+    tree K/V row once, Q read once, O written once."""
+    esz = 2 if w.dtype == "bf16" else 4
+    kv = int(np.sum(w.prefix_len.astype(np.int64) + w.N)) * w.H * w.D * esz * 2
+    qo = 2 * w.B * w.N * w.H * w.D * esz
+    return kv + qo
+
+
+def logit_bytes(w):
+    """Algorithmic bytes of one verify call: every target row read once."""
+    return w.B * (w.N + 1) * w.V * 4
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the verification step shards by request with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    import tree_speculative_verification_attn_amd as tv
+    from tests.gpu_util import to_dev
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    w = synth.make_config(args.config)
+    bf = w.dtype == "bf16"
+    B, N, H, D, V, R = w.B, w.N, w.H, w.D, w.V, w.R
+    step_bytes = w.k_cache.nbytes * 2 + w.target_logits.nbytes + w.ssm_probs.nbytes
+    n_copies = max(2, int(np.ceil(2 * MALL_BYTES / max(1, step_bytes))) + 1)
+
+    copies = []
+    for _ in range(n_copies):
+        copies.append(dict(q=to_dev(w.q, bf), k=to_dev(w.k_cache, bf), v=to_dev(w.v_cache, bf),
+                           tl=to_dev(w.target_logits), sp=to_dev(w.ssm_probs)))
+    bt = to_dev(w.block_table)
+    pl0 = to_dev(w.prefix_len)
+    pl = pl0.clone()
+    parent = to_dev(w.parent)
+    token = to_dev(w.token)
+    qr = to_dev(w.q_row)
+    anc = torch.zeros((B, N), dtype=torch.int64, device=dev)
+    child = torch.zeros((B, N + 1), dtype=torch.int64, device=dev)
+    depth = torch.zeros((B, N), dtype=torch.int32, device=dev)
+    status = torch.zeros((B,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(copies[0]["q"])
+    code = tv.TV_BF16 if bf else tv.TV_F32
+    ws_a = tv.tree_attn_verify_workspace(code, B, N, H, D, w.max_blocks)
+    ws_attn = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev) if ws_a else None
+    ws_v = torch.empty(tv.tree_verify_workspace(B, N, V), dtype=torch.uint8, device=dev)
+    g_acc = torch.empty((B, N), dtype=torch.int32, device=dev)
+    g_num = torch.empty((B,), dtype=torch.int32, device=dev)
+    g_bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    m_acc = torch.empty((B, N), dtype=torch.int32, device=dev)
+    m_num = torch.empty((B,), dtype=torch.int32, device=dev)
+    m_bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    m_rounds = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = copies[i % n_copies]
+        pl.copy_(pl0)                                  # the commit of the last step grew it
+        if ev: ev[0].record(stream)
+        tv.tree_build_mask(parent, anc, child, depth, status)
+        if ev: ev[1].record(stream)
+        tv.tree_attn_verify(c["q"], c["k"], c["v"], bt, pl, anc, status, out, ws_attn, scale=w.scale)
+        if ev: ev[2].record(stream)
+        tv.tree_verify_greedy(c["tl"], token, child, status, g_acc, g_num, g_bonus, ws_v)
+        if ev: ev[3].record(stream)
+        tv.tree_verify_mss(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset + i, m_acc,
+                           m_num, m_bonus, m_rounds, ws_v)
+        if ev: ev[4].record(stream)
+        tv.kv_commit_accepted(c["k"], c["v"], bt, pl, m_acc, m_num, status)
+        if ev: ev[5].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    names = ["mask", "attn", "greedy", "mss", "commit"]
+    comp = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
+            for k, n in enumerate(names)}
+    acc_tokens = float(np.mean(np.maximum(m_num.cpu().numpy(), 0) + 1))
+    assert int((status != 0).sum()) == 0, "a request failed during the benchmark"
+
+    a_bytes = attn_bytes(w)
+    l_bytes = logit_bytes(w)
+    attn_gbs = a_bytes / (comp["attn"] * 1e-3) / 1e9
+    mss_gbs = l_bytes / (comp["mss"] * 1e-3) / 1e9
+    value = B * N / (ms_per_step * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified tree tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic (seeded NumPy; page-shaped, no model weights)",
+        "config": {"workload": f"{w.name}: B={B} H={H} D={D} L={int(w.prefix_len.max())} N={N} V={V}",
+                   "tree": str(w.meta.get("tree")), "batch": B, "tree_nodes": N,
+                   "prefix_len": int(w.prefix_len.max()), "vocab": V,
+                   "input_copies_rotated": n_copies},
+        "roofline": {"bound": "hbm", "kernel": "tree_attn_verify", "achieved": round(attn_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": a_bytes},
+        "components_ms": {k: round(v, 5) for k, v in comp.items()},
+        "mss": {"achieved_GBps_on_logit_bytes": round(mss_gbs, 1),
+                "frac": round(mss_gbs / HBM_PEAK_GBS, 4), "logit_bytes": l_bytes,
+                "tree_attn_plus_mss_tokens_per_s": round(B * N / ((comp["attn"] + comp["mss"]) * 1e-3), 1),
+                "mean_tokens_emitted_per_request": round(acc_tokens, 3)},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, value)
+    print(json.dumps(res))
+
+
+def cpu_baseline(w, budget_s, gpu_value):
+    """The float64 oracle on a bounded sample of the same workload, scaled
+    to a whole step: attention is timed on a few (request, head) pairs,
+    verification on a few requests."""
+    import threadpoolctl
+
+    from oracle import attention, commit, tree, verify
+
+    with threadpoolctl.threadpool_limits(1):
+        t = time.perf_counter()
+        anc, child, depth, st = tree.build_mask_batch(w.parent)
+        t_mask = time.perf_counter() - t
+        pairs_done = 0
+        t_attn = 0.0
+        rng = np.random.default_rng(0)
+        while t_attn < budget_s * 0.6 and pairs_done < w.B * w.H:
+            b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
+            t = time.perf_counter()
+            attention.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len, anc, st,
+                                     w.dtype, w.scale, pairs=[(b, h)])
+            t_attn += time.perf_counter() - t
+            pairs_done += 1
+        reqs = 0
+        t_ver = 0.0
+        while t_ver < budget_s * 0.3 and reqs < w.B:
+            t = time.perf_counter()
+            verify.verify_greedy(w.parent[reqs:reqs + 1], w.token[reqs:reqs + 1],
+                                 w.target_logits[reqs:reqs + 1], [0])
+            verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0] * w.B,
+                              w.seed, requests=[reqs])
+            t_ver += time.perf_counter() - t
+            reqs += 1
+    full = (t_mask + t_attn * (w.B * w.H) / pairs_done + t_ver * w.B / reqs)
+    v = w.B * w.N / full
+    return {"value": round(v, 3), "unit": "verified tree tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 NumPy oracle, 1 thread: masks for all {w.B} requests, attention on "
+                      f"{pairs_done} of {w.B * w.H} (request, head) pairs, greedy + MSS on {reqs} of "
+                      f"{w.B} requests; scaled to one full step ({full:.1f} s)",
+            "host_cpus": os.cpu_count(), "gpu_over_cpu": round(gpu_value / v, 1)}
+
+
+if __name__ == "__main__":
+    main()

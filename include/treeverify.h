@@ -1,0 +1,221 @@
+/*
+ * treeverify.h - tree-based speculative verification on AMD MI355X (gfx950).
+ *
+ * One verification step of tree-based speculative inference, as the SpecInfer
+ * paper describes it ("SpecInfer: Accelerating Large Language Model Serving
+ * with Tree-based Speculative Inference and Verification", arXiv 2305.09781):
+ * the target model scores every node of a token tree in one pass with tree
+ * attention over a shared KV cache, the tree is verified greedily or by
+ * multi-step speculative sampling (MSS), and the KV entries of the accepted
+ * path are kept in contiguous cache slots.
+ *
+ * Conventions shared by every entry point
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, frees nothing and keeps no state between calls.
+ *  - Every call is asynchronous on `stream` (0 = the null stream).
+ *  - The return value reports host-checkable problems only: bad sizes or
+ *    dtypes, null pointers, a workspace that is too small, a failed launch.
+ *    On a non-OK return nothing has been launched.
+ *  - Data-dependent problems are reported per request in `status[b]`
+ *    (TV_REQ_* codes).  tree_build_mask writes it; later calls read it, skip a
+ *    request whose status is nonzero, and may set it (only from 0) when they
+ *    find a problem of their own.  Outputs of a skipped request are filled as
+ *    stated per call.
+ *  - A tree has N <= 64 nodes in an order where every parent precedes its
+ *    children (DFS preorder in practice).  The tree root is NOT a node: it is
+ *    the end of the verified prefix, whose K/V is already cached; parent[i] =
+ *    -1 marks a child of the root.
+ *  - Row r of a per-request logits array is the target model's output for a
+ *    context: r = 0 is the root (the verified prefix), r = 1 + i is node i.
+ *  - The paged KV cache stores head h of logical slot t of request b at
+ *    k_cache[block_table[b][t / block_size]][h][t % block_size][0..D-1].
+ *    Slots 0..L_b-1 hold the verified prefix (L_b = prefix_len[b]); the
+ *    caller writes the K/V of tree node i at slot L_b + i before attention.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TV_OK = 0,
+  TV_EINVAL = 1,      /* a size, a null pointer or an unsupported shape */
+  TV_ETOOBIG = 2,     /* N > 64 */
+  TV_EDTYPE = 3,      /* unknown tv_dtype */
+  TV_EWORKSPACE = 4,  /* workspace smaller than the *_workspace() size */
+  TV_EHIP = 5         /* a HIP launch failed */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* Per-request status codes written to status[b]. */
+enum {
+  TV_REQ_OK = 0,
+  TV_REQ_BAD_PARENT = 1,    /* parent[i] not in {-1} U [0, i) */
+  TV_REQ_BAD_TOKEN = 2,     /* token[i] not in [0, V) */
+  TV_REQ_BAD_QROW = 3,      /* q_row[i] not in [0, R) */
+  TV_REQ_NONFINITE = 4,     /* a visited logits row holds NaN or +inf or no finite
+                               value, or a draft probability the walk reads is
+                               NaN, infinite or negative */
+  TV_REQ_KV_CAPACITY = 6,   /* prefix_len < 0 or prefix_len + N > max_blocks * block_size */
+  TV_REQ_BAD_BLOCK = 7,     /* a block_table entry the call needs is outside [0, num_blocks) */
+  TV_REQ_BAD_ACCEPTED = 8   /* num_accepted > N or an accepted id outside [0, N) */
+};
+
+/*
+ * tree_build_mask - topology-aware causal mask of every tree.
+ * Defines: SpecInfer summary, section "Tree-based Parallel Decoding:
+ * Topology-Aware Causal Mask" (TreeMask equation): node u attends node v iff
+ * v is an ancestor of u or v = u; the verified prefix is visible to all.
+ *
+ *   parent [B][N] int32     parent node of each node, -1 = child of the root
+ *   anc    [B][N] uint64    out: bit j set iff node j is node i or an ancestor
+ *   child  [B][N+1] uint64  out: child[b][0] = children of the root,
+ *                           child[b][u+1] = children of node u (bit j = node j)
+ *   depth  [B][N] int32     out: nodes on the root-to-i path (1 for root children)
+ *   status [B] int32        out: TV_REQ_OK, or TV_REQ_BAD_PARENT (then anc,
+ *                           child and depth of that request are all zero)
+ * Errors: TV_EINVAL if B < 0, N < 0 or a needed pointer is null; TV_ETOOBIG if
+ * N > 64.  B = 0 launches nothing.
+ */
+tv_status tree_build_mask(int B, int N, const int32_t* parent, uint64_t* anc,
+                          uint64_t* child, int32_t* depth, int32_t* status,
+                          hipStream_t stream);
+
+/*
+ * tree_attn_verify - tree attention for every node, head and request.
+ * Defines: SpecInfer summary, Definition 4.1 (TreeAttention(u) =
+ * Attention(S_u)), Equations 1-4 (scores Q K^T / sqrt(d), mask, softmax,
+ * times V) and the TreeMask equation; "KV-cache for verified tokens" (tree K/V
+ * live in the same cache, after the verified prefix).
+ *
+ * For request b, node i, head h: softmax over keys t in
+ *   {0..L_b-1} U {L_b + j : bit j of anc[b][i]}
+ * of scale * (q . k_t), times v_t, with fp32 accumulation.
+ *
+ *   dt            TV_F32 or TV_BF16: element type of q, k_cache, v_cache, out
+ *   D             head dim, 64 or 128;  scale: usually 1/sqrt(D)
+ *   q             [B][N][H][D]
+ *   k_cache, v_cache [num_blocks][H][block_size][D]; block_size must be 16
+ *   block_table   [B][max_blocks] int32
+ *   prefix_len    [B] int32
+ *   anc           [B][N] uint64 from tree_build_mask
+ *   status        [B] int32 in/out: requests with status != 0 get zero output;
+ *                 the call may set TV_REQ_KV_CAPACITY or TV_REQ_BAD_BLOCK
+ *                 (then that request's output is unspecified)
+ *   out           [B][N][H][D]
+ *   workspace     ws_bytes >= tree_attn_verify_workspace(...) bytes of device
+ *                 memory (may be null when that size is 0); contents on entry
+ *                 do not matter
+ * Errors: TV_EINVAL for N < 0, B < 0, H < 1, D not 64/128, block_size != 16,
+ * max_blocks < 1, num_blocks < 1 or null pointers; TV_ETOOBIG for N > 64;
+ * TV_EDTYPE; TV_EWORKSPACE.
+ */
+size_t tree_attn_verify_workspace(tv_dtype dt, int B, int N, int H, int D, int max_blocks);
+tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
+                           const void* q, const void* k_cache, const void* v_cache,
+                           int num_blocks, int block_size, const int32_t* block_table,
+                           int max_blocks, const int32_t* prefix_len, const uint64_t* anc,
+                           int32_t* status, void* out, void* workspace, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * tree_verify_greedy - VerifyGreedy.
+ * Defines: SpecInfer summary, section "Token Verification: Greedy Decoding
+ * (VerifyGreedy)": from the root, while a child v of the current node u has
+ * token O(u), accept v and continue; at the first miss emit O(u).
+ * O(u) = lowest index of the maximal fp32 logit of u's row; among children
+ * with the same token the lowest node index wins.
+ *
+ *   target_logits [B][N+1][V] fp32
+ *   token         [B][N] int32;   child [B][N+1] uint64 from tree_build_mask
+ *   status        [B] in/out (may set TV_REQ_BAD_TOKEN, TV_REQ_NONFINITE)
+ *   accepted      [B][N] out: accepted node ids in path order, then -1
+ *   num_accepted  [B] out: path length (-1 for a request with status != 0)
+ *   bonus         [B] out: the emitted target token (-1 if status != 0)
+ *   workspace     >= tree_verify_workspace(B, N, V) bytes
+ * Errors: TV_EINVAL (B, N < 0, V < 1 or V > 2^20, null pointers),
+ * TV_ETOOBIG, TV_EWORKSPACE.
+ */
+size_t tree_verify_workspace(int B, int N, int V);
+tv_status tree_verify_greedy(int B, int N, int V, const float* target_logits,
+                             const int32_t* token, const uint64_t* child, int32_t* status,
+                             int32_t* accepted, int32_t* num_accepted, int32_t* bonus,
+                             void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * tree_verify_mss - VerifyStochastic, multi-step speculative sampling.
+ * Defines: SpecInfer summary, section "Token Verification: Stochastic
+ * Decoding and Multi-Step Speculative Sampling (VerifyStochastic)"; the leaf
+ * bonus token and the zero-normaliser guard follow the wiki concept page
+ * "Speculative decoding", "Implementation sketch".
+ *
+ * At node u with untested children U (initially all children), round j:
+ *   words (x0,x1,x2,x3) = Philox4x32-10(key = seed, counter =
+ *       (64*slot(u) + j, b, offset mod 2^32, offset >> 32)),
+ *       slot(root) = 0, slot(node i) = i + 1;
+ *   s = the ((x0>>8) * |U| >> 24)-th member of U in ascending node order;
+ *   accept s iff ((x1>>8)+1) * 2^-24 <= p(token[s]) / q_s(token[s]) where p is
+ *   u's current target distribution (softmax of its row at first) and q_s =
+ *   ssm_probs[b][q_row[b][s]] (q = 0: ratio +inf if p > 0, else 0);
+ *   on acceptance move to s; on rejection p <- norm(max(0, p - q_s)) (left
+ *   unchanged if the normaliser is 0) and drop s from U.
+ * When U is empty (all rejected, or a leaf reached by acceptance) the bonus is
+ * the smallest x with sum_{y<=x} p(y) >= ((x2>>8)+1) * 2^-24 * sum(p), x2 from
+ * round 0 at that node.
+ *
+ *   target_logits [B][N+1][V] fp32;  ssm_probs [B][R][V] fp32 (used as given)
+ *   q_row         [B][N] int32 row of ssm_probs that proposed node i
+ *   token, child  as for greedy
+ *   status        [B] in/out (may set TV_REQ_BAD_TOKEN, TV_REQ_BAD_QROW,
+ *                 TV_REQ_NONFINITE)
+ *   accepted, num_accepted, bonus  as for greedy
+ *   rounds        [B] out, or null: number of ratio tests (-1 if skipped)
+ *   workspace     >= tree_verify_workspace(B, N, V) bytes
+ * Errors: as for greedy, plus TV_EINVAL for R < 1.
+ */
+tv_status tree_verify_mss(int B, int N, int V, int R, const float* target_logits,
+                          const float* ssm_probs, const int32_t* q_row, const int32_t* token,
+                          const uint64_t* child, int32_t* status, uint64_t seed,
+                          uint64_t offset, int32_t* accepted, int32_t* num_accepted,
+                          int32_t* bonus, int32_t* rounds, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * kv_commit_accepted - keep only the accepted path's KV entries.
+ * Defines: SpecInfer summary, "KV-cache for verified tokens" (only accepted
+ * tokens keep their cache entries); wiki concept page "Speculative decoding",
+ * "KV-cache rollback" (the accepted path is compacted into contiguous slots).
+ *
+ * For each request with status 0 and num_accepted k >= 0: for j < k, K and V
+ * of slot L + accepted[j] move to slot L + j (all heads; every read sees the
+ * cache as it was before the call), then prefix_len[b] = L + k.
+ *
+ *   k_cache, v_cache in/out, layout as for tree_attn_verify; N = tree size
+ *   prefix_len   [B] in/out
+ *   accepted     [B][N], num_accepted [B] from a verify call
+ *   status       [B] in/out (may set TV_REQ_KV_CAPACITY, TV_REQ_BAD_BLOCK,
+ *                TV_REQ_BAD_ACCEPTED; such a request is left unchanged)
+ * Errors: TV_EINVAL, TV_ETOOBIG, TV_EDTYPE as for tree_attn_verify.
+ */
+tv_status kv_commit_accepted(tv_dtype dt, int B, int N, int H, int D, void* k_cache,
+                             void* v_cache, int num_blocks, int block_size,
+                             const int32_t* block_table, int max_blocks, int32_t* prefix_len,
+                             const int32_t* accepted, const int32_t* num_accepted,
+                             int32_t* status, hipStream_t stream);
+
+/* Human-readable name of a tv_status value (static storage). */
+const char* tv_status_string(tv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEVERIFY_H */

@@ -21,8 +21,9 @@ BLOCK = 16
 def commit_status(block_table_row, L, N, num_blocks, accepted_row, k):
     if L < 0 or L + N > len(block_table_row) * BLOCK:
         return ST_KV_CAPACITY
-    nblk = (L + N + BLOCK - 1) // BLOCK
-    if any(not (0 <= int(block_table_row[j]) < num_blocks) for j in range(nblk)):
+    # the blocks holding the tree slots L .. L+N-1 (the only ones the move touches)
+    if N > 0 and any(not (0 <= int(block_table_row[j]) < num_blocks)
+                     for j in range(L // BLOCK, (L + N - 1) // BLOCK + 1)):
         return ST_BAD_BLOCK
     if k > N or any(not (0 <= int(accepted_row[j]) < N) for j in range(k)):
         return ST_BAD_ACCEPTED

@@ -23,6 +23,9 @@ Readings where the pages are silent:
   * the random child is the idx-th untested child in ascending node order,
     idx = (top 24 bits of word 0) * m >> 24; the accept uniform is in (0, 1];
   * q(x) = 0 gives ratio +inf when p(x) > 0 and 0 otherwise;
+  * -inf logits are allowed (probability 0); a visited row with NaN, +inf or
+    no finite entry, and a draft probability read by the walk that is NaN,
+    infinite or negative, stop the request with status 4;
   * a zero normaliser after a rejection leaves the distribution unchanged;
   * the final sample is the smallest x whose cumulative mass reaches
     u * sum(p) (falling back to the last x with p(x) > 0 if rounding leaves
@@ -59,28 +62,41 @@ def argmax_row(logits_row):
     return int(np.argmax(np.asarray(logits_row, dtype=np.float32)))
 
 
-def _request_checks(logits_b, token_b, V, q_row_b=None, R=None):
-    """Status of one request after the data checks, in the fixed order:
-    tokens in [0, V), then draft-row indices in [0, R), then finite logits."""
+def _request_checks(token_b, V, q_row_b=None, R=None):
+    """Status of one request after the up-front checks, in a fixed order:
+    tokens in [0, V), then draft-row indices in [0, R)."""
     if any(not (0 <= int(t) < V) for t in token_b):
         return ST_BAD_TOKEN
     if q_row_b is not None and any(not (0 <= int(r) < R) for r in q_row_b):
         return ST_BAD_QROW
-    if not np.all(np.isfinite(np.asarray(logits_b, dtype=np.float32))):
-        return ST_NONFINITE
     return ST_OK
+
+
+def row_ok(logits_row):
+    """A visited logits row is usable iff it holds no NaN, no +inf and at least
+    one finite value (-inf entries are allowed: probability 0)."""
+    l = np.asarray(logits_row, dtype=np.float32)
+    return not (np.isnan(l).any() or np.isposinf(l).any() or not np.isfinite(l.max()))
+
+
+def q_row_ok(q):
+    """A draft row read in full is usable iff every entry is finite and >= 0."""
+    return bool(np.all(np.isfinite(q)) and np.all(q >= 0.0))
 
 
 # ----------------------------------------------------------------------------
 # VerifyGreedy
 # ----------------------------------------------------------------------------
 def verify_greedy_one(parent, token, logits):
-    """Greedy walk for one request (assumes valid inputs).
+    """Greedy walk for one request (tokens already checked).
 
-    Returns (accepted node ids, bonus token)."""
+    Returns (accepted node ids, bonus token, status); a visited row that
+    fails row_ok stops the walk with status 4."""
     accepted = []
     u = -1
     while True:
+        if not row_ok(logits[u + 1]):
+            return accepted, -1, ST_NONFINITE
         o = argmax_row(logits[u + 1])
         nxt = None
         for c in children_of(parent, u):
@@ -88,7 +104,7 @@ def verify_greedy_one(parent, token, logits):
                 nxt = c
                 break
         if nxt is None:
-            return accepted, o
+            return accepted, o, ST_OK
         accepted.append(nxt)
         u = nxt
 
@@ -104,10 +120,13 @@ def verify_greedy(parent, token, target_logits, status):
     st = [int(s) for s in status]
     for b in range(B):
         if st[b] == ST_OK:
-            st[b] = _request_checks(target_logits[b], token[b], V)
+            st[b] = _request_checks(token[b], V)
         if st[b] != ST_OK:
             continue
-        path, bn = verify_greedy_one(parent[b], token[b], target_logits[b])
+        path, bn, s_b = verify_greedy_one(parent[b], token[b], target_logits[b])
+        st[b] = s_b
+        if s_b != ST_OK:
+            continue
         acc[b, : len(path)] = path
         num[b] = len(path)
         bonus[b] = bn
@@ -166,6 +185,8 @@ def mss_one(b, parent, token, logits, ssm, q_row, seed, offset):
     trace = []
     rounds = 0
     u = -1
+    if not row_ok(logits[0]):
+        return accepted, -1, rounds, ST_NONFINITE, trace
     p_cur = softmax_row(logits[0])
     while True:
         untested = children_of(parent, u)
@@ -187,12 +208,14 @@ def mss_one(b, parent, token, logits, ssm, q_row, seed, offset):
             if u1 <= ratio:
                 accepted.append(s)
                 u = s
+                if not row_ok(logits[s + 1]):
+                    return accepted, -1, rounds, ST_NONFINITE, trace
                 p_cur = softmax_row(logits[s + 1])
                 moved = True
                 break
-            p_new, z = residual(p_cur, qrow)
-            if not math.isfinite(z):
+            if not q_row_ok(qrow):
                 return accepted, -1, rounds, ST_NONFINITE, trace
+            p_new, z = residual(p_cur, qrow)
             if z == 0.0:
                 trace.append(("zero_residual", 0.0))
             p_cur = p_new
@@ -223,7 +246,7 @@ def verify_mss(parent, token, target_logits, ssm_probs, q_row, status, seed, off
     traces = [[] for _ in range(B)]
     for b in (range(B) if requests is None else requests):
         if st[b] == ST_OK:
-            st[b] = _request_checks(target_logits[b], token[b], V, q_row[b], R)
+            st[b] = _request_checks(token[b], V, q_row[b], R)
         if st[b] != ST_OK:
             continue
         path, bn, rd, s_b, tr = mss_one(b, parent[b], token[b], target_logits[b], ssm_probs[b],

@@ -1,0 +1,397 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded
+inputs.
+
+Bars: masks, accepted paths, bonus tokens, rounds, status and KV compaction
+bit-exact; MSS decisions may differ only for requests whose oracle trace has a
+near tie (|u - ratio| < 1e-6, or an inverse-CDF boundary within 1e-6 of the
+total mass), counted and printed; attention per element within
+2e-2 + 2e-2*|ref| for bf16 and 1e-5 + 1e-5*|ref| for fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.golden.load import read_mask_fixture
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests.gpu_util import (GpuRun, compare_mss, o_attn, o_commit, o_tree, o_verify, out_to_f64,
+                                to_dev, u64)
+
+TOL = {"bf16": (2e-2, 2e-2), "f32": (1e-5, 1e-5)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+SMALL = {
+    "c1_tiny": dict(cfg=1),
+    "c2_small": dict(cfg=2, B=2, L=100, H=4, V=3000),
+    "c2_small_f32": dict(cfg=2, B=2, L=100, H=3, V=3000, dtype="f32"),
+    "c2_small_d64": dict(cfg=2, B=2, L=70, H=4, D=64, V=3000),
+    "c3_small": dict(cfg=3, B=3, L=77, H=3, V=5003),
+    "c4_small": dict(cfg=4, B=3, H=2, V=4000),
+    "c5_small": dict(cfg=5, B=1, L=1500, H=2, V=2000),
+    "c5_small_f32_d64": dict(cfg=5, B=2, L=301, H=2, D=64, V=1000, dtype="f32"),
+}
+
+
+def _small(name):
+    kw = dict(SMALL[name])
+    cfg = kw.pop("cfg")
+    return synth.make_workload(cfg, **kw)
+
+
+def _print_case(*a):
+    print("[case]", *a, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# masks
+# ----------------------------------------------------------------------------
+def _mask_case(parent_2d):
+    B, N = parent_2d.shape
+    p = to_dev(parent_2d.astype(np.int32))
+    anc = torch.zeros((B, N), dtype=torch.int64, device="cuda:0")
+    child = torch.zeros((B, N + 1), dtype=torch.int64, device="cuda:0")
+    depth = torch.zeros((B, N), dtype=torch.int32, device="cuda:0")
+    st = torch.full((B,), -5, dtype=torch.int32, device="cuda:0")
+    import tree_speculative_verification_attn_amd as tv
+    tv.tree_build_mask(p, anc, child, depth, st)
+    torch.cuda.synchronize()
+    ra, rc, rd, rs = o_tree.build_mask_batch(parent_2d)
+    assert np.array_equal(u64(anc), np.array(ra, dtype=np.uint64).reshape(B, N))
+    assert np.array_equal(u64(child), np.array(rc, dtype=np.uint64).reshape(B, N + 1))
+    assert np.array_equal(depth.cpu().numpy(), np.array(rd).reshape(B, N))
+    assert np.array_equal(st.cpu().numpy(), np.array(rs))
+
+
+def test_mask_golden_and_random():
+    _print_case("mask golden")
+    for fx in ("p3_tree_mask.txt", "fig3_tree.txt"):
+        parent, _ = read_mask_fixture(fx)
+        _mask_case(np.array([parent]))
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 17, 63, 64):
+        par = np.array([[-1] + [int(rng.integers(-1, i)) for i in range(1, n)] for _ in range(37)])
+        _mask_case(par)
+    # chains, stars, malformed rows mixed in one batch
+    rows = [[-1] + list(range(63)), [-1] * 64, [0] + [-1] * 63, [-1, 1] + [-1] * 62,
+            [-1, 0, 5] + [-1] * 61, [-2] + [-1] * 63]
+    _mask_case(np.array(rows))
+
+
+def test_mask_all_configs():
+    for cfg in (1, 2, 3, 4, 5):
+        _print_case("mask config", cfg)
+        w = synth.make_workload(cfg, B=4 if cfg != 1 else 1, L=10, H=1, V=64)
+        _mask_case(w.parent)
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+def _check_attn(run, pairs=None):
+    w = run.w
+    anc, _, _, st = o_tree.build_mask_batch(w.parent)
+    ref, rst = o_attn.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len, anc, st,
+                                     w.dtype, w.scale, pairs=pairs)
+    got = out_to_f64(run.out)
+    sel = pairs if pairs is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
+    atol, rtol = TOL[w.dtype]
+    worst = 0.0
+    for b, h in sel:
+        r = ref[b, :, h]
+        g = got[b, :, h]
+        err = np.abs(g - r)
+        worst = max(worst, float(err.max()))
+        bad = err > atol + rtol * np.abs(r)
+        assert not bad.any(), (b, h, float(err.max()), np.argwhere(bad)[:5])
+    assert list(run.status.cpu().numpy()) == rst
+    return worst
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attention_small(name):
+    _print_case("attention", name)
+    w = _small(name)
+    run = GpuRun(w).mask().attn()
+    torch.cuda.synchronize()
+    worst = _check_attn(run)
+    print(f"{name}: max abs err {worst:.3e}")
+
+
+def test_attention_edge_shapes():
+    # prefix 0, one node, ragged prefix that is not a multiple of 16 or 32
+    for kw in (dict(L=0), dict(L=1), dict(L=15), dict(L=33), dict(L=129)):
+        for tree_ in (("parents", [-1]), ("parents", [-1, 0, 0, 1, -1]), ("expand", (4, 4, 2, 1, 1))):
+            for dt in ("bf16", "f32"):
+                _print_case("attention edge", kw, tree_, dt)
+                w = synth.make_workload(dict(name="e", B=2, H=2, D=128, V=50, dtype=dt, tree=tree_,
+                                             sig_t=1.0, sig_s=1.0, **kw), 77)
+                run = GpuRun(w).mask().attn()
+                torch.cuda.synchronize()
+                _check_attn(run)
+
+
+def test_attention_status_paths():
+    w = synth.make_workload(2, B=3, L=40, H=2, V=100)
+    _print_case("attention status")
+    run = GpuRun(w).mask()
+    # request 0 malformed upstream, request 1 over capacity, request 2 fine
+    run.status[0] = 1
+    pl = w.prefix_len.copy()
+    pl[1] = w.max_blocks * 16
+    run.pl = to_dev(pl)
+    run.attn()
+    torch.cuda.synchronize()
+    st = run.status.cpu().numpy()
+    assert list(st) == [1, 6, 0]
+    out = out_to_f64(run.out)
+    assert np.all(out[0] == 0)
+    # request 2 matches the oracle
+    w2 = w
+    anc, _, _, _ = o_tree.build_mask_batch(w2.parent)
+    ref, _ = o_attn.tree_attention(w2.q, w2.k_cache, w2.v_cache, w2.block_table, w2.prefix_len, anc,
+                                   [0, 0, 0], w2.dtype, w2.scale, pairs=[(2, 0), (2, 1)])
+    np.testing.assert_allclose(out[2], ref[2], atol=2e-2, rtol=2e-2)
+    # a bad block id is reported as status 7
+    bt = w.block_table.copy()
+    bt[2, 0] = w.num_blocks + 5
+    run2 = GpuRun(w).mask()
+    run2.bt = to_dev(bt)
+    run2.attn()
+    torch.cuda.synchronize()
+    assert run2.status.cpu().numpy()[2] == 7
+
+
+# ----------------------------------------------------------------------------
+# greedy / MSS
+# ----------------------------------------------------------------------------
+def _check_greedy(run):
+    w = run.w
+    ref = o_verify.verify_greedy(w.parent, w.token, w.target_logits, [0] * w.B)
+    assert np.array_equal(run.g_acc.cpu().numpy(), ref["accepted"])
+    assert np.array_equal(run.g_num.cpu().numpy(), ref["num_accepted"])
+    assert np.array_equal(run.g_bonus.cpu().numpy(), ref["bonus"])
+    assert np.array_equal(run.status.cpu().numpy(), ref["status"])
+
+
+def _check_mss(run, label):
+    w = run.w
+    ref = o_verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0] * w.B,
+                              w.seed, w.offset)
+    exact, excused, bad = compare_mss(run, ref)
+    print(f"{label}: MSS exact {exact}, near-tie {excused}, unexcused {len(bad)}; "
+          f"accepted {run.m_num.cpu().numpy().tolist()}")
+    assert not bad, (bad, run.m_num.cpu().numpy()[bad], ref["num_accepted"][bad])
+    return ref
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_verify_small(name):
+    _print_case("verify", name)
+    w = _small(name)
+    run = GpuRun(w).mask().greedy()
+    torch.cuda.synchronize()
+    _check_greedy(run)
+    run = GpuRun(w).mask().mss()
+    torch.cuda.synchronize()
+    _check_mss(run, name)
+
+
+def test_greedy_forced_paths():
+    # logits make the LLM's choice equal a chosen child at every level
+    w = synth.make_workload(1)
+    tl = w.target_logits.copy()
+    path = [0, 1, 2]        # learning -> algorithm -> is
+    for d, node in enumerate(path):
+        row = 0 if d == 0 else path[d - 1] + 1
+        tl[0, row, :] = 0
+        tl[0, row, w.token[0, node]] = 5.0
+    tl[0, path[-1] + 1, :] = 0
+    tl[0, path[-1] + 1, 7] = 5.0
+    w.target_logits = tl
+    run = GpuRun(w).mask().greedy()
+    torch.cuda.synchronize()
+    assert run.g_num.cpu().numpy()[0] == 3 and run.g_bonus.cpu().numpy()[0] == 7
+    _check_greedy(run)
+
+
+def test_verify_status_paths():
+    w = synth.make_workload(2, B=6, L=20, H=1, V=500)
+    tok = w.token.copy()
+    qr = w.q_row.copy()
+    tl = w.target_logits.copy()
+    sp = w.ssm_probs.copy()
+    tok[1, 3] = w.V                 # bad token
+    qr[2, 5] = w.R                  # bad q row
+    tl[3, 0, 17] = np.nan           # the root row is always visited
+    tl[4, 0, :] = -np.inf           # no finite value in a visited row
+    tl[5, 0, :5] = -np.inf          # masked entries are fine
+    w.token, w.q_row, w.target_logits, w.ssm_probs = tok, qr, tl, sp
+    _print_case("verify status")
+    run = GpuRun(w).mask()
+    run.status[0] = 1               # upstream fault
+    run.greedy()
+    torch.cuda.synchronize()
+    st_g = run.status.cpu().numpy().copy()
+    ref_g = o_verify.verify_greedy(w.parent, w.token, w.target_logits, [1, 0, 0, 0, 0, 0])
+    assert list(st_g) == list(ref_g["status"])
+    assert np.array_equal(run.g_num.cpu().numpy(), ref_g["num_accepted"])
+    run = GpuRun(w).mask()
+    run.status[0] = 1
+    run.mss()
+    torch.cuda.synchronize()
+    ref = o_verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row,
+                              [1, 0, 0, 0, 0, 0], w.seed)
+    assert list(run.status.cpu().numpy()) == list(ref["status"])
+    assert list(run.status.cpu().numpy())[:5] == [1, 2, 3, 4, 4]
+    exact, excused, bad = compare_mss(run, ref)
+    assert not bad
+
+
+def test_mss_q_row_problems():
+    # a negative draft probability on a tested child, and a NaN in a row read in full
+    w = synth.make_workload(1)
+    base_run = GpuRun(w).mask().mss()
+    torch.cuda.synchronize()
+    sp = w.ssm_probs.copy()
+    sp[0, :, :] = np.where(sp[0] > 0, sp[0], 0)
+    sp[0, 0, 5] = np.nan            # row 0 proposes the root's children
+    w.ssm_probs = sp
+    run = GpuRun(w).mask().mss()
+    torch.cuda.synchronize()
+    ref = o_verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0], w.seed)
+    exact, excused, bad = compare_mss(run, ref)
+    assert not bad
+    assert base_run.status.cpu().numpy()[0] == 0
+
+
+def test_mss_offsets_and_determinism():
+    w = _small("c2_small")
+    a = GpuRun(w).mask().mss(offset=3)
+    b = GpuRun(w).mask().mss(offset=3)
+    torch.cuda.synchronize()
+    for x, y in ((a.m_acc, b.m_acc), (a.m_bonus, b.m_bonus), (a.m_rounds, b.m_rounds)):
+        assert torch.equal(x, y)
+    ref = o_verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0] * w.B,
+                              w.seed, 3)
+    exact, excused, bad = compare_mss(a, ref)
+    assert not bad
+
+
+def test_empty_tree_verify():
+    w = synth.make_workload(dict(name="e", B=3, H=1, D=64, L=5, V=300, dtype="f32",
+                                 tree=("parents", []), sig_t=2.0, sig_s=1.0), 3)
+    run = GpuRun(w).mask().greedy()
+    torch.cuda.synchronize()
+    _check_greedy(run)
+    run = GpuRun(w).mask().mss()
+    torch.cuda.synchronize()
+    _check_mss(run, "empty tree")
+
+
+# ----------------------------------------------------------------------------
+# KV compaction
+# ----------------------------------------------------------------------------
+def _slots(cache, bt, b, slots):
+    blk = bt[b, np.asarray(slots) // 16]
+    return cache[blk, :, np.asarray(slots) % 16]
+
+
+def _check_commit(run, w, acc, num, st_in, k_before, v_before):
+    k_ref, v_ref, pl_ref, st_ref = o_commit.kv_commit(k_before, v_before, w.block_table, w.prefix_len,
+                                                      acc, num, st_in, w.N)
+    assert np.array_equal(run.pl.cpu().numpy(), pl_ref)
+    assert np.array_equal(run.status.cpu().numpy(), st_ref)
+    kg = run.k.view(torch.int16).cpu().numpy() if run.k.dtype == torch.bfloat16 else run.k.cpu().numpy()
+    vg = run.v.view(torch.int16).cpu().numpy() if run.v.dtype == torch.bfloat16 else run.v.cpu().numpy()
+    kr = k_ref.view(np.int16) if k_ref.dtype == np.uint16 else k_ref
+    vr = v_ref.view(np.int16) if v_ref.dtype == np.uint16 else v_ref
+    assert np.array_equal(kg, kr) and np.array_equal(vg, vr)
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "c2_small", "c3_small", "c5_small", "c5_small_f32_d64"])
+def test_commit_small(name):
+    _print_case("commit", name)
+    w = _small(name)
+    run = GpuRun(w).mask().mss()
+    torch.cuda.synchronize()
+    acc = run.m_acc.cpu().numpy()
+    num = run.m_num.cpu().numpy()
+    st_in = run.status.cpu().numpy().copy()
+    run.commit(run.m_acc, run.m_num)
+    torch.cuda.synchronize()
+    _check_commit(run, w, acc, num, st_in, w.k_cache, w.v_cache)
+
+
+def test_commit_hazard_and_errors():
+    # path (1,2,4) overlaps sources and destinations; bad ids and capacity
+    w = synth.make_workload(dict(name="h", B=5, H=3, D=128, L=29, V=40, dtype="bf16",
+                                 tree=("parents", [-1, -1, 1, 2, 2, 3, 0]), sig_t=1.0, sig_s=1.0), 9)
+    acc = np.full((5, 7), -1, dtype=np.int32)
+    num = np.array([3, 2, 3, 0, -1], dtype=np.int32)
+    acc[0, :3] = [1, 2, 4]
+    acc[1, :2] = [6, 0]
+    acc[2, :3] = [1, 2, 7]          # 7 >= N: bad accepted list
+    run = GpuRun(w).mask()
+    torch.cuda.synchronize()
+    st_in = run.status.cpu().numpy().copy()
+    run.commit(to_dev(acc), to_dev(num))
+    torch.cuda.synchronize()
+    _check_commit(run, w, acc, num, st_in, w.k_cache, w.v_cache)
+    assert run.status.cpu().numpy()[2] == 8
+
+
+# ----------------------------------------------------------------------------
+# full-size configurations (sampled attention outputs)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_config(cfg):
+    _print_case("full config", cfg, "generate")
+    w = synth.make_config(cfg)
+    _print_case("full config", cfg, "mask+attn")
+    run = GpuRun(w).mask().attn()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg)
+    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(3)]
+    pairs += [(0, 0), (w.B - 1, w.H - 1)]
+    worst = _check_attn(run, pairs=pairs)
+    print(f"config {cfg}: attention max abs err {worst:.3e} over {len(pairs)} (b,h) pairs")
+    _print_case("full config", cfg, "greedy")
+    run.greedy()
+    torch.cuda.synchronize()
+    _check_greedy(run)
+    _print_case("full config", cfg, "mss")
+    run.mss()
+    torch.cuda.synchronize()
+    _check_mss(run, f"config {cfg}")
+    _print_case("full config", cfg, "commit")
+    acc = run.m_acc.cpu().numpy()
+    num = run.m_num.cpu().numpy()
+    L = w.prefix_len
+    before_k = {}
+    for b in range(w.B):
+        if num[b] > 0:
+            before_k[b] = (_slots(w.k_cache, w.block_table, b, L[b] + acc[b, : num[b]]),
+                           _slots(w.v_cache, w.block_table, b, L[b] + acc[b, : num[b]]))
+    run.commit(run.m_acc, run.m_num)
+    torch.cuda.synchronize()
+    assert np.array_equal(run.pl.cpu().numpy(), L + np.maximum(num, 0))
+    kd = run.k.view(torch.int16) if run.k.dtype == torch.bfloat16 else run.k
+    vd = run.v.view(torch.int16) if run.v.dtype == torch.bfloat16 else run.v
+    for b, (kk, vv) in before_k.items():
+        slots = L[b] + np.arange(num[b])
+        blk = torch.from_numpy(w.block_table[b, slots // 16].astype(np.int64)).to("cuda:0")
+        off = torch.from_numpy((slots % 16).astype(np.int64)).to("cuda:0")
+        kg = kd[blk, :, off].cpu().numpy()
+        vg = vd[blk, :, off].cpu().numpy()
+        kr = kk.view(np.int16) if kk.dtype == np.uint16 else kk
+        vr = vv.view(np.int16) if vv.dtype == np.uint16 else vv
+        assert np.array_equal(kg, kr) and np.array_equal(vg, vr)

@@ -474,13 +474,21 @@ def test_status_codes():
     r = verify.verify_mss(parent, np.array([[1, 2]]), tl, sp, np.array([[0, 2]]), [0], 1)
     assert r["status"][0] == ST_BAD_QROW
     tl2 = tl.copy()
-    tl2[0, 2, 5] = np.inf
+    tl2[0, 0, 5] = np.inf           # the root row is always visited
     r = verify.verify_mss(parent, np.array([[1, 2]]), tl2, sp, qr, [0], 1)
     assert r["status"][0] == ST_NONFINITE
+    tl3 = tl.copy()
+    tl3[0, 0, :] = -np.inf
+    tl3[0, 0, 1] = 0.0              # -inf entries are masked tokens, not errors
+    tl3[0, 2, 4] = np.nan           # a row the walk never visits
+    sp3 = np.full((1, 2, V), 1e-3, dtype=np.float32)
+    r = verify.verify_mss(np.array([[-1, -1]]), np.array([[3, 2]]), tl3, sp3, qr, [0], 1)
+    assert r["status"][0] == ST_OK and r["bonus"][0] == 1
     sp2 = sp.copy()
-    sp2[0, 0, 1] = -0.5
+    sp2[0, 0, 1] = -0.5             # the tested child's own probability
     r = verify.verify_mss(parent, np.array([[1, 2]]), tl, sp2, qr, [0], 1)
     assert r["status"][0] == ST_NONFINITE
+    assert not verify.q_row_ok(np.array([0.5, np.nan])) and verify.q_row_ok(np.array([0.0, 1.0]))
     r = verify.verify_mss(parent, np.array([[1, 2]]), tl, sp, qr, [3], 1)
     assert r["status"][0] == 3 and r["num_accepted"][0] == -1
     g = verify.verify_greedy(parent, np.array([[1, -1]]), tl, [0])

@@ -1,0 +1,78 @@
+// tree_build_mask: ancestor / child bitmasks and depths of every tree.
+//
+// TreeMask (SpecInfer summary, "Tree-based Parallel Decoding: Topology-Aware
+// Causal Mask"): node u may attend node v iff v is u or one of u's ancestors.
+// One wave64 per request; lane i owns node i.  Each lane climbs its parent
+// chain through cross-lane reads (depth <= 64 steps), so no mask is ever
+// materialised on the host.
+#include "tv_common.h"
+
+namespace {
+
+__global__ __launch_bounds__(64) void build_mask_kernel(int N, const int32_t* __restrict__ parent,
+                                                        uint64_t* __restrict__ anc,
+                                                        uint64_t* __restrict__ child,
+                                                        int32_t* __restrict__ depth,
+                                                        int32_t* __restrict__ status) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const bool live = i < N;
+  const int p = live ? parent[static_cast<size_t>(b) * N + i] : -1;
+  const int bad = __any(live && (p < -1 || p >= i));
+
+  uint64_t a = 0;
+  int d = 0;
+  if (!bad && live) {
+    a = 1ull << i;
+    d = 1;
+  }
+  // climb: cur = current ancestor of node i (-1 = reached the root)
+  int cur = bad ? -1 : p;
+  for (int step = 0; step < N; ++step) {
+    const int any_left = __any(cur >= 0);
+    if (!any_left) break;
+    const int src = cur >= 0 ? cur : 0;
+    const int up = __shfl(p, src, 64);   // parent of my current ancestor
+    if (cur >= 0) {
+      a |= 1ull << cur;
+      ++d;
+      cur = up;
+    }
+  }
+  if (live) {
+    anc[static_cast<size_t>(b) * N + i] = a;
+    depth[static_cast<size_t>(b) * N + i] = d;
+  }
+  // child[u + 1] = set of nodes whose parent is u, u = -1 .. N-1
+  for (int u = -1; u < N; ++u) {
+    const uint64_t m = bad ? 0ull : static_cast<uint64_t>(__ballot(live && p == u));
+    if (i == 0) child[static_cast<size_t>(b) * (N + 1) + (u + 1)] = m;
+  }
+  if (i == 0) status[b] = bad ? TV_REQ_BAD_PARENT : TV_REQ_OK;
+}
+
+}  // namespace
+
+extern "C" tv_status tree_build_mask(int B, int N, const int32_t* parent, uint64_t* anc,
+                                     uint64_t* child, int32_t* depth, int32_t* status,
+                                     hipStream_t stream) {
+  if (B < 0 || N < 0) return TV_EINVAL;
+  if (N > TV_MAX_NODES) return TV_ETOOBIG;
+  if (B == 0) return TV_OK;
+  if (!child || !status || (N > 0 && (!parent || !anc || !depth))) return TV_EINVAL;
+  hipLaunchKernelGGL(build_mask_kernel, dim3(B), dim3(64), 0, stream, N, parent, anc, child, depth,
+                     status);
+  return tv::launch_status();
+}
+
+extern "C" const char* tv_status_string(tv_status s) {
+  switch (s) {
+    case TV_OK: return "ok";
+    case TV_EINVAL: return "invalid argument";
+    case TV_ETOOBIG: return "tree larger than 64 nodes";
+    case TV_EDTYPE: return "unsupported dtype";
+    case TV_EWORKSPACE: return "workspace too small";
+    case TV_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
