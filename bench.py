@@ -94,7 +94,7 @@ def main():
     out = torch.empty_like(copies[0]["q"])
     code = tv.TV_BF16 if bf else tv.TV_F32
     ws_a = tv.tree_attn_verify_workspace(code, B, N, H, D, w.max_blocks)
-    ws_attn = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev) if ws_a else None
+    ws_attn = torch.zeros(max(ws_a, 1), dtype=torch.uint8, device=dev) if ws_a else None
     ws_v = torch.empty(tv.tree_verify_workspace(B, N, V), dtype=torch.uint8, device=dev)
     g_acc = torch.empty((B, N), dtype=torch.int32, device=dev)
     g_num = torch.empty((B,), dtype=torch.int32, device=dev)

@@ -112,8 +112,9 @@ tv_status tree_build_mask(int B, int N, const int32_t* parent, uint64_t* anc,
  *                 (then that request's output is unspecified)
  *   out           [B][N][H][D]
  *   workspace     ws_bytes >= tree_attn_verify_workspace(...) bytes of device
- *                 memory (may be null when that size is 0); contents on entry
- *                 do not matter
+ *                 memory for per-chunk partial results (may be null when that
+ *                 size is 0); contents on entry do not matter.  Calls that
+ *                 overlap in time must not share a workspace.
  * Errors: TV_EINVAL for N < 0, B < 0, H < 1, D not 64/128, block_size != 16,
  * max_blocks < 1, num_blocks < 1 or null pointers; TV_ETOOBIG for N > 64;
  * TV_EDTYPE; TV_EWORKSPACE.

@@ -52,6 +52,8 @@ def gather_slots(cache, block_table_row, slots, head, dtype):
 def masked_attention_one(qv, K, V, visible, scale):
     """softmax(mask(K qv / sqrt(d))) V for one query: Equations 2-4, with -inf
     outside `visible` (scale = 1/sqrt(d))."""
+    if not visible.any():            # a padding slot over an empty prefix
+        return np.zeros(V.shape[1])
     s = (K @ qv) * scale
     s = np.where(visible, s, -np.inf)
     m = s.max()

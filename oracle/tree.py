@@ -9,6 +9,9 @@ prefix + own-ancestors rule explicitly).
 Representation: nodes 0..N-1 in an order where every parent precedes its
 children (DFS preorder in practice); parent[i] = -1 marks a child of the
 root, the root being the end of the verified prefix (not a node).
+parent[i] = -2 marks an unused padding slot, so that trees of different sizes
+share one batch: it is nobody's child, has no ancestors (anc 0, depth 0) and
+cannot be a parent.
   anc[i]      bit j set iff node j is node i itself or one of its ancestors
   child[0]    bit j set iff node j is a child of the root
   child[u+1]  bit j set iff node j is a child of node u
@@ -20,18 +23,23 @@ from .status import ST_OK, ST_BAD_PARENT
 def build_mask(parent):
     """Return (anc, child, depth, status) for one request, as Python ints.
 
-    A request whose parent array is malformed (parent[i] not in {-1} U [0, i))
-    or longer than 64 nodes gets status 1 and all-zero outputs.
+    A request whose parent array is malformed (parent[i] not in {-2, -1} U
+    {j < i : j not padding}) or longer than 64 nodes gets status 1 and
+    all-zero outputs.
     """
     n = len(parent)
     anc = [0] * n
     depth = [0] * n
     child = [0] * (n + 1)
-    ok = n <= 64 and all(-1 <= int(parent[i]) < i for i in range(n))
+    ok = n <= 64 and all(int(parent[i]) in (-2, -1) or
+                         (0 <= int(parent[i]) < i and int(parent[int(parent[i])]) != -2)
+                         for i in range(n))
     if not ok:
         return anc, child, depth, ST_BAD_PARENT
     for i in range(n):
         p = int(parent[i])
+        if p == -2:
+            continue
         if p < 0:
             depth[i] = 1
             anc[i] = 1 << i
@@ -46,6 +54,11 @@ def build_mask_batch(parent_2d):
     """build_mask for every row of a [B][N] parent array."""
     out = [build_mask(list(row)) for row in parent_2d]
     return ([o[0] for o in out], [o[1] for o in out], [o[2] for o in out], [o[3] for o in out])
+
+
+def is_node(parent, i):
+    """False for a padding slot."""
+    return int(parent[i]) != -2
 
 
 def children_of(parent, u):

@@ -62,12 +62,14 @@ def argmax_row(logits_row):
     return int(np.argmax(np.asarray(logits_row, dtype=np.float32)))
 
 
-def _request_checks(token_b, V, q_row_b=None, R=None):
+def _request_checks(parent_b, token_b, V, q_row_b=None, R=None):
     """Status of one request after the up-front checks, in a fixed order:
-    tokens in [0, V), then draft-row indices in [0, R)."""
-    if any(not (0 <= int(t) < V) for t in token_b):
+    tokens in [0, V), then draft-row indices in [0, R) (padding slots,
+    parent -2, are not checked)."""
+    nodes = [i for i in range(len(token_b)) if int(parent_b[i]) != -2]
+    if any(not (0 <= int(token_b[i]) < V) for i in nodes):
         return ST_BAD_TOKEN
-    if q_row_b is not None and any(not (0 <= int(r) < R) for r in q_row_b):
+    if q_row_b is not None and any(not (0 <= int(q_row_b[i]) < R) for i in nodes):
         return ST_BAD_QROW
     return ST_OK
 
@@ -120,7 +122,7 @@ def verify_greedy(parent, token, target_logits, status):
     st = [int(s) for s in status]
     for b in range(B):
         if st[b] == ST_OK:
-            st[b] = _request_checks(token[b], V)
+            st[b] = _request_checks(parent[b], token[b], V)
         if st[b] != ST_OK:
             continue
         path, bn, s_b = verify_greedy_one(parent[b], token[b], target_logits[b])
@@ -246,7 +248,7 @@ def verify_mss(parent, token, target_logits, ssm_probs, q_row, status, seed, off
     traces = [[] for _ in range(B)]
     for b in (range(B) if requests is None else requests):
         if st[b] == ST_OK:
-            st[b] = _request_checks(token[b], V, q_row[b], R)
+            st[b] = _request_checks(parent[b], token[b], V, q_row[b], R)
         if st[b] != ST_OK:
             continue
         path, bn, rd, s_b, tr = mss_one(b, parent[b], token[b], target_logits[b], ssm_probs[b],

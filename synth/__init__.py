@@ -21,7 +21,8 @@ Layouts (all row-major):
   v_cache      [num_blocks][H][16][D]
   block_table  [B][max_blocks] int32  physical block of logical block j (-1 unused)
   prefix_len   [B] int32              verified prefix length L_b
-  parent       [B][N] int32           parent node index, -1 for children of the root
+  parent       [B][N] int32           parent node index, -1 for children of the root,
+                                      -2 for padding slots of a smaller tree
   token        [B][N] int32           speculated token of each node
   target_logits[B][N+1][V] float32    row 0 = root context, row 1+i = node i's context
   ssm_probs    [B][R][V] float32      draft distributions (softmaxed)
@@ -396,17 +397,17 @@ def make_workload(cfg: int | dict, seed: int | None = None, *, B=None, L=None, H
         else:
             raise ValueError(f"unknown tree kind {kind!r}")
 
+    # Trees of different sizes (merge-built ones) share the batch: the extra
+    # slots are padding (parent -2), which no node attends or verifies.
     N = max(len(r[0]) for r in per_req)
     R = max(r[2].shape[0] for r in per_req)
-    parent = np.full((Bn, N), -1, dtype=np.int32)
+    parent = np.full((Bn, N), -2, dtype=np.int32)
     token = np.zeros((Bn, N), dtype=np.int32)
     q_row = np.zeros((Bn, N), dtype=np.int32)
     tl = np.zeros((Bn, N + 1, Vn), dtype=np.float32)
     sp = np.zeros((Bn, R, Vn), dtype=np.float32)
     for b, (par, tl_b, sp_b, tok_b, qr_b) in enumerate(per_req):
         n_b = len(par)
-        if n_b != N:
-            raise ValueError("all requests of one workload must have the same node count")
         parent[b, :n_b] = par
         token[b, :n_b] = tok_b
         q_row[b, :n_b] = qr_b

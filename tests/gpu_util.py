@@ -53,7 +53,7 @@ class GpuRun:
         w = self.w
         code = tv.TV_BF16 if w.dtype == "bf16" else tv.TV_F32
         ws = tv.tree_attn_verify_workspace(code, w.B, w.N, w.H, w.D, w.max_blocks)
-        self.ws_attn = torch.empty(max(ws, 1), dtype=torch.uint8, device=DEV)
+        self.ws_attn = torch.zeros(max(ws, 1), dtype=torch.uint8, device=DEV)   # counters start at 0
         self.out = torch.empty_like(self.q)
         tv.tree_attn_verify(self.q, self.k, self.v, self.bt, self.pl, self.anc, self.status, self.out,
                             self.ws_attn if ws else None, scale=w.scale)

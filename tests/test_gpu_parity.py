@@ -80,9 +80,10 @@ def test_mask_golden_and_random():
     for n in (1, 2, 17, 63, 64):
         par = np.array([[-1] + [int(rng.integers(-1, i)) for i in range(1, n)] for _ in range(37)])
         _mask_case(par)
-    # chains, stars, malformed rows mixed in one batch
+    # chains, stars, padding slots, malformed rows mixed in one batch
     rows = [[-1] + list(range(63)), [-1] * 64, [0] + [-1] * 63, [-1, 1] + [-1] * 62,
-            [-1, 0, 5] + [-1] * 61, [-2] + [-1] * 63]
+            [-1, 0, 5] + [-1] * 61, [-3] + [-1] * 63, [-1, -2, 0] + [-2] * 61,
+            [-2, 0] + [-1] * 62, [-2] * 64]
     _mask_case(np.array(rows))
 
 
@@ -129,7 +130,8 @@ def test_attention_small(name):
 def test_attention_edge_shapes():
     # prefix 0, one node, ragged prefix that is not a multiple of 16 or 32
     for kw in (dict(L=0), dict(L=1), dict(L=15), dict(L=33), dict(L=129)):
-        for tree_ in (("parents", [-1]), ("parents", [-1, 0, 0, 1, -1]), ("expand", (4, 4, 2, 1, 1))):
+        for tree_ in (("parents", [-1]), ("parents", [-1, 0, 0, 1, -1]),
+                      ("expand_trunc", (4, 4, 2, 1, 1), 64), ("parents", [-1, -2, 0, -2])):
             for dt in ("bf16", "f32"):
                 _print_case("attention edge", kw, tree_, dt)
                 w = synth.make_workload(dict(name="e", B=2, H=2, D=128, V=50, dtype=dt, tree=tree_,

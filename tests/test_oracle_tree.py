@@ -70,7 +70,7 @@ def test_invariants_random_trees():
             assert (child[par[i] + 1] >> i) & 1
 
 
-@pytest.mark.parametrize("bad", [[0], [-2], [-1, 1], [-1, 0, 3], [-1, 5, 0]])
+@pytest.mark.parametrize("bad", [[0], [-3], [-1, 1], [-1, 0, 3], [-1, 5, 0], [-2, 0], [-1, -2, 1]])
 def test_bad_parent_status(bad):
     anc, child, depth, st = tree.build_mask(bad)
     assert st == ST_BAD_PARENT
@@ -85,3 +85,15 @@ def test_too_many_nodes():
 def test_empty_tree():
     anc, child, depth, st = tree.build_mask([])
     assert st == ST_OK and anc == [] and child == [0] and depth == []
+
+
+def test_padding_slots():
+    # -2 marks an unused slot: no ancestors, nobody's child, never a parent
+    anc, child, depth, st = tree.build_mask([-1, -2, 0, -2, 2])
+    assert st == ST_OK
+    assert anc == [0b1, 0, 0b101, 0, 0b10101]
+    assert depth == [1, 0, 2, 0, 3]
+    assert child == [0b1, 0b100, 0, 0b10000, 0, 0]
+    assert tree.children_of([-1, -2, 0], -1) == [0]
+    anc, child, depth, st = tree.build_mask([-2, -2])
+    assert st == ST_OK and anc == [0, 0] and child == [0, 0, 0]

@@ -41,6 +41,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
+constexpr int kMaxSplits = 64;                      // chunks per (request, head)
+constexpr int kMaxChunkKeys = 16384;                // keys per workgroup chunk (bf16 path)
+constexpr int kMaxChunkBlocks = kMaxChunkKeys / TV_BLOCK + 1;
 
 struct AttnArgs {
   int B, N, H, D;
@@ -128,18 +131,51 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   return as_bf16x8(r);
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tile of K or V for one 64-key stage: row-major [64 keys][D] bf16 with
+// the 16-byte chunks of row r permuted (XOR) so that the 16 rows one matrix
+// operand read touches fall in different banks.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c16) {
+  if constexpr (D == 128) return c16 ^ (r & 15);
+  else return c16 ^ ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c16) {   // byte offset
+  return r * (2 * D) + swz<D>(r, c16) * 16;
+}
+
+// One workgroup = 4 waves per (request b, head h, key chunk s).  K/V stages of
+// 64 keys are copied HBM -> LDS with direct-to-LDS loads (no registers), two
+// stages in flight; all 4 waves load, waves 0..NQT-1 each own one 16-query
+// tile of the tree for the whole chunk.  Per 32 keys and query tile:
+//   S^T[key][query] = K . Q^T     (A = K rows from LDS, B = Q^T in registers)
+//   O^T[dim][query] += V^T . P^T  (A = V^T via LDS transpose reads,
+//                                  B = P^T straight from the S^T accumulator)
+// With several chunks, each workgroup leaves an unnormalised partial and the
+// last one to finish (counter in the workspace) merges them.
 template <int D, int NQT>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int KC = D / 32;     // 32-dim chunks of the contraction over D
-  constexpr int DT = D / 16;     // 16-dim output tiles
-  constexpr int NQ = 16 * NQT;   // padded queries
+__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int KC = D / 32;               // contraction steps over D
+  constexpr int DT = D / 16;               // output dim tiles
+  constexpr int CPR = D / 8;               // 16-byte chunks per key row
+  constexpr int SK = 64;                   // keys per stage
+  constexpr int TILE = SK * D * 2;         // bytes of one K or V stage tile
+  constexpr int LPW = (2 * TILE / 1024) / 4;   // 1 KB wave-loads per wave per stage
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
 
-  __shared__ int s_gate;
-  __shared__ int s_badblk;
+  // two stage buffers, each [K tile | V tile]; separate arrays so the
+  // compiler can tell the in-flight stage from the one being read
+  __shared__ __attribute__((aligned(16))) uint8_t stage_buf0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_buf1[2 * TILE];
+  __shared__ int s_gate, s_badblk;
+  __shared__ int s_blk[kMaxChunkBlocks];
+
   if (threadIdx.x == 0) {
     s_gate = request_gate(a, b);
     s_badblk = 0;
@@ -149,160 +185,114 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
   if (gate != TV_REQ_OK) {
     if (gate == TV_REQ_KV_CAPACITY && threadIdx.x == 0 && a.status[b] == TV_REQ_OK)
       a.status[b] = TV_REQ_KV_CAPACITY;
-    if (a.splits == 1) zero_out<uint16_t>(a, b, h);
+    if (s == 0) zero_out<uint16_t>(a, b, h);
     return;
   }
   const int L = a.prefix_len[b];
   const int N = a.N;
   const int T = L + N;
   const int k_begin = s * a.chunk;
-  if (k_begin >= T) return;  // empty chunk: the merge never reads it
+  if (k_begin >= T) return;                 // empty chunk: not counted by the merge
   const int k_end = min(T, k_begin + a.chunk);
+  const int nst = (k_end - k_begin + SK - 1) / SK;
 
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.kc);
-  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(a.vc);
+  const uint8_t* __restrict__ kg = static_cast<const uint8_t*>(a.kc);
+  const uint8_t* __restrict__ vg = static_cast<const uint8_t*>(a.vc);
   const int32_t* __restrict__ bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  const size_t head_bytes = static_cast<size_t>(TV_BLOCK) * D * 2;
+  const size_t blk_bytes = static_cast<size_t>(a.H) * head_bytes;
+  const int last_blk = (T - 1) / TV_BLOCK, last_row = (T - 1) % TV_BLOCK;
 
-  // Q^T operand (B of S^T): lane holds Q[n = 16qt + lr][32c + 8lg .. +7].
-  // Kept in registers, or - when registers are short (64 queries, D = 128) -
-  // in LDS with rows padded by 16 bytes so the 16 rows of one read fall in
-  // different banks.
-  constexpr bool kQInLds = (NQT == 4 && D == 128);
-  constexpr int QROW = D + 8;                      // bf16 elements per LDS row
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kQInLds ? NQ * QROW : 8];
-  bf16x8 qv[kQInLds ? 1 : NQT][KC];
-  uint64_t ancq[NQT];
+  // Q^T operand of this wave's query tile, and the tile's ancestor masks
+  const bool computes = wave < NQT;
+  const int n_q = 16 * wave + lr;
+  bf16x8 qv[KC];
+  uint64_t ancq = 0;
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    const int n = 16 * qt + lr;
-    ancq[qt] = n < N ? a.anc[static_cast<size_t>(b) * N + n] : 0ull;
+  for (int c = 0; c < KC; ++c) qv[c] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  if (computes && n_q < N) {
+    ancq = a.anc[static_cast<size_t>(b) * N + n_q];
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      qv[c] = as_bf16x8(*reinterpret_cast<const uint4*>(
+          qg + ((static_cast<size_t>(b) * N + n_q) * a.H + h) * D + 32 * c + 8 * lg));
   }
-  if constexpr (kQInLds) {
-    for (int e = threadIdx.x; e < NQ * (D / 8); e += kThreads) {
-      const int n = e / (D / 8), c8 = e - n * (D / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < N)
-        v = *reinterpret_cast<const uint4*>(qg + ((static_cast<size_t>(b) * N + n) * a.H + h) * D + 8 * c8);
-      *reinterpret_cast<uint4*>(q_lds + n * QROW + 8 * c8) = v;
+
+  // Block ids of the chunk, validated once and kept in LDS.
+  const int blk_first = k_begin / TV_BLOCK;
+  const int nblk = (k_end - 1) / TV_BLOCK - blk_first + 1;      // <= kMaxChunkBlocks
+  for (int i = threadIdx.x; i < nblk; i += kThreads) {
+    int blk = bt[blk_first + i];
+    if (blk < 0 || blk >= a.num_blocks) {
+      s_badblk = 1;
+      blk = 0;
     }
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int qt = 0; qt < (kQInLds ? 1 : NQT); ++qt) {
-      const int n = 16 * qt + lr;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (n < N)
-          v = *reinterpret_cast<const uint4*>(qg + ((static_cast<size_t>(b) * N + n) * a.H + h) * D +
-                                              32 * c + 8 * lg);
-        qv[qt][c] = as_bf16x8(v);
-      }
-    }
+    s_blk[i] = blk;
   }
-  auto q_operand = [&](int qt, int c) -> bf16x8 {
-    if constexpr (kQInLds)
-      return as_bf16x8(*reinterpret_cast<const uint4*>(q_lds + (16 * qt + lr) * QROW + 32 * c + 8 * lg));
-    else
-      return qv[qt][c];
-  };
+  __syncthreads();
 
-  // selection matrices for the V transpose: B[k][n] = (k == 16*hh + n)
-  bf16x8 sel[2];
+  // Issue this wave's share of stage `st` into `dst` (K tile then V tile).
+  // Each 1 KB load covers 64/CPR consecutive keys of one cache block, so its
+  // block id is uniform across the wave.  The loads go HBM -> LDS directly;
+  // they are issued and awaited by hand (see the pipeline below).
+  auto issue = [&](int st, uint8_t* dst) {
+    const int t0 = k_begin + SK * st;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    uint4 v;
-    uint32_t w[4];
-#pragma unroll
-    for (int j2 = 0; j2 < 4; ++j2) {
-      const int k0 = 8 * lg + 2 * j2;
-      const uint32_t lo = (k0 == 16 * hh + lr) ? 0x3F80u : 0u;
-      const uint32_t hi = (k0 + 1 == 16 * hh + lr) ? 0x3F80u : 0u;
-      w[j2] = lo | (hi << 16);
-    }
-    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
-    sel[hh] = as_bf16x8(v);
-  }
-
-  f32x4 o[NQT][DT];
-  float mrun[NQT], lrun[NQT];
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    mrun[qt] = -INFINITY;
-    lrun[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const size_t head_off = static_cast<size_t>(h) * TV_BLOCK * D;
-  const size_t blk_stride = static_cast<size_t>(a.H) * TV_BLOCK * D;
-  int badblk = 0;
-
-  // one 32-key step: keys t0 .. t0+31 as two 16-key tiles
-  auto load_step = [&](int t0, bf16x8 (&kv)[2][KC], bf16x8 (&vv)[2][KC]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int tt = t0 + 16 * kt;
-      int blk = -1;
-      if (tt < T) {
-        blk = bt[tt / TV_BLOCK];
-        if (blk < 0 || blk >= a.num_blocks) {
-          badblk = 1;
-          blk = -1;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-        if (blk >= 0) {
-          const size_t off = blk * blk_stride + head_off + static_cast<size_t>(lr) * D + 32 * c + 8 * lg;
-          kx = *reinterpret_cast<const uint4*>(kg + off);
-          vx = *reinterpret_cast<const uint4*>(vg + off);
-          if (tt + lr >= T) vx = make_uint4(0, 0, 0, 0);   // rows past the last slot
-        }
-        kv[kt][c] = as_bf16x8(kx);
-        vv[kt][c] = as_bf16x8(vx);
-      }
+    for (int r = 0; r < LPW; ++r) {
+      const int li = wave * LPW + r;                 // 1 KB load index within the stage
+      const int which = li / (TILE / 1024);          // 0 = K, 1 = V
+      const int lt = li % (TILE / 1024);
+      const int key0 = lt * (64 / CPR);              // first key of this load
+      int blk_i = (t0 + key0) / TV_BLOCK;
+      const bool past_blk = blk_i > last_blk;
+      if (past_blk) blk_i = last_blk;
+      const int blk = __builtin_amdgcn_readfirstlane(s_blk[blk_i - blk_first]);
+      const int p = lt * 64 + lane;                  // 16-byte slot within the tile
+      const int key = p / CPR, phys = p % CPR;
+      const int c16 = swz<D>(key, phys);             // XOR swizzle is its own inverse
+      int row = (t0 + key) % TV_BLOCK;
+      if (past_blk || (blk_i == last_blk && row > last_row)) row = last_row;   // past the last slot
+      const uint8_t* src = (which ? vg : kg) + static_cast<size_t>(blk) * blk_bytes + h * head_bytes +
+                           static_cast<size_t>(row) * D * 2 + c16 * 16;
+      const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + which * TILE + lt * 1024));
+      // lane i's 16 bytes land at M0 + 16 * i
+      asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds_addr) : "memory");
     }
   };
 
-  // Register prefetch of the next step, except for the widest variant where
-  // the registers are needed for the accumulators.
-  constexpr bool kPrefetch = !(NQT == 4 && D == 128);
-  bf16x8 kv[2][KC], vv[2][KC], kn[kPrefetch ? 2 : 1][KC], vn[kPrefetch ? 2 : 1][KC];
-  int t0 = k_begin + 32 * wave;
-  if (t0 < k_end) load_step(t0, kv, vv);
-  for (; t0 < k_end; t0 += 128) {
-    const int t1 = t0 + 128;
-    if constexpr (kPrefetch) {
-      if (t1 < k_end) load_step(t1, kn, vn);
-    }
-
-    // 1) scores, online-softmax update and P^T operands for every query tile
-    bf16x8 pb[NQT];
-    float corr[NQT];
-    int rescale[NQT];
+  f32x4 o[DT];
+  float mrun = -INFINITY, lrun = 0.f;
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int st, const uint8_t* cur) {
+    const int t0 = k_begin + SK * st;
+    const uint8_t* kt_base = cur;
+    const uint8_t* vt_base = cur + TILE;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      // ---- scores S^T for 32 keys ----
       f32x4 sc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        const int r = 32 * sub + 16 * kt + lr;
         f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[kt][c], q_operand(qt, c), acc, 0, 0, 0);
+        for (int c = 0; c < KC; ++c) {
+          const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(kt_base + tile_off<D>(r, 4 * c + lg)));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[c], acc, 0, 0, 0);
+        }
         sc[kt] = acc;
       }
-      // mask + scale; lane holds keys t0 + 16kt + 4lg + i for query 16qt + lr
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * kt + 4 * lg + i;
+          const int t = t0 + 32 * sub + 16 * kt + 4 * lg + i;
           bool vis = t < T;
-          if (t >= L) vis = vis && ((ancq[qt] >> ((t - L) & 63)) & 1ull);
+          if (t >= L) vis = vis && ((ancq >> ((t - L) & 63)) & 1ull);
           const float v = vis ? sc[kt][i] * a.scale_log2 : -INFINITY;
           sc[kt][i] = v;
           mx = fmaxf(mx, v);
@@ -310,20 +300,23 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Lazy rescaling: the running max only moves (and O is only rescaled)
-      // when this tile's max exceeds it by more than 2^8; otherwise
-      // probabilities up to 256 are accumulated against the old max, which
-      // is exact in the final O / l.
-      rescale[qt] = __any(mx > mrun[qt] + 8.f);
-      if (rescale[qt]) {
-        const float m_new = fmaxf(mrun[qt], mx);
-        const float m_use_new = m_new == -INFINITY ? 0.f : m_new;
-        corr[qt] = tv::exp2_fast(mrun[qt] - m_use_new);
-        mrun[qt] = m_new;
+      // Lazy rescaling: the running max moves (and O is rescaled) only when
+      // this tile's max exceeds it by more than 2^8; otherwise probabilities
+      // up to 256 are accumulated against the old max (exact in O / l).
+      const int rescale = __any(mx > mrun + 8.f);
+      float corr = 1.f;
+      if (rescale) {
+        const float m_new = fmaxf(mrun, mx);
+        corr = tv::exp2_fast(mrun - (m_new == -INFINITY ? 0.f : m_new));
+        mrun = m_new;
+        lrun *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          o[dt][0] *= corr; o[dt][1] *= corr; o[dt][2] *= corr; o[dt][3] *= corr;
+        }
       }
-      const float m_use = mrun[qt] == -INFINITY ? 0.f : mrun[qt];
+      const float m_use = mrun == -INFINITY ? 0.f : mrun;
       f32x4 p[2];
-      float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -331,116 +324,94 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
           const float e = tv::exp2_fast(sc[kt][i] - m_use);
           const float eb = tv::bf16_to_f32(tv::f32_to_bf16(e));   // the value the PV product uses
           p[kt][i] = eb;
-          psum += eb;
+          lrun += eb;
         }
       }
-      if (rescale[qt]) lrun[qt] *= corr[qt];
-      lrun[qt] += psum;
-      pb[qt] = pack8(p[0], p[1]);
+      const bf16x8 pb = pack8(p[0], p[1]);
+      // ---- O^T += V^T P^T: V^T operand from two LDS transpose reads ----
+      // lane s of group lg supplies row 32sub + 16*half + 4lg + s/4, dims
+      // 16dt + 4(s%4) .. +3; lane j then holds those 4 rows at dim 16dt + j
+      const int vrow0 = 32 * sub + 4 * lg + (lr >> 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d0 = 16 * dt + 4 * (lr & 3);
+        const int c16 = d0 >> 3, within = (d0 & 7) * 2;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0, c16) + within));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0 + 16, c16) + within));
+        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+        const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[dt], 0, 0, 0);
+      }
     }
+  };
 
-    // 2) V^T tiles for this step (A operand of the PV product), 3) O^T += V^T P^T
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const f32x4 z{0.f, 0.f, 0.f, 0.f};
-        const f32x4 t_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[0][c], sel[hh], z, 0, 0, 0);
-        const f32x4 t_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[1][c], sel[hh], z, 0, 0, 0);
-        const bf16x8 va = pack8(t_lo, t_hi);
-        const int dt = 2 * c + hh;
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-          f32x4 acc = o[qt][dt];
-          if (rescale[qt]) {
-            acc[0] *= corr[qt]; acc[1] *= corr[qt]; acc[2] *= corr[qt]; acc[3] *= corr[qt];
-          }
-          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qt], acc, 0, 0, 0);
-        }
-      }
-    }
-    if constexpr (kPrefetch) {
-      if (t1 < k_end) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            kv[kt][c] = kn[kt][c];
-            vv[kt][c] = vn[kt][c];
-          }
-      }
+  // ---- pipeline: two stages in flight ----
+  // Each wave waits for its own loads of the stage it is about to read
+  // (vmcnt: at most LPW loads - the next stage's - may still be in flight),
+  // then a barrier makes the whole stage visible; a second barrier after
+  // the compute frees the buffer for the stage after next.
+  auto wait_stage = [&](bool next_in_flight) {
+    if (next_in_flight) {
+      if constexpr (LPW == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     } else {
-      if (t1 < k_end) load_step(t1, kv, vv);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+  };
+  auto step = [&](int it, uint8_t* cur) {
+    wait_stage(it + 1 < nst);
+    asm volatile("s_barrier" ::: "memory");
+    if (computes) compute(it, cur);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (it + 2 < nst) issue(it + 2, cur);
+  };
+  issue(0, stage_buf0);
+  // A wait the compiler can see: the Q and mask loads above are complete
+  // from here on, so it adds no wait of its own inside the loop (such a
+  // wait would also drain the next stage's loads, which it does not know).
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
+  if (nst > 1) issue(1, stage_buf1);
+  for (int it = 0; it < nst; it += 2) {
+    step(it, stage_buf0);
+    if (it + 1 < nst) step(it + 1, stage_buf1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-  // ---- combine the 4 waves: wave 0 absorbs waves 1, 2, 3 through LDS ----
-  __shared__ float po[NQ * D];
-  __shared__ float pm[NQ], pl[NQ];
+  lrun += __shfl_xor(lrun, 16, 64);
+  lrun += __shfl_xor(lrun, 32, 64);
+  __syncthreads();
+  if (s_badblk && threadIdx.x == 0) a.status[b] = TV_REQ_BAD_BLOCK;
+
+  if (a.splits == 1) {
+    if (computes && n_q < N) {
+      uint16_t* out = static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(b) * N + n_q) * a.H + h) * D;
+      const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    lrun[qt] += __shfl_xor(lrun[qt], 16, 64);
-    lrun[qt] += __shfl_xor(lrun[qt], 32, 64);
-  }
-  if (badblk) s_badblk = 1;
-  for (int src = 1; src < 4; ++src) {
-    if (wave == src) {
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        const int n = 16 * qt + lr;
-        if (lg == 0) {
-          pm[n] = mrun[qt];
-          pl[n] = lrun[qt];
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(po + n * D + 16 * dt + 4 * lg) = o[qt][dt];
+      for (int dt = 0; dt < DT; ++dt) {
+        uint2 v;
+        v.x = tv::pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+        v.y = tv::pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+        *reinterpret_cast<uint2*>(out + 16 * dt + 4 * lg) = v;
       }
     }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        const int n = 16 * qt + lr;
-        const float m2 = pm[n], l2 = pl[n];
-        const float M = fmaxf(mrun[qt], m2);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        const float w1 = tv::exp2_fast(mrun[qt] - Mu), w2 = tv::exp2_fast(m2 - Mu);
-        mrun[qt] = M;
-        lrun[qt] = lrun[qt] * w1 + l2 * w2;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(po + n * D + 16 * dt + 4 * lg);
-          f32x4 r = o[qt][dt];
-          r[0] = r[0] * w1 + x[0] * w2;
-          r[1] = r[1] * w1 + x[1] * w2;
-          r[2] = r[2] * w1 + x[2] * w2;
-          r[3] = r[3] * w1 + x[3] * w2;
-          o[qt][dt] = r;
-        }
-      }
-    }
-    __syncthreads();
-  }
-  if (s_badblk) {
-    if (threadIdx.x == 0) a.status[b] = TV_REQ_BAD_BLOCK;
     return;
   }
-  if (wave == 0) {
+  // ---- several chunks: write this chunk's unnormalised partial ----
+  // (merged by attn_merge_kernel after this kernel; the kernel boundary makes
+  // the partials of every XCD's L2 visible, no device-scope fence is needed)
+  const size_t pbase = ((static_cast<size_t>(b) * a.H + h) * a.splits + s) * a.npad;
+  if (computes && n_q < N) {
+    float* po = a.part_o + (pbase + n_q) * D;
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      const int n = 16 * qt + lr;
-      if (lg == 0) {
-        pm[n] = mrun[qt];
-        pl[n] = lrun[qt];
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4*>(po + n * D + 16 * dt + 4 * lg) = o[qt][dt];
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lg) = o[dt];
+    if (lg == 0) {
+      a.part_ml[(pbase + n_q) * 2 + 0] = mrun;
+      a.part_ml[(pbase + n_q) * 2 + 1] = lrun;
     }
   }
-  __syncthreads();
-  write_result<uint16_t>(a, b, h, s, po, pm, pl, min(NQ, N));
 }
 
 // ===========================================================================
@@ -568,44 +539,56 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(AttnArgs a) {
 }
 
 // ===========================================================================
-// Split merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// Split merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One thread per 4 output dims of (b, n, h): the loads of a thread are
+// independent, so the kernel runs at the speed of its reads.
 // ===========================================================================
-constexpr int kMaxSplits = 64;
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float x0, float x1, float x2, float x3);
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float x0, float x1, float x2, float x3) {
+  uint2 v;
+  v.x = tv::pack_bf16x2(x0, x1);
+  v.y = tv::pack_bf16x2(x2, x3);
+  *reinterpret_cast<uint2*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float x0, float x1, float x2, float x3) {
+  *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
+}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  __shared__ float w_s[kMaxSplits * 64];
-  __shared__ float inv_l[64];
+  const int D4 = a.D / 4;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const size_t total = static_cast<size_t>(a.B) * a.N * a.H * D4;
+  if (idx >= total) return;
+  const int d4 = static_cast<int>(idx % D4);
+  const int h = static_cast<int>((idx / D4) % a.H);
+  const int n = static_cast<int>((idx / D4 / a.H) % a.N);
+  const int b = static_cast<int>(idx / D4 / a.H / a.N);
+  T* out = static_cast<T*>(a.out) + ((static_cast<size_t>(b) * a.N + n) * a.H + h) * a.D + 4 * d4;
   if (a.status[b] != TV_REQ_OK) {
-    zero_out<T>(a, b, h);
+    store4<T>(out, 0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const int N = a.N;
-  const int T_ = a.prefix_len[b] + N;
+  const int T_ = a.prefix_len[b] + a.N;
   const int Sb = min(a.splits, (T_ + a.chunk - 1) / a.chunk);
-  const size_t base = (static_cast<size_t>(b) * a.H + h) * a.splits;
-  for (int n = threadIdx.x; n < N; n += kThreads) {
-    float M = -INFINITY;
-    for (int s = 0; s < Sb; ++s) M = fmaxf(M, a.part_ml[((base + s) * a.npad + n) * 2]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float l = 0.f;
-    for (int s = 0; s < Sb; ++s) {
-      const float w = tv::exp2_fast(a.part_ml[((base + s) * a.npad + n) * 2] - Mu);
-      w_s[s * 64 + n] = w;
-      l += w * a.part_ml[((base + s) * a.npad + n) * 2 + 1];
-    }
-    inv_l[n] = l > 0.f ? 1.f / l : 0.f;
+  const size_t bh = (static_cast<size_t>(b) * a.H + h) * a.splits;
+  float M = -INFINITY;
+  for (int s = 0; s < Sb; ++s) M = fmaxf(M, a.part_ml[((bh + s) * a.npad + n) * 2]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float l = 0.f;
+  f32x4 acc{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < Sb; ++s) {
+    const size_t row = (bh + s) * a.npad + n;
+    const float w = tv::exp2_fast(a.part_ml[row * 2] - Mu);
+    l += w * a.part_ml[row * 2 + 1];
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + row * a.D + 4 * d4);
+    acc[0] += w * x[0]; acc[1] += w * x[1]; acc[2] += w * x[2]; acc[3] += w * x[3];
   }
-  __syncthreads();
-  T* out = static_cast<T*>(a.out);
-  const int D = a.D;
-  for (int e = threadIdx.x; e < N * D; e += kThreads) {
-    const int n = e / D, d = e - n * D;
-    float acc = 0.f;
-    for (int s = 0; s < Sb; ++s) acc += w_s[s * 64 + n] * a.part_o[((base + s) * a.npad + n) * D + d];
-    store_out<T>(out + ((static_cast<size_t>(b) * N + n) * a.H + h) * D + d, acc * inv_l[n]);
-  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  store4<T>(out, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
 }
 
 // ===========================================================================
@@ -613,22 +596,33 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
 // ===========================================================================
 struct Plan {
   int chunk, splits, npad;
-  size_t ws_bytes;
+  size_t off_ml, ws_bytes;
 };
 
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Chunking of the key range: about 512 workgroups (two per CU) when the
+// prefixes are long enough, chunks of at least 256 keys, a multiple of 64.
 Plan make_plan(int B, int N, int H, int D, int max_blocks) {
   Plan p;
   const long keys_max = static_cast<long>(max_blocks) * TV_BLOCK;
   const long bh = static_cast<long>(B) * H;
-  long s = (1024 + bh - 1) / bh;                       // aim for >= 1024 workgroups
-  s = std::min(s, (keys_max + 511) / 512);             // chunks of at least ~512 keys
+  long s = (512 + bh - 1) / bh;
+  s = std::min(s, (keys_max + 255) / 256);
   s = std::max(1L, std::min(s, static_cast<long>(kMaxSplits)));
+  s = std::max(s, (keys_max + kMaxChunkKeys - 1) / kMaxChunkKeys);
   long c = (keys_max + s - 1) / s;
-  c = (c + 127) / 128 * 128;
+  c = (c + 63) / 64 * 64;
   p.chunk = static_cast<int>(c);
   p.splits = static_cast<int>((keys_max + c - 1) / c);
   p.npad = (N + 15) / 16 * 16;
-  p.ws_bytes = p.splits > 1 ? static_cast<size_t>(B) * H * p.splits * p.npad * (D + 2) * sizeof(float) : 0;
+  if (p.splits > 1) {
+    const size_t rows = static_cast<size_t>(B) * H * p.splits * p.npad;
+    p.off_ml = align256(rows * D * sizeof(float));
+    p.ws_bytes = p.off_ml + align256(rows * 2 * sizeof(float));
+  } else {
+    p.off_ml = p.ws_bytes = 0;
+  }
   return p;
 }
 
@@ -669,8 +663,9 @@ extern "C" tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, f
   a.q = q; a.kc = k_cache; a.vc = v_cache;
   a.num_blocks = num_blocks; a.block_table = block_table; a.max_blocks = max_blocks;
   a.prefix_len = prefix_len; a.anc = anc; a.status = status; a.out = out;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_ml = p.ws_bytes ? a.part_o + static_cast<size_t>(B) * H * p.splits * p.npad * D : nullptr;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.part_o = p.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_ml = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
   a.chunk = p.chunk; a.splits = p.splits; a.npad = p.npad;
 
   const dim3 grid(p.splits, H, B);
@@ -691,18 +686,19 @@ extern "C" tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, f
         default: launch_mfma<64, 4>(grid, stream, a); break;
       }
     }
+  } else if (D == 128) {
+    hipLaunchKernelGGL(attn_valu_kernel<128>, grid, dim3(kThreads), 0, stream, a);
   } else {
-    if (D == 128)
-      hipLaunchKernelGGL(attn_valu_kernel<128>, grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(attn_valu_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_valu_kernel<64>, grid, dim3(kThreads), 0, stream, a);
   }
   if (hipGetLastError() != hipSuccess) return TV_EHIP;
   if (p.splits > 1) {
+    const size_t threads = static_cast<size_t>(B) * N * H * (D / 4);
+    const dim3 mgrid(static_cast<unsigned>((threads + kThreads - 1) / kThreads));
     if (dt == TV_BF16)
-      hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, dim3(H, B), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, mgrid, dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(attn_merge_kernel<float>, dim3(H, B), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(attn_merge_kernel<float>, mgrid, dim3(kThreads), 0, stream, a);
   }
   return tv::launch_status();
 }

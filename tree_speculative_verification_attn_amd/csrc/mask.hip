@@ -2,7 +2,8 @@
 //
 // TreeMask (SpecInfer summary, "Tree-based Parallel Decoding: Topology-Aware
 // Causal Mask"): node u may attend node v iff v is u or one of u's ancestors.
-// One wave64 per request; lane i owns node i.  Each lane climbs its parent
+// One wave64 per request; lane i owns node i.  parent[i] = -2 marks a padding
+// slot: no ancestors, nobody's child, never a parent.  Each lane climbs its parent
 // chain through cross-lane reads (depth <= 64 steps), so no mask is ever
 // materialised on the host.
 #include "tv_common.h"
@@ -17,17 +18,21 @@ __global__ __launch_bounds__(64) void build_mask_kernel(int N, const int32_t* __
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   const bool live = i < N;
-  const int p = live ? parent[static_cast<size_t>(b) * N + i] : -1;
-  const int bad = __any(live && (p < -1 || p >= i));
+  // parent -2 marks a padding slot (trees of different sizes in one batch);
+  // lanes past N behave like padding
+  const int p = live ? parent[static_cast<size_t>(b) * N + i] : -2;
+  const int pp = __shfl(p, p >= 0 ? p : 0, 64);      // parent of my parent
+  const int bad = __any(live && (p < -2 || p >= i || (p >= 0 && pp == -2)));
+  const bool node = live && p != -2;
 
   uint64_t a = 0;
   int d = 0;
-  if (!bad && live) {
+  if (!bad && node) {
     a = 1ull << i;
     d = 1;
   }
   // climb: cur = current ancestor of node i (-1 = reached the root)
-  int cur = bad ? -1 : p;
+  int cur = (bad || !node) ? -1 : p;
   for (int step = 0; step < N; ++step) {
     const int any_left = __any(cur >= 0);
     if (!any_left) break;

@@ -212,8 +212,63 @@ __device__ RowStat merge_row(const Stats& st, size_t row, bool with_sum) {
   return r;
 }
 
+// Per-request small arrays staged in LDS by the walk kernels.
+struct ReqLds {
+  int tok[TV_MAX_NODES];
+  int qrow[TV_MAX_NODES];
+  uint64_t child[TV_MAX_NODES + 1];
+  // merged statistics of every row (root + nodes)
+  float m[TV_MAX_NODES + 1];
+  double s[TV_MAX_NODES + 1];
+  int arg[TV_MAX_NODES + 1];
+  int ok[TV_MAX_NODES + 1];
+};
+
+// Load tokens, draft rows and child masks, merge every row's pieces, and run
+// the up-front checks.  Returns the request status (shared by all threads).
+// Tokens and draft rows are only checked for nodes that are somebody's child
+// (padding slots are nobody's child).
+__device__ int stage_request(ReqLds& R, int b, int N, int V, int Rrows, const int32_t* token,
+                             const int32_t* q_row, const uint64_t* child, const Stats& st,
+                             bool with_sum, int status_in, uint64_t* s_real, int* s_flag) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    *s_real = 0ull;
+    *s_flag = 0;
+  }
+  __syncthreads();
+  for (int i = t; i <= N; i += blockDim.x) {
+    const uint64_t c = child[static_cast<size_t>(b) * (N + 1) + i] & later_nodes(i - 1, N);
+    R.child[i] = c;
+    if (c) atomicOr(reinterpret_cast<unsigned long long*>(s_real), static_cast<unsigned long long>(c));
+    const RowStat r = merge_row(st, static_cast<size_t>(b) * (N + 1) + i, with_sum);
+    R.m[i] = r.m;
+    R.s[i] = r.s;
+    R.arg[i] = r.arg;
+    R.ok[i] = r.ok;
+  }
+  for (int i = t; i < N; i += blockDim.x) {
+    R.tok[i] = token[static_cast<size_t>(b) * N + i];
+    R.qrow[i] = q_row ? q_row[static_cast<size_t>(b) * N + i] : 0;
+  }
+  __syncthreads();
+  const uint64_t real = *s_real;
+  for (int i = t; i < N; i += blockDim.x) {
+    if ((real >> i) & 1ull) {
+      if (R.tok[i] < 0 || R.tok[i] >= V) atomicOr(s_flag, 1);
+      if (q_row && (R.qrow[i] < 0 || R.qrow[i] >= Rrows)) atomicOr(s_flag, 2);
+    }
+  }
+  __syncthreads();
+  if (status_in != TV_REQ_OK) return status_in;
+  const int f = *s_flag;
+  if (f & 1) return TV_REQ_BAD_TOKEN;
+  if (f & 2) return TV_REQ_BAD_QROW;
+  return TV_REQ_OK;
+}
+
 // ---------------------------------------------------------------------------
-// Phase 2a: greedy walk, one wave per request.
+// Phase 2a: greedy walk, one workgroup of one wave per request.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void greedy_walk_kernel(int N, int V, const int32_t* __restrict__ token,
                                                          const uint64_t* __restrict__ child,
@@ -222,53 +277,53 @@ __global__ __launch_bounds__(64) void greedy_walk_kernel(int N, int V, const int
                                                          int32_t* __restrict__ num_accepted,
                                                          int32_t* __restrict__ bonus, Stats st) {
   const int b = blockIdx.x;
-  const int i = threadIdx.x;
-  const int32_t* tok = token + static_cast<size_t>(b) * N;
-  if (i < N) accepted[static_cast<size_t>(b) * N + i] = -1;
-  int stt = status[b];
-  if (stt == TV_REQ_OK) {
-    const int bad = __any(i < N && (tok[i] < 0 || tok[i] >= V));
-    if (bad) stt = TV_REQ_BAD_TOKEN;
-  }
-  if (i != 0) return;
-  int k = 0, bn = -1;
-  if (stt == TV_REQ_OK) {
-    int u = -1;
-    while (true) {
-      const RowStat r = merge_row(st, static_cast<size_t>(b) * (N + 1) + (u + 1), false);
-      if (!r.ok) {
-        stt = TV_REQ_NONFINITE;
-        break;
-      }
-      const int o = r.arg;
-      uint64_t kids = child[static_cast<size_t>(b) * (N + 1) + (u + 1)] & later_nodes(u, N);
-      int nxt = -1;
-      while (kids) {
-        const int c = __builtin_ctzll(kids);
-        kids &= kids - 1;
-        if (tok[c] == o) {
-          nxt = c;
+  const int t = threadIdx.x;
+  __shared__ ReqLds R;
+  __shared__ uint64_t s_real;
+  __shared__ int s_flag, s_k;
+  __shared__ int s_acc[TV_MAX_NODES];
+  int stt = stage_request(R, b, N, V, 0, token, nullptr, child, st, false, status[b], &s_real, &s_flag);
+  if (t == 0) {
+    int k = 0, bn = -1;
+    if (stt == TV_REQ_OK) {
+      int u = -1;
+      while (true) {
+        if (!R.ok[u + 1]) {
+          stt = TV_REQ_NONFINITE;
           break;
         }
+        const int o = R.arg[u + 1];
+        uint64_t kids = R.child[u + 1];
+        int nxt = -1;
+        while (kids) {
+          const int c = __builtin_ctzll(kids);
+          kids &= kids - 1;
+          if (R.tok[c] == o) {
+            nxt = c;
+            break;
+          }
+        }
+        if (nxt < 0) {
+          bn = o;
+          break;
+        }
+        s_acc[k++] = nxt;
+        u = nxt;
       }
-      if (nxt < 0) {
-        bn = o;
-        break;
-      }
-      accepted[static_cast<size_t>(b) * N + k] = nxt;
-      ++k;
-      u = nxt;
     }
+    if (stt != TV_REQ_OK) {
+      status[b] = stt;
+      num_accepted[b] = -1;
+      bonus[b] = -1;
+      k = 0;
+    } else {
+      num_accepted[b] = k;
+      bonus[b] = bn;
+    }
+    s_k = k;
   }
-  if (stt != TV_REQ_OK) {
-    for (int j = 0; j < k; ++j) accepted[static_cast<size_t>(b) * N + j] = -1;
-    status[b] = stt;
-    num_accepted[b] = -1;
-    bonus[b] = -1;
-  } else {
-    num_accepted[b] = k;
-    bonus[b] = bn;
-  }
+  __syncthreads();
+  for (int i = t; i < N; i += blockDim.x) accepted[static_cast<size_t>(b) * N + i] = i < s_k ? s_acc[i] : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -278,6 +333,10 @@ __global__ __launch_bounds__(64) void greedy_walk_kernel(int N, int V, const int
 // A rejection of a child proposed from q writes r'(x) = max(0, c(x) - Z q(x))
 // (c = exp(l - m) or r, Z = S or the old Z) into the other buffer, which
 // equals Z * max(0, p - q); Z' = sum r'.  If Z' = 0 the distribution is kept.
+//
+// Thread 0 makes every decision from LDS; each step that needs global data
+// is one parallel round trip: at a node, all children's target logits and
+// draft probabilities; after a residual pass, the children's new residuals.
 // ---------------------------------------------------------------------------
 struct MssArgs {
   int N, V, R;
@@ -296,244 +355,283 @@ struct MssArgs {
   float* resid;            // [B][2][V]
 };
 
-__device__ __forceinline__ double block_sum_1024(double v, double* red) {
+__device__ __forceinline__ double block_sum(double v, double* red) {
   v = tv::wave_sum(v);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
   if (lane == 0) red[wave] = v;
   __syncthreads();
   double s = 0.0;
-#pragma unroll
-  for (int w = 0; w < kWalkThreads / 64; ++w) s += red[w];
+  const int nw = blockDim.x >> 6;
+  for (int w = 0; w < nw; ++w) s += red[w];
   return s;
+}
+
+// Inclusive scan within a wave (double).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// The current distribution's unnormalised value at x.
+__device__ __forceinline__ float cur_value(int mode, const float* lrow, float m, const float* src, int x) {
+  if (mode == 0) {
+    const float l = lrow[x];
+    return l == -INFINITY ? 0.f : tv::exp_acc(l - m);
+  }
+  return src[x];
 }
 
 __global__ __launch_bounds__(kWalkThreads) void mss_walk_kernel(MssArgs a) {
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int N = a.N, V = a.V;
-  const int32_t* tok = a.token + static_cast<size_t>(b) * N;
-  const int32_t* qr = a.q_row + static_cast<size_t>(b) * N;
   const float* lbase = a.logits + static_cast<size_t>(b) * (N + 1) * V;
   const float* sbase = a.ssm + static_cast<size_t>(b) * a.R * V;
-  float* rbuf[2] = {a.resid + static_cast<size_t>(b) * 2 * V, a.resid + (static_cast<size_t>(b) * 2 + 1) * V};
+  float* rbuf0 = a.resid + static_cast<size_t>(b) * 2 * V;
 
-  __shared__ int s_status, s_done, s_action, s_mode, s_cur, s_row, s_qrow, s_k, s_rounds, s_bonus;
-  __shared__ float s_m;
-  __shared__ double s_Z, s_T;
+  __shared__ ReqLds R;
+  __shared__ uint64_t s_real;
+  __shared__ int s_flag;
+  __shared__ float lx_s[TV_MAX_NODES], qx_s[TV_MAX_NODES], rx_s[TV_MAX_NODES];
   __shared__ double red[kWalkThreads / 64];
   __shared__ int s_acc[TV_MAX_NODES];
-  __shared__ int s_flag, s_found;
-  __shared__ double s_excl[kWalkThreads];
+  // walk state (written by thread 0 only, read by all after a barrier)
+  __shared__ int s_status, s_action, s_u, s_mode, s_cur, s_qrow, s_slot, s_k, s_rounds, s_found;
+  __shared__ uint64_t s_untested;
+  __shared__ float s_m;
+  __shared__ double s_Z, s_T;
 
+  const int st0 = stage_request(R, b, N, V, a.R, a.token, a.q_row, a.child, a.st, true, a.status[b],
+                                &s_real, &s_flag);
   if (t == 0) {
-    s_status = a.status[b];
-    s_flag = 0;
-  }
-  __syncthreads();
-  if (s_status == TV_REQ_OK) {
-    int bt_ = 0, bq = 0;
-    if (t < N) {
-      bt_ = tok[t] < 0 || tok[t] >= V;
-      bq = qr[t] < 0 || qr[t] >= a.R;
+    s_status = st0;
+    s_u = -1;
+    s_slot = 0;
+    s_k = 0;
+    s_rounds = 0;
+    s_mode = 0;
+    s_cur = 0;
+    s_action = 0;   // 0 = enter node
+    if (st0 == TV_REQ_OK && !R.ok[0]) s_status = TV_REQ_NONFINITE;
+    if (s_status == TV_REQ_OK) {
+      s_m = R.m[0];
+      s_Z = R.s[0];
+      s_untested = R.child[0];
     }
-    if (bt_) atomicOr(&s_flag, 1);
-    if (bq) atomicOr(&s_flag, 2);
   }
   __syncthreads();
-  if (t == 0 && s_status == TV_REQ_OK) {
-    if (s_flag & 1) s_status = TV_REQ_BAD_TOKEN;
-    else if (s_flag & 2) s_status = TV_REQ_BAD_QROW;
-  }
 
-  // control state lives in thread 0's registers; shared copies drive passes
-  int u = -1, slot = 0, j = 0, k = 0, rounds = 0, mode = 0, cur = 0;
-  uint64_t untested = 0;
-  float m = 0.f;
-  double Z = 0.0;
-  if (t == 0) {
-    s_done = s_status != TV_REQ_OK;
-    if (!s_done) {
-      const RowStat r = merge_row(a.st, static_cast<size_t>(b) * (N + 1), true);
-      if (!r.ok) {
-        s_status = TV_REQ_NONFINITE;
-        s_done = 1;
-      } else {
-        m = r.m;
-        Z = r.s;
-        untested = a.child[static_cast<size_t>(b) * (N + 1)] & later_nodes(-1, N);
+  int j = 0;   // round at the current node (thread 0)
+  while (s_status == TV_REQ_OK) {
+    const int action = s_action;
+    const int u = s_u;
+    const int mode = s_mode, cb = s_cur;
+    const float* lrow = lbase + static_cast<size_t>(u + 1) * V;
+    const float mm = s_m;
+    const double ZZ = s_Z;
+    float* src = rbuf0 + static_cast<size_t>(cb) * V;
+
+    if (action == 0) {
+      // node entry: every child's target logit and draft probability at once
+      const uint64_t kids = s_untested;
+      if (t < N && ((kids >> t) & 1ull)) {
+        const int x = R.tok[t];
+        lx_s[t] = lrow[x];
+        qx_s[t] = sbase[static_cast<size_t>(R.qrow[t]) * V + x];
       }
-    }
-  }
-  __syncthreads();
-
-  while (!s_done) {
-    // ---- thread 0: ratio tests until a full-vocab pass is needed ----
-    if (t == 0) {
-      s_action = 0;  // 1 = residual pass, 2 = final sample
-      while (true) {
-        if (!untested) {
-          s_action = 2;
-          break;
+    } else if (action == 1) {
+      // residual pass after rejecting a child proposed from row s_qrow
+      const float* q = sbase + static_cast<size_t>(s_qrow) * V;
+      float* dst = rbuf0 + static_cast<size_t>(cb ^ 1) * V;
+      double acc = 0.0;
+      int bad = 0;
+      const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(q) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(lrow) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+      if (vec) {
+        for (int x4 = t; x4 < V / 4; x4 += kWalkThreads) {
+          const float4 qv = reinterpret_cast<const float4*>(q)[x4];
+          const float4 cv = mode == 0 ? reinterpret_cast<const float4*>(lrow)[x4]
+                                      : reinterpret_cast<const float4*>(src)[x4];
+          float c[4] = {cv.x, cv.y, cv.z, cv.w};
+          const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (mode == 0) c[e] = c[e] == -INFINITY ? 0.f : tv::exp_acc(c[e] - mm);
+            if (!(qq[e] >= 0.f) || qq[e] == INFINITY) bad = 1;
+            r[e] = static_cast<float>(fmax(0.0, static_cast<double>(c[e]) - ZZ * static_cast<double>(qq[e])));
+            acc += static_cast<double>(r[e]);
+          }
+          reinterpret_cast<float4*>(dst)[x4] = make_float4(r[0], r[1], r[2], r[3]);
         }
+      } else {
+        for (int x = t; x < V; x += kWalkThreads) {
+          const float c = cur_value(mode, lrow, mm, src, x);
+          const float qv = q[x];
+          if (!(qv >= 0.f) || qv == INFINITY) bad = 1;
+          const float r = static_cast<float>(fmax(0.0, static_cast<double>(c) - ZZ * static_cast<double>(qv)));
+          dst[x] = r;
+          acc += static_cast<double>(r);
+        }
+      }
+      if (bad) atomicOr(&s_flag, 4);
+      const double Znew = block_sum(acc, red);
+      const int flag = s_flag;
+      __syncthreads();
+      const bool take = !(flag & 4) && Znew > 0.0;
+      if (take) {
+        // the remaining children's values under the new distribution
+        const uint64_t kids = s_untested;
+        if (t < N && ((kids >> t) & 1ull)) rx_s[t] = dst[R.tok[t]];
+      }
+      if (t == 0) {
+        if (flag & 4) {
+          s_status = TV_REQ_NONFINITE;
+        } else if (take) {
+          s_mode = 1;
+          s_cur = cb ^ 1;
+          s_Z = Znew;
+        }
+      }
+    } else {
+      // final sample: smallest x with cumsum >= u2 * total; thread t owns a
+      // contiguous chunk, chunk sums are scanned across the workgroup
+      const int chunk = (V + kWalkThreads - 1) / kWalkThreads;
+      const int xa = min(V, t * chunk), xb = min(V, xa + chunk);
+      double part = 0.0;
+      for (int x = xa; x < xb; ++x) part += static_cast<double>(cur_value(mode, lrow, mm, src, x));
+      const double wincl = wave_incl_scan(part);
+      const int wave = t >> 6, lane = t & 63;
+      if (lane == 63) red[wave] = wincl;
+      __syncthreads();
+      double wbase = 0.0, total = 0.0;
+      for (int w2 = 0; w2 < kWalkThreads / 64; ++w2) {
+        if (w2 < wave) wbase += red[w2];
+        total += red[w2];
+      }
+      const double incl = wbase + wincl;
+      // the previous thread's inclusive sum, bit for bit: the same wave base
+      // plus its wave-scan value (lane 0: the base itself, which equals the
+      // last lane of the previous wave summed in the same order)
+      const double prev_w = __shfl_up(wincl, 1, 64);
+      const double excl = lane > 0 ? wbase + prev_w : wbase;
+      if (t == 0) {
+        const tv::u32x4 w = tv::mss_words(a.seed, a.offset, b, s_slot, 0);
+        s_T = tv::unit_open0(w.z) * total;
+        s_found = -1;
+      }
+      __syncthreads();
+      const double T = s_T;
+      // exactly one owner: the first thread whose inclusive sum reaches T
+      if (excl < T && incl >= T) {
+        double accd = excl;
+        int xs = -1, last_pos = -1;
+        for (int x = xa; x < xb; ++x) {
+          const float c = cur_value(mode, lrow, mm, src, x);
+          if (c > 0.f) last_pos = x;
+          accd += static_cast<double>(c);
+          if (accd >= T) {
+            xs = x;
+            break;
+          }
+        }
+        s_found = xs >= 0 ? xs : last_pos;   // rounding left the chunk short: last positive entry
+      }
+      __syncthreads();
+      if (t == 0) {
+        s_action = 3;   // done
+      }
+      __syncthreads();
+      break;
+    }
+    __syncthreads();
+
+    // ---- thread 0: ratio tests until a full-vocab pass is needed ----
+    if (t == 0 && s_status == TV_REQ_OK) {
+      int uu = s_u;
+      uint64_t untested = s_untested;
+      int md = s_mode;
+      float m_ = s_m;
+      double Z = s_Z;
+      int k = s_k, rounds = s_rounds, slot = s_slot;
+      int next = 2;     // default: final sample
+      while (untested) {
         const tv::u32x4 w = tv::mss_words(a.seed, a.offset, b, slot, j);
         const int mcnt = __builtin_popcountll(untested);
         int idx = tv::pick_index(w.x, mcnt);
         uint64_t bits = untested;
         while (idx--) bits &= bits - 1;
         const int sidx = __builtin_ctzll(bits);
-        const int x = tok[sidx];
-        const float qx = sbase[static_cast<size_t>(qr[sidx]) * V + x];
+        const float qx = qx_s[sidx];
         if (!(qx >= 0.f) || qx == INFINITY) {
           s_status = TV_REQ_NONFINITE;
-          s_action = 3;
+          next = -1;
           break;
         }
         double px;
-        if (mode == 0) {
-          const float lx = lbase[static_cast<size_t>(u + 1) * V + x];
-          px = lx == -INFINITY ? 0.0 : exp(static_cast<double>(lx) - static_cast<double>(m)) / Z;
+        if (md == 0) {
+          const float lx = lx_s[sidx];
+          px = lx == -INFINITY ? 0.0 : exp(static_cast<double>(lx) - static_cast<double>(m_)) / Z;
         } else {
-          px = static_cast<double>(rbuf[cur][x]) / Z;
+          px = static_cast<double>(rx_s[sidx]) / Z;
         }
         const double ratio = qx > 0.f ? px / static_cast<double>(qx) : (px > 0.0 ? INFINITY : 0.0);
         const double u1 = tv::unit_open0(w.y);
         ++rounds;
         if (u1 <= ratio) {
-          if (k < TV_MAX_NODES) s_acc[k] = sidx;
-          ++k;
-          u = sidx;
+          s_acc[k++] = sidx;
+          uu = sidx;
           slot = sidx + 1;
           j = 0;
-          const RowStat r = merge_row(a.st, static_cast<size_t>(b) * (N + 1) + slot, true);
-          if (!r.ok) {
+          if (!R.ok[slot]) {
             s_status = TV_REQ_NONFINITE;
-            s_action = 3;
+            next = -1;
             break;
           }
-          m = r.m;
-          Z = r.s;
-          mode = 0;
-          untested = a.child[static_cast<size_t>(b) * (N + 1) + slot] & later_nodes(u, N);
-          continue;
-        }
-        // rejection: residual pass over the full vocabulary
-        untested &= ~(1ull << sidx);
-        ++j;
-        s_qrow = qr[sidx];
-        s_action = 1;
-        break;
-      }
-      s_mode = mode;
-      s_cur = cur;
-      s_row = u + 1;
-      s_m = m;
-      s_Z = Z;
-      s_flag = 0;
-    }
-    __syncthreads();
-    const int action = s_action;
-    if (action == 3) break;
-    const int md = s_mode, cb = s_cur;
-    const float* lrow = lbase + static_cast<size_t>(s_row) * V;
-    const float mm = s_m;
-    const double ZZ = s_Z;
-    if (action == 1) {
-      const float* q = sbase + static_cast<size_t>(s_qrow) * V;
-      const float* src = rbuf[cb];
-      float* dst = rbuf[cb ^ 1];
-      double acc = 0.0;
-      int bad = 0;
-      for (int x = t; x < V; x += kWalkThreads) {
-        const float c = md == 0 ? (lrow[x] == -INFINITY ? 0.f : tv::exp_acc(lrow[x] - mm)) : src[x];
-        const float qv = q[x];
-        if (!(qv >= 0.f) || qv == INFINITY) bad = 1;
-        const double r = fmax(0.0, static_cast<double>(c) - ZZ * static_cast<double>(qv));
-        const float rf = static_cast<float>(r);
-        dst[x] = rf;
-        acc += static_cast<double>(rf);
-      }
-      if (bad) atomicOr(&s_flag, 1);
-      const double Znew = block_sum_1024(acc, red);
-      if (t == 0) {
-        if (s_flag) {
-          s_status = TV_REQ_NONFINITE;
-          s_done = 1;
-        } else if (Znew > 0.0) {
-          mode = 1;
-          cur ^= 1;
-          Z = Znew;
-        }
-        // Znew == 0: keep the current distribution (zero-normaliser guard)
-      }
-      __syncthreads();
-      continue;
-    }
-    // ---- action 2: final sample, smallest x with cumsum >= u2 * total ----
-    const int chunk = (V + kWalkThreads - 1) / kWalkThreads;
-    const int xa = min(V, t * chunk), xb = min(V, xa + chunk);
-    const float* src = rbuf[cb];
-    double part = 0.0;
-    for (int x = xa; x < xb; ++x) {
-      const float c = md == 0 ? (lrow[x] == -INFINITY ? 0.f : tv::exp_acc(lrow[x] - mm)) : src[x];
-      part += static_cast<double>(c);
-    }
-    // exclusive scan of the per-thread sums
-    s_excl[t] = part;
-    __syncthreads();
-    for (int o = 1; o < kWalkThreads; o <<= 1) {
-      const double add = t >= o ? s_excl[t - o] : 0.0;
-      __syncthreads();
-      s_excl[t] += add;
-      __syncthreads();
-    }
-    const double incl = s_excl[t];
-    const double excl = t > 0 ? s_excl[t - 1] : 0.0;   // the previous thread's inclusive sum
-    if (t == 0) {
-      const tv::u32x4 w = tv::mss_words(a.seed, a.offset, b, slot, 0);
-      s_T = tv::unit_open0(w.z) * s_excl[kWalkThreads - 1];
-      s_found = -1;
-    }
-    __syncthreads();
-    const double T = s_T;
-    // exactly one thread has excl < T <= incl (sums are non-negative)
-    if (excl < T && incl >= T) {
-      double accd = excl;
-      int xs = -1, last_pos = -1;
-      for (int x = xa; x < xb; ++x) {
-        const float c = md == 0 ? (lrow[x] == -INFINITY ? 0.f : tv::exp_acc(lrow[x] - mm)) : src[x];
-        if (c > 0.f) last_pos = x;
-        accd += static_cast<double>(c);
-        if (accd >= T) {
-          xs = x;
+          s_m = R.m[slot];
+          s_Z = R.s[slot];
+          s_mode = 0;
+          untested = R.child[slot];
+          next = 0;     // enter the new node: fetch its children's values
           break;
         }
+        untested &= ~(1ull << sidx);
+        ++j;
+        s_qrow = R.qrow[sidx];
+        next = 1;
+        break;
       }
-      s_found = xs >= 0 ? xs : last_pos;   // rounding left the chunk short: last positive entry
+      s_u = uu;
+      s_untested = untested;
+      s_k = k;
+      s_rounds = rounds;
+      s_slot = slot;
+      s_flag = 0;
+      if (next >= 0) s_action = next;
     }
     __syncthreads();
-    if (t == 0) {
-      s_bonus = s_found;
-      s_done = 1;
-    }
-    __syncthreads();
-    break;
   }
   __syncthreads();
   if (t == 0) {
     const int stt = s_status;
-    int32_t* acc = a.accepted + static_cast<size_t>(b) * N;
     if (stt != TV_REQ_OK) {
       a.status[b] = stt;
       a.num_accepted[b] = -1;
       a.bonus[b] = -1;
       if (a.rounds) a.rounds[b] = -1;
+      s_k = 0;
     } else {
-      a.num_accepted[b] = k;
-      a.bonus[b] = s_bonus;
-      if (a.rounds) a.rounds[b] = rounds;
+      a.num_accepted[b] = s_k;
+      a.bonus[b] = s_found;
+      if (a.rounds) a.rounds[b] = s_rounds;
     }
-    s_k = stt == TV_REQ_OK ? k : 0;
   }
   __syncthreads();
   for (int i = t; i < N; i += kWalkThreads)
