@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (2 = LLaMA-7B layer)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU sample time")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     return ap.parse_args()
 
 
@@ -95,7 +96,7 @@ def main():
     code = tv.TV_BF16 if bf else tv.TV_F32
     ws_a = tv.tree_attn_verify_workspace(code, B, N, H, D, w.max_blocks)
     ws_attn = torch.zeros(max(ws_a, 1), dtype=torch.uint8, device=dev) if ws_a else None
-    ws_v = torch.empty(tv.tree_verify_workspace(B, N, V), dtype=torch.uint8, device=dev)
+    ws_v = torch.zeros(tv.tree_verify_workspace(B, N, V), dtype=torch.uint8, device=dev)   # zero once; calls leave it zero
     g_acc = torch.empty((B, N), dtype=torch.int32, device=dev)
     g_num = torch.empty((B,), dtype=torch.int32, device=dev)
     g_bonus = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -125,24 +126,72 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # Eager pass with HIP events between the calls: per-call times on the
+    # launch stream (the attention figure feeds the roofline).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     names = ["mask", "attn", "greedy", "mss", "commit"]
     comp = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
             for k, n in enumerate(names)}
+    assert int((status != 0).sum()) == 0, "a request failed during the benchmark"
+
+    # The timed loop: one HIP graph per input copy holds the whole step, so
+    # the host issues one launch per step.
+    graphs = []
+    if not args.eager:
+        for c in range(n_copies):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                step(c)
+            graphs.append(gph)
+        for gph in graphs:
+            gph.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if graphs:
+            graphs[i % n_copies].replay()
+        else:
+            step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
     acc_tokens = float(np.mean(np.maximum(m_num.cpu().numpy(), 0) + 1))
     assert int((status != 0).sum()) == 0, "a request failed during the benchmark"
 
+    # Device time per launch of the dominant call (and of MSS): a graph of
+    # back-to-back calls over the rotating input copies, timed with HIP
+    # events on the stream the graph runs on.
+    def per_call_ms(call, reps=10):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            for c in copies * 2:
+                call(c)
+        gph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            gph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * 2 * n_copies)
+
+    t_attn = per_call_ms(lambda c: tv.tree_attn_verify(c["q"], c["k"], c["v"], bt, pl0, anc, status, out, ws_attn,
+                                                       scale=w.scale))
+    t_mss = per_call_ms(lambda c: tv.tree_verify_mss(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset,
+                                                     m_acc, m_num, m_bonus, m_rounds, ws_v))
+    assert int((status != 0).sum()) == 0, "a request failed during the benchmark"
     a_bytes = attn_bytes(w)
     l_bytes = logit_bytes(w)
-    attn_gbs = a_bytes / (comp["attn"] * 1e-3) / 1e9
-    mss_gbs = l_bytes / (comp["mss"] * 1e-3) / 1e9
+    attn_gbs = a_bytes / (t_attn * 1e-3) / 1e9
+    mss_gbs = l_bytes / (t_mss * 1e-3) / 1e9
     value = B * N / (ms_per_step * 1e-3)
 
     res = {
@@ -164,11 +213,13 @@ def main():
                    "input_copies_rotated": n_copies},
         "roofline": {"bound": "hbm", "kernel": "tree_attn_verify", "achieved": round(attn_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": a_bytes},
-        "components_ms": {k: round(v, 5) for k, v in comp.items()},
-        "mss": {"achieved_GBps_on_logit_bytes": round(mss_gbs, 1),
+                     "traffic": None, "algorithmic_bytes": a_bytes, "ms_per_launch": round(t_attn, 5)},
+        "eager_components_ms": {k: round(v, 5) for k, v in comp.items()},
+        "launch": "eager" if args.eager else "hip_graph_per_step",
+        "eager_ms_per_step": round(eager_ms, 5),
+        "mss": {"ms_per_launch": round(t_mss, 5), "achieved_GBps_on_logit_bytes": round(mss_gbs, 1),
                 "frac": round(mss_gbs / HBM_PEAK_GBS, 4), "logit_bytes": l_bytes,
-                "tree_attn_plus_mss_tokens_per_s": round(B * N / ((comp["attn"] + comp["mss"]) * 1e-3), 1),
+                "tree_attn_plus_mss_tokens_per_s": round(B * N / ((t_attn + t_mss) * 1e-3), 1),
                 "mean_tokens_emitted_per_request": round(acc_tokens, 3)},
     }
     if not args.no_cpu:

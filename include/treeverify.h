@@ -24,7 +24,10 @@
  *  - A tree has N <= 64 nodes in an order where every parent precedes its
  *    children (DFS preorder in practice).  The tree root is NOT a node: it is
  *    the end of the verified prefix, whose K/V is already cached; parent[i] =
- *    -1 marks a child of the root.
+ *    -1 marks a child of the root.  parent[i] = -2 marks an unused padding
+ *    slot, so that trees of different sizes share one [B][N] batch: it is
+ *    nobody's child, has no ancestors and no children, and its outputs are
+ *    never read.
  *  - Row r of a per-request logits array is the target model's output for a
  *    context: r = 0 is the root (the verified prefix), r = 1 + i is node i.
  *  - The paged KV cache stores head h of logical slot t of request b at
@@ -58,7 +61,8 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 /* Per-request status codes written to status[b]. */
 enum {
   TV_REQ_OK = 0,
-  TV_REQ_BAD_PARENT = 1,    /* parent[i] not in {-1} U [0, i) */
+  TV_REQ_BAD_PARENT = 1,    /* parent[i] not in {-2, -1} U [0, i), or the parent
+                               is a padding slot */
   TV_REQ_BAD_TOKEN = 2,     /* token[i] not in [0, V) */
   TV_REQ_BAD_QROW = 3,      /* q_row[i] not in [0, R) */
   TV_REQ_NONFINITE = 4,     /* a visited logits row holds NaN or +inf or no finite
@@ -66,7 +70,10 @@ enum {
                                NaN, infinite or negative */
   TV_REQ_KV_CAPACITY = 6,   /* prefix_len < 0 or prefix_len + N > max_blocks * block_size */
   TV_REQ_BAD_BLOCK = 7,     /* a block_table entry the call needs is outside [0, num_blocks) */
-  TV_REQ_BAD_ACCEPTED = 8   /* num_accepted > N or an accepted id outside [0, N) */
+  TV_REQ_BAD_ACCEPTED = 8,  /* num_accepted > N or an accepted id outside [0, N) */
+  TV_REQ_TIMEOUT = 9        /* a verify call's workgroups did not meet within the
+                               wait bound (they were not all resident); the
+                               request's outputs are as for a skipped request */
 };
 
 /*
@@ -75,11 +82,14 @@ enum {
  * Topology-Aware Causal Mask" (TreeMask equation): node u attends node v iff
  * v is an ancestor of u or v = u; the verified prefix is visible to all.
  *
- *   parent [B][N] int32     parent node of each node, -1 = child of the root
+ *   parent [B][N] int32     parent node of each node, -1 = child of the root,
+ *                           -2 = padding slot
  *   anc    [B][N] uint64    out: bit j set iff node j is node i or an ancestor
+ *                           (0 for a padding slot)
  *   child  [B][N+1] uint64  out: child[b][0] = children of the root,
  *                           child[b][u+1] = children of node u (bit j = node j)
- *   depth  [B][N] int32     out: nodes on the root-to-i path (1 for root children)
+ *   depth  [B][N] int32     out: nodes on the root-to-i path (1 for root children,
+ *                           0 for a padding slot)
  *   status [B] int32        out: TV_REQ_OK, or TV_REQ_BAD_PARENT (then anc,
  *                           child and depth of that request are all zero)
  * Errors: TV_EINVAL if B < 0, N < 0 or a needed pointer is null; TV_ETOOBIG if
@@ -137,13 +147,23 @@ tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
  *
  *   target_logits [B][N+1][V] fp32
  *   token         [B][N] int32;   child [B][N+1] uint64 from tree_build_mask
- *   status        [B] in/out (may set TV_REQ_BAD_TOKEN, TV_REQ_NONFINITE)
+ *   status        [B] in/out (may set TV_REQ_BAD_TOKEN, TV_REQ_NONFINITE,
+ *                 TV_REQ_TIMEOUT)
  *   accepted      [B][N] out: accepted node ids in path order, then -1
  *   num_accepted  [B] out: path length (-1 for a request with status != 0)
  *   bonus         [B] out: the emitted target token (-1 if status != 0)
- *   workspace     >= tree_verify_workspace(B, N, V) bytes
+ *   workspace     >= tree_verify_workspace(B, N, V) bytes of device memory
+ *                 that is ALL ZERO before its first use; every call that
+ *                 completes leaves it all zero again, so one zero fill at
+ *                 allocation serves any number of later calls.  It holds the
+ *                 counters and values the workgroups of one request exchange.
+ *                 Calls that overlap in time must not share a workspace.
+ * Work split: each request is walked by ceil(V / 2048) workgroups that must
+ * all be resident at once; with more than one the launch is cooperative, in
+ * batches of requests that fit the device.  Their waits are bounded: a wait
+ * that runs out sets TV_REQ_TIMEOUT instead of hanging.
  * Errors: TV_EINVAL (B, N < 0, V < 1 or V > 2^20, null pointers),
- * TV_ETOOBIG, TV_EWORKSPACE.
+ * TV_ETOOBIG, TV_EWORKSPACE, TV_EHIP (the cooperative launch failed).
  */
 size_t tree_verify_workspace(int B, int N, int V);
 tv_status tree_verify_greedy(int B, int N, int V, const float* target_logits,
@@ -176,10 +196,10 @@ tv_status tree_verify_greedy(int B, int N, int V, const float* target_logits,
  *   q_row         [B][N] int32 row of ssm_probs that proposed node i
  *   token, child  as for greedy
  *   status        [B] in/out (may set TV_REQ_BAD_TOKEN, TV_REQ_BAD_QROW,
- *                 TV_REQ_NONFINITE)
+ *                 TV_REQ_NONFINITE, TV_REQ_TIMEOUT)
  *   accepted, num_accepted, bonus  as for greedy
  *   rounds        [B] out, or null: number of ratio tests (-1 if skipped)
- *   workspace     >= tree_verify_workspace(B, N, V) bytes
+ *   workspace     as for greedy (all zero before first use, left all zero)
  * Errors: as for greedy, plus TV_EINVAL for R < 1.
  */
 tv_status tree_verify_mss(int B, int N, int V, int R, const float* target_logits,

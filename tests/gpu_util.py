@@ -60,9 +60,13 @@ class GpuRun:
         return self
 
     def _ws_verify(self):
-        w = self.w
-        n = tv.tree_verify_workspace(w.B, w.N, w.V)
-        return torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        """One verify workspace for every verify call of this run: zeroed once
+        at allocation, and each completed call leaves it zeroed again."""
+        if getattr(self, "ws_v", None) is None:
+            w = self.w
+            n = tv.tree_verify_workspace(w.B, w.N, w.V)
+            self.ws_v = torch.zeros(max(n, 1), dtype=torch.uint8, device=DEV)
+        return self.ws_v
 
     def greedy(self):
         w = self.w

@@ -37,7 +37,7 @@ def _run(parent, tok, tl, sp, qr, seed):
     acc = torch.empty((n, N), dtype=torch.int32, device="cuda:0")
     num = torch.empty((n,), dtype=torch.int32, device="cuda:0")
     bonus = torch.empty((n,), dtype=torch.int32, device="cuda:0")
-    ws = torch.empty(tv.tree_verify_workspace(n, N, tl.shape[2]), dtype=torch.uint8, device="cuda:0")
+    ws = torch.zeros(tv.tree_verify_workspace(n, N, tl.shape[2]), dtype=torch.uint8, device="cuda:0")  # zero before first use
     tok_d = to_dev(tok.astype(np.int32))
     tv.tree_verify_mss(to_dev(tl), to_dev(sp), to_dev(qr), tok_d, child, st, seed, 0, acc, num, bonus,
                        None, ws)

@@ -299,6 +299,39 @@ def test_empty_tree_verify():
     _check_mss(run, "empty tree")
 
 
+def test_verify_workspace_reuse():
+    # several workgroups per request (V = 5003: 3 slices, ragged tail, scalar
+    # loads); one workspace for every call, left all zero after each
+    w = _small("c3_small")
+    run = GpuRun(w).mask()
+    outs = []
+    for rep in range(3):
+        _print_case("verify workspace reuse", rep)
+        run.greedy().mss(offset=w.offset + rep % 2)
+        torch.cuda.synchronize()
+        assert int(run.ws_v.count_nonzero()) == 0
+        outs.append([t.cpu().numpy().copy() for t in (run.g_acc, run.g_bonus, run.m_acc, run.m_num,
+                                                      run.m_bonus, run.m_rounds)])
+    for x, y in zip(outs[0], outs[2]):
+        assert np.array_equal(x, y)
+    _check_greedy(run)
+    _check_mss(run, "workspace reuse")
+
+
+def test_verify_many_requests():
+    # more requests than one cooperative launch holds: 20000-entry vocabulary
+    # (10 workgroups per request), 200 requests, a 7-node tree
+    w = synth.make_workload(dict(name="many", B=200, H=1, D=64, L=3, V=20000, dtype="f32",
+                                 tree=("parents", [-1, 0, 0, 1, -1, 4, 5]), sig_t=2.0, sig_s=1.0), 11)
+    _print_case("verify many requests", w.B, w.V)
+    run = GpuRun(w).mask().greedy().mss()
+    torch.cuda.synchronize()
+    _check_greedy(run)
+    ref = _check_mss(run, "many requests")
+    assert int(run.ws_v.count_nonzero()) == 0
+    assert (ref["status"] == 0).all()
+
+
 # ----------------------------------------------------------------------------
 # KV compaction
 # ----------------------------------------------------------------------------

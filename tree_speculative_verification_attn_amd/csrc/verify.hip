@@ -6,167 +6,141 @@
 // guard follow the wiki concept page "Speculative decoding", "Implementation
 // sketch".
 //
-// Two phases, both on the GPU so no logits travel to the host:
-//  1. row_stats: one pass over every target logits row (B * (N+1) rows of V
-//     floats, the dominant HBM traffic).  Rows are cut into pieces of 8192
-//     values so that even a few requests fill the chip; each piece yields
-//     (max, sum of exp(l - max) in fp64, first index of the max, NaN/+inf
-//     flags).  Consumers merge the pieces of the rows they visit.
-//  2. the walk: one workgroup per request.
-//     greedy: one wave; integer walk over the child bitmasks.
-//     MSS: 1024 threads; control decisions on thread 0, and every full-vocab
-//     step (a residual after a rejection, the final inverse-CDF sample) as a
-//     parallel pass with fp64 accumulation.
+// Work decomposition.  The walk over a request's tree is sequential, but each
+// of its steps touches a whole vocabulary row (32K-50K floats): the target
+// statistics of the node reached, the residual after a rejection, the final
+// inverse-CDF sample.  One request therefore gets G = ceil(V / 2048)
+// workgroups that run at the same time; workgroup g owns the vocabulary slice
+// [2048 g, 2048 g + 2048) and keeps its slice of the current distribution in
+// registers.  Every workgroup of a request makes the same decisions (random
+// child, ratio test) from the same data, so only a few scalars per step cross
+// workgroups: slice max / sum / argmax when a node is entered, slice residual
+// mass and the residual at the remaining children's tokens after a
+// rejection.  The final sample needs no exchange: the slice totals of the
+// current distribution are already known everywhere, so every workgroup can
+// tell which slice holds the inverse-CDF threshold, and that slice's
+// workgroup finishes the search alone.
+//
+// Latency, not bandwidth, bounds a walk (a handful of 128 KB rows per
+// request), so each pass issues its loads as early as their addresses are
+// known: the root row at kernel start, and in every MSS pass the logits row
+// and draft row of the child tested after the pass (the random choice of that
+// child does not depend on the test's outcome).
+//
+// Exchange protocol.  Each exchanged value is one 64-bit word whose high half
+// is a tag (the exchange's number + 1) and whose low half is the data; the
+// word is written and read with device-scope atomics, which stay coherent
+// across the per-XCD L2 caches without cache-wide fences.  A reader polls a
+// word until it carries the tag it expects, so one store and one load are
+// the whole cost of an exchange.  Words alternate between two banks by the
+// parity of the exchange number: a workgroup can only reach exchange n + 2
+// after every workgroup has published exchange n + 1, which each does only
+// after it has finished reading exchange n, so bank reuse never overwrites a
+// word that is still to be read.  The last workgroup to leave zeroes the
+// words, so every call starts from a zeroed workspace.
 #include "tv_common.h"
+
+#include <algorithm>
 
 namespace {
 
-constexpr int kPiece = 8192;               // logits per row_stats workgroup
-constexpr int kStatThreads = 256;
-constexpr int kPerThread = kPiece / kStatThreads;   // 32
-constexpr int kWalkThreads = 1024;
+constexpr int kCoThreads = 256;                    // threads per workgroup
+constexpr int kElem = 8;                           // vocabulary entries per thread
+constexpr int kSlice = kCoThreads * kElem;         // entries per workgroup
+constexpr int kMaxG = (1 << 20) / kSlice;          // workgroups per request at V = 2^20
+constexpr int kHdr = 4;                            // header words per workgroup per exchange
+constexpr unsigned kSpinLimit = 1u << 22;          // polls of one word before giving up
 
 enum : int { FLAG_NAN = 1, FLAG_PINF = 2, FLAG_FINITE = 4 };
-
-struct Stats {            // views into the workspace
-  float* m;               // [rows][P]
-  int* arg;               // [rows][P]
-  int* flag;              // [rows][P]
-  double* s;              // [rows][P]
-  int P;
-};
-
-__host__ __device__ inline int num_pieces(int V) { return (V + kPiece - 1) / kPiece; }
+enum : int { MODE_GREEDY = 0, MODE_MSS = 1 };
+enum : int { P_ENTER = 0, P_RESID = 1, P_FINAL = 2, P_DONE = 3 };
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// ---------------------------------------------------------------------------
+// Workspace, per request (all zero between calls):
+//   done [B][64] uint32            workgroups that have left (one 256-byte line)
+//   hdr  [B][2][G][kHdr] uint64    tagged header words, bank = exchange parity
+//   kid  [B][2][64] uint64         tagged residual value at child c's token,
+//                                  written by the workgroup owning that token
+// ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t off_m, off_arg, off_flag, off_s, off_res, total;
+  size_t off_hdr, off_kid, total;
 };
 
-WsLayout ws_layout(int B, int N, int V) {
-  const size_t rows = static_cast<size_t>(B) * (N + 1);
-  const size_t P = num_pieces(V);
+WsLayout ws_layout(int B, int V) {
+  const size_t G = (static_cast<size_t>(V) + kSlice - 1) / kSlice;
   WsLayout w;
-  w.off_m = 0;
-  w.off_arg = align256(w.off_m + rows * P * sizeof(float));
-  w.off_flag = align256(w.off_arg + rows * P * sizeof(int));
-  w.off_s = align256(w.off_flag + rows * P * sizeof(int));
-  w.off_res = align256(w.off_s + rows * P * sizeof(double));
-  w.total = align256(w.off_res + 2 * static_cast<size_t>(B) * V * sizeof(float));
+  w.off_hdr = align256(static_cast<size_t>(B) * 64 * sizeof(uint32_t));
+  w.off_kid = w.off_hdr + align256(static_cast<size_t>(B) * 2 * G * kHdr * sizeof(uint64_t));
+  w.total = w.off_kid + align256(static_cast<size_t>(B) * 2 * 64 * sizeof(uint64_t));
   return w;
 }
 
-Stats stats_view(void* ws, const WsLayout& w, int V) {
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  Stats s;
-  s.m = reinterpret_cast<float*>(p + w.off_m);
-  s.arg = reinterpret_cast<int*>(p + w.off_arg);
-  s.flag = reinterpret_cast<int*>(p + w.off_flag);
-  s.s = reinterpret_cast<double*>(p + w.off_s);
-  s.P = num_pieces(V);
-  return s;
+struct WalkArgs {
+  int mode;
+  int N, V, R, G;
+  int b0;                   // first request of this launch
+  const float* logits;      // [B][N+1][V]
+  const float* ssm;         // [B][R][V]
+  const int32_t* q_row;     // [B][N]
+  const int32_t* token;     // [B][N]
+  const uint64_t* child;    // [B][N+1]
+  int32_t* status;
+  uint64_t seed, offset;
+  int32_t* accepted;
+  int32_t* num_accepted;
+  int32_t* bonus;
+  int32_t* rounds;
+  uint32_t* done;
+  uint64_t* hdr;
+  uint64_t* kid;
+};
+
+// device-scope relaxed atomics: coherent across XCDs without L2 flushes
+__device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_u64(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------------------------------
-// Phase 1: per-piece row statistics.  grid (P, rows).  kWithSum = false
-// computes only the argmax and flags (greedy).
-// ---------------------------------------------------------------------------
-template <bool kWithSum>
-__global__ __launch_bounds__(kStatThreads) void row_stats_kernel(const float* __restrict__ logits,
-                                                                 int V, Stats st) {
-  const size_t row = blockIdx.x;
-  const int p = blockIdx.y;
-  const float* __restrict__ lr = logits + row * static_cast<size_t>(V);
-  const int x0 = p * kPiece;
-  const int x1 = min(V, x0 + kPiece);
-  const int t = threadIdx.x;
+__device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t tag, uint32_t v) {
+  st_u64(p, (static_cast<uint64_t>(tag) << 32) | v);
+}
 
-  float v[kPerThread];
-  // thread t holds x = x0 + 4*t + 1024*k + e (k < 8, e < 4): coalesced
-  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+// Poll n consecutive tagged words until all carry `tag`; their data go to
+// out[0..n).  Returns false when the poll bound runs out.
+template <int n>
+__device__ __forceinline__ bool take_tagged(uint64_t* p, uint32_t tag, uint32_t (&out)[kHdr]) {
+  for (unsigned polls = 0; polls < kSpinLimit; ++polls) {
+    uint64_t x[n];
 #pragma unroll
-  for (int k = 0; k < kPerThread / 4; ++k) {
-    const int xb = x0 + 4 * t + 1024 * k;
-    if (vec && xb + 3 < x1) {
-      const float4 f = *reinterpret_cast<const float4*>(lr + xb);
-      v[4 * k + 0] = f.x; v[4 * k + 1] = f.y; v[4 * k + 2] = f.z; v[4 * k + 3] = f.w;
-    } else {
+    for (int i = 0; i < n; ++i) x[i] = ld_u64(p + i);
+    bool ok = true;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * k + e] = (xb + e < x1) ? lr[xb + e] : -INFINITY;
+    for (int i = 0; i < n; ++i) ok = ok && static_cast<uint32_t>(x[i] >> 32) == tag;
+    if (ok) {
+#pragma unroll
+      for (int i = 0; i < n; ++i) out[i] = static_cast<uint32_t>(x[i]);
+      return true;
     }
+    __builtin_amdgcn_s_sleep(1);
   }
-  float mx = -INFINITY;
-  int arg = 0x7FFFFFFF;
-  int flags = 0;
-#pragma unroll
-  for (int k = 0; k < kPerThread / 4; ++k) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int x = x0 + 4 * t + 1024 * k + e;
-      const float f = v[4 * k + e];
-      if (x < x1) {
-        if (f != f) flags |= FLAG_NAN;
-        else if (f == INFINITY) flags |= FLAG_PINF;
-        else if (f != -INFINITY) flags |= FLAG_FINITE;
-        if (f > mx || (f == mx && x < arg && f == f)) {
-          mx = f;
-          arg = x;
-        }
-      }
-    }
-  }
-  // workgroup reduction of (max, first index, flags)
-  __shared__ float r_m[kStatThreads / 64];
-  __shared__ int r_a[kStatThreads / 64], r_f[kStatThreads / 64];
-  __shared__ double r_s[kStatThreads / 64];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(mx, o, 64);
-    const int a2 = __shfl_xor(arg, o, 64);
-    if (m2 > mx || (m2 == mx && a2 < arg)) {
-      mx = m2;
-      arg = a2;
-    }
-    flags |= __shfl_xor(flags, o, 64);
-  }
-  const int wave = t >> 6, lane = t & 63;
-  if (lane == 0) {
-    r_m[wave] = mx;
-    r_a[wave] = arg;
-    r_f[wave] = flags;
-  }
-  __syncthreads();
-  float M = r_m[0];
-  int A = r_a[0];
-  int F = r_f[0];
-  for (int w = 1; w < kStatThreads / 64; ++w) {
-    if (r_m[w] > M || (r_m[w] == M && r_a[w] < A)) {
-      M = r_m[w];
-      A = r_a[w];
-    }
-    F |= r_f[w];
-  }
-  double S = 0.0;
-  if (kWithSum && M != -INFINITY && M == M) {
-    double acc = 0.0;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const float f = v[k];
-      if (f != -INFINITY) acc += static_cast<double>(tv::exp_acc(f - M));
-    }
-    acc = tv::wave_sum(acc);
-    if (lane == 0) r_s[wave] = acc;
-    __syncthreads();
-    for (int w = 0; w < kStatThreads / 64; ++w) S += r_s[w];
-  }
-  if (t == 0) {
-    const size_t i = row * st.P + p;
-    st.m[i] = M;
-    st.arg[i] = A == 0x7FFFFFFF ? x0 : A;
-    st.flag[i] = F;
-    if (kWithSum) st.s[i] = S;
-  }
+  return false;
+}
+
+__device__ __forceinline__ uint32_t lo32(double d) {
+  return static_cast<uint32_t>(static_cast<uint64_t>(__double_as_longlong(d)));
+}
+__device__ __forceinline__ uint32_t hi32(double d) {
+  return static_cast<uint32_t>(static_cast<uint64_t>(__double_as_longlong(d)) >> 32);
+}
+__device__ __forceinline__ double join64(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
 // Children of u can only be nodes u+1 .. N-1 (parents precede children).
@@ -178,196 +152,12 @@ __device__ __forceinline__ uint64_t later_nodes(int u, int N) {
   return below_n & ~upto_u;
 }
 
-// Merge the pieces of one row (single thread).
-struct RowStat {
-  float m;
-  double s;
-  int arg;
-  bool ok;   // no NaN, no +inf, some finite value
-};
-
-__device__ RowStat merge_row(const Stats& st, size_t row, bool with_sum) {
-  RowStat r;
-  r.m = -INFINITY;
-  r.arg = 0;
-  r.s = 0.0;
-  int F = 0;
-  for (int p = 0; p < st.P; ++p) {
-    const size_t i = row * st.P + p;
-    const float m = st.m[i];
-    F |= st.flag[i];
-    if (m > r.m) {          // strict: the earlier piece keeps ties
-      r.m = m;
-      r.arg = st.arg[i];
-    }
-  }
-  r.ok = !(F & (FLAG_NAN | FLAG_PINF)) && (F & FLAG_FINITE);
-  if (with_sum && r.ok) {
-    for (int p = 0; p < st.P; ++p) {
-      const size_t i = row * st.P + p;
-      const float m = st.m[i];
-      if (m != -INFINITY) r.s += st.s[i] * exp(static_cast<double>(m) - static_cast<double>(r.m));
-    }
-  }
-  return r;
+// Index of the i-th set bit of m (i < popcount(m)).
+__device__ __forceinline__ int nth_bit(uint64_t m, int i) {
+  while (i--) m &= m - 1;
+  return __builtin_ctzll(m);
 }
 
-// Per-request small arrays staged in LDS by the walk kernels.
-struct ReqLds {
-  int tok[TV_MAX_NODES];
-  int qrow[TV_MAX_NODES];
-  uint64_t child[TV_MAX_NODES + 1];
-  // merged statistics of every row (root + nodes)
-  float m[TV_MAX_NODES + 1];
-  double s[TV_MAX_NODES + 1];
-  int arg[TV_MAX_NODES + 1];
-  int ok[TV_MAX_NODES + 1];
-};
-
-// Load tokens, draft rows and child masks, merge every row's pieces, and run
-// the up-front checks.  Returns the request status (shared by all threads).
-// Tokens and draft rows are only checked for nodes that are somebody's child
-// (padding slots are nobody's child).
-__device__ int stage_request(ReqLds& R, int b, int N, int V, int Rrows, const int32_t* token,
-                             const int32_t* q_row, const uint64_t* child, const Stats& st,
-                             bool with_sum, int status_in, uint64_t* s_real, int* s_flag) {
-  const int t = threadIdx.x;
-  if (t == 0) {
-    *s_real = 0ull;
-    *s_flag = 0;
-  }
-  __syncthreads();
-  for (int i = t; i <= N; i += blockDim.x) {
-    const uint64_t c = child[static_cast<size_t>(b) * (N + 1) + i] & later_nodes(i - 1, N);
-    R.child[i] = c;
-    if (c) atomicOr(reinterpret_cast<unsigned long long*>(s_real), static_cast<unsigned long long>(c));
-    const RowStat r = merge_row(st, static_cast<size_t>(b) * (N + 1) + i, with_sum);
-    R.m[i] = r.m;
-    R.s[i] = r.s;
-    R.arg[i] = r.arg;
-    R.ok[i] = r.ok;
-  }
-  for (int i = t; i < N; i += blockDim.x) {
-    R.tok[i] = token[static_cast<size_t>(b) * N + i];
-    R.qrow[i] = q_row ? q_row[static_cast<size_t>(b) * N + i] : 0;
-  }
-  __syncthreads();
-  const uint64_t real = *s_real;
-  for (int i = t; i < N; i += blockDim.x) {
-    if ((real >> i) & 1ull) {
-      if (R.tok[i] < 0 || R.tok[i] >= V) atomicOr(s_flag, 1);
-      if (q_row && (R.qrow[i] < 0 || R.qrow[i] >= Rrows)) atomicOr(s_flag, 2);
-    }
-  }
-  __syncthreads();
-  if (status_in != TV_REQ_OK) return status_in;
-  const int f = *s_flag;
-  if (f & 1) return TV_REQ_BAD_TOKEN;
-  if (f & 2) return TV_REQ_BAD_QROW;
-  return TV_REQ_OK;
-}
-
-// ---------------------------------------------------------------------------
-// Phase 2a: greedy walk, one workgroup of one wave per request.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void greedy_walk_kernel(int N, int V, const int32_t* __restrict__ token,
-                                                         const uint64_t* __restrict__ child,
-                                                         int32_t* __restrict__ status,
-                                                         int32_t* __restrict__ accepted,
-                                                         int32_t* __restrict__ num_accepted,
-                                                         int32_t* __restrict__ bonus, Stats st) {
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
-  __shared__ ReqLds R;
-  __shared__ uint64_t s_real;
-  __shared__ int s_flag, s_k;
-  __shared__ int s_acc[TV_MAX_NODES];
-  int stt = stage_request(R, b, N, V, 0, token, nullptr, child, st, false, status[b], &s_real, &s_flag);
-  if (t == 0) {
-    int k = 0, bn = -1;
-    if (stt == TV_REQ_OK) {
-      int u = -1;
-      while (true) {
-        if (!R.ok[u + 1]) {
-          stt = TV_REQ_NONFINITE;
-          break;
-        }
-        const int o = R.arg[u + 1];
-        uint64_t kids = R.child[u + 1];
-        int nxt = -1;
-        while (kids) {
-          const int c = __builtin_ctzll(kids);
-          kids &= kids - 1;
-          if (R.tok[c] == o) {
-            nxt = c;
-            break;
-          }
-        }
-        if (nxt < 0) {
-          bn = o;
-          break;
-        }
-        s_acc[k++] = nxt;
-        u = nxt;
-      }
-    }
-    if (stt != TV_REQ_OK) {
-      status[b] = stt;
-      num_accepted[b] = -1;
-      bonus[b] = -1;
-      k = 0;
-    } else {
-      num_accepted[b] = k;
-      bonus[b] = bn;
-    }
-    s_k = k;
-  }
-  __syncthreads();
-  for (int i = t; i < N; i += blockDim.x) accepted[static_cast<size_t>(b) * N + i] = i < s_k ? s_acc[i] : -1;
-}
-
-// ---------------------------------------------------------------------------
-// Phase 2b: multi-step speculative sampling, one 1024-thread workgroup per
-// request.  The current target distribution of node u is either its fresh
-// row, p(x) = exp(l(x) - m) / S, or a residual buffer r with p = r / Z.
-// A rejection of a child proposed from q writes r'(x) = max(0, c(x) - Z q(x))
-// (c = exp(l - m) or r, Z = S or the old Z) into the other buffer, which
-// equals Z * max(0, p - q); Z' = sum r'.  If Z' = 0 the distribution is kept.
-//
-// Thread 0 makes every decision from LDS; each step that needs global data
-// is one parallel round trip: at a node, all children's target logits and
-// draft probabilities; after a residual pass, the children's new residuals.
-// ---------------------------------------------------------------------------
-struct MssArgs {
-  int N, V, R;
-  const float* logits;
-  const float* ssm;
-  const int32_t* q_row;
-  const int32_t* token;
-  const uint64_t* child;
-  int32_t* status;
-  uint64_t seed, offset;
-  int32_t* accepted;
-  int32_t* num_accepted;
-  int32_t* bonus;
-  int32_t* rounds;
-  Stats st;
-  float* resid;            // [B][2][V]
-};
-
-__device__ __forceinline__ double block_sum(double v, double* red) {
-  v = tv::wave_sum(v);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  double s = 0.0;
-  const int nw = blockDim.x >> 6;
-  for (int w = 0; w < nw; ++w) s += red[w];
-  return s;
-}
-
-// Inclusive scan within a wave (double).
 __device__ __forceinline__ double wave_incl_scan(double v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -378,264 +168,532 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
   return v;
 }
 
-// The current distribution's unnormalised value at x.
-__device__ __forceinline__ float cur_value(int mode, const float* lrow, float m, const float* src, int x) {
-  if (mode == 0) {
-    const float l = lrow[x];
-    return l == -INFINITY ? 0.f : tv::exp_acc(l - m);
-  }
-  return src[x];
+__device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(v), o, 64));
+  return v;
 }
 
-__global__ __launch_bounds__(kWalkThreads) void mss_walk_kernel(MssArgs a) {
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  v = tv::wave_sum(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < kCoThreads / 64; ++w) s += red[w];
+  return s;
+}
+
+__device__ __forceinline__ bool q_bad(float q) { return !(q >= 0.f) || q == INFINITY; }
+
+// ---------------------------------------------------------------------------
+// The walk kernel.  grid = (requests in this launch) * G, block = 256.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
+  const int G = a.G;
+  const int b = a.b0 + static_cast<int>(blockIdx.x) / G;
+  const int g = static_cast<int>(blockIdx.x) % G;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int N = a.N, V = a.V;
+  const bool mss = a.mode == MODE_MSS;
+  const int xa = g * kSlice + t * kElem;              // first entry of this thread
+  const int nx = max(0, min(kElem, V - xa));          // entries it owns
   const float* lbase = a.logits + static_cast<size_t>(b) * (N + 1) * V;
-  const float* sbase = a.ssm + static_cast<size_t>(b) * a.R * V;
-  float* rbuf0 = a.resid + static_cast<size_t>(b) * 2 * V;
+  const float* sbase = mss ? a.ssm + static_cast<size_t>(b) * a.R * V : nullptr;
+  uint32_t* done = a.done + static_cast<size_t>(b) * 64;
+  uint64_t* hdr = a.hdr + static_cast<size_t>(b) * 2 * G * kHdr;
+  uint64_t* kid = a.kid + static_cast<size_t>(b) * 2 * 64;
+  const bool vec = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 &&
+                   (!mss || (reinterpret_cast<uintptr_t>(a.ssm) & 15) == 0);
 
-  __shared__ ReqLds R;
-  __shared__ uint64_t s_real;
-  __shared__ int s_flag;
-  __shared__ float lx_s[TV_MAX_NODES], qx_s[TV_MAX_NODES], rx_s[TV_MAX_NODES];
-  __shared__ double red[kWalkThreads / 64];
-  __shared__ int s_acc[TV_MAX_NODES];
-  // walk state (written by thread 0 only, read by all after a barrier)
-  __shared__ int s_status, s_action, s_u, s_mode, s_cur, s_qrow, s_slot, s_k, s_rounds, s_found;
-  __shared__ uint64_t s_untested;
+  __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES];
+  __shared__ uint64_t s_child[TV_MAX_NODES + 1];
+  __shared__ float s_rx[TV_MAX_NODES], s_rx2[TV_MAX_NODES];
+  __shared__ double red[kCoThreads / 64];
+  __shared__ uint32_t s_hw[kMaxG][kHdr];   // header words of every workgroup, last exchange
+  __shared__ double s_tot[kMaxG];          // slice totals of the current distribution
+  __shared__ float s_wm[kCoThreads / 64];  // per-wave max / argmax / flags
+  __shared__ int s_wa[kCoThreads / 64], s_wf[kCoThreads / 64];
+  // walk state, written by thread 0 between passes
+  __shared__ int s_status, s_timeout, s_pass, s_u, s_j, s_k, s_rounds, s_mode, s_take, s_bonus;
+  __shared__ int s_owner, s_found, s_last;
+  __shared__ uint64_t s_U;
   __shared__ float s_m;
-  __shared__ double s_Z, s_T;
+  __shared__ double s_Z, s_Tloc;
+  __shared__ float own_s[kElem];
 
-  const int st0 = stage_request(R, b, N, V, a.R, a.token, a.q_row, a.child, a.st, true, a.status[b],
-                                &s_real, &s_flag);
-  if (t == 0) {
-    s_status = st0;
-    s_u = -1;
-    s_slot = 0;
-    s_k = 0;
-    s_rounds = 0;
-    s_mode = 0;
-    s_cur = 0;
-    s_action = 0;   // 0 = enter node
-    if (st0 == TV_REQ_OK && !R.ok[0]) s_status = TV_REQ_NONFINITE;
-    if (s_status == TV_REQ_OK) {
-      s_m = R.m[0];
-      s_Z = R.s[0];
-      s_untested = R.child[0];
+  auto load8 = [&](const float* row, float (&dst)[kElem]) {
+    if (vec && nx == kElem) {
+      const float4 f0 = *reinterpret_cast<const float4*>(row + xa);
+      const float4 f1 = *reinterpret_cast<const float4*>(row + xa + 4);
+      dst[0] = f0.x; dst[1] = f0.y; dst[2] = f0.z; dst[3] = f0.w;
+      dst[4] = f1.x; dst[5] = f1.y; dst[6] = f1.z; dst[7] = f1.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < kElem; ++k) dst[k] = k < nx ? row[xa + k] : 0.f;
+    }
+  };
+
+  // ---------------- issue the first loads, stage the request ----------------
+  float lv[kElem];         // logits of the current node's row, this thread's entries
+  load8(lbase, lv);        // the root row is always visited
+  if (wave == 0) {
+    const size_t rb = static_cast<size_t>(b);
+    const int st0 = lane == 0 ? a.status[b] : 0;
+    // child[N] (children of the last node) is empty after masking
+    const uint64_t cm = lane < N ? a.child[rb * (N + 1) + lane] & later_nodes(lane - 1, N) : 0ull;
+    const int tok = lane < N ? a.token[rb * N + lane] : 0;
+    const int qr = (mss && lane < N) ? a.q_row[rb * N + lane] : 0;
+    const uint64_t real = wave_or64(cm);     // padding slots are nobody's child: unchecked
+    const uint64_t bad_tok = __ballot(lane < N && (tok < 0 || tok >= V));
+    const uint64_t bad_q = __ballot(mss && lane < N && (qr < 0 || qr >= a.R));
+    s_child[lane] = cm;
+    s_tok[lane] = tok;
+    s_qrow[lane] = qr;
+    if (lane == 0) {
+      s_child[TV_MAX_NODES] = 0ull;
+      int st = st0;
+      if (st == TV_REQ_OK) {
+        if (bad_tok & real) st = TV_REQ_BAD_TOKEN;
+        else if (bad_q & real) st = TV_REQ_BAD_QROW;
+      }
+      s_status = st;
+      s_timeout = 0;
+      s_pass = P_ENTER;
+      s_u = -1;
+      s_U = cm;            // children of the root
+      s_j = 0;
+      s_k = 0;
+      s_rounds = 0;
+      s_mode = 0;
+      s_take = 0;
+      s_bonus = -1;
+      s_owner = -1;
     }
   }
   __syncthreads();
 
-  int j = 0;   // round at the current node (thread 0)
-  while (s_status == TV_REQ_OK) {
-    const int action = s_action;
-    const int u = s_u;
-    const int mode = s_mode, cb = s_cur;
-    const float* lrow = lbase + static_cast<size_t>(u + 1) * V;
-    const float mm = s_m;
-    const double ZZ = s_Z;
-    float* src = rbuf0 + static_cast<size_t>(cb) * V;
+  float cv[kElem], rn[kElem];   // residual in use / residual of the last pass
+  float qv[kElem], qn[kElem];   // draft row of the rejected child / of the next candidate
+  float lvn[kElem];             // logits row of the next candidate
+#pragma unroll
+  for (int k = 0; k < kElem; ++k) cv[k] = rn[k] = qv[k] = qn[k] = lvn[k] = 0.f;
 
-    if (action == 0) {
-      // node entry: every child's target logit and draft probability at once
-      const uint64_t kids = s_untested;
-      if (t < N && ((kids >> t) & 1ull)) {
-        const int x = R.tok[t];
-        lx_s[t] = lrow[x];
-        qx_s[t] = sbase[static_cast<size_t>(R.qrow[t]) * V + x];
+  int ex_no = 0;                // exchanges done (identical in every workgroup)
+  for (;;) {
+    // ---- pass state (read before the pass's first barrier) ----
+    const int pass = s_pass;
+    if (pass >= P_FINAL || s_status != TV_REQ_OK || s_timeout) break;
+    const int u = s_u;
+    const uint64_t U = s_U;
+    const int j = s_j;
+    if (s_take) {
+#pragma unroll
+      for (int k = 0; k < kElem; ++k) cv[k] = rn[k];
+    }
+    if (pass == P_RESID) {
+#pragma unroll
+      for (int k = 0; k < kElem; ++k) qv[k] = qn[k];
+    }
+    const float* lrow = lbase + static_cast<size_t>(u + 1) * V;
+    if (pass == P_ENTER && u >= 0) {
+      if (mss) {
+#pragma unroll
+        for (int k = 0; k < kElem; ++k) lv[k] = lvn[k];
+      } else {
+        load8(lrow, lv);
       }
-    } else if (action == 1) {
-      // residual pass after rejecting a child proposed from row s_qrow
-      const float* q = sbase + static_cast<size_t>(s_qrow) * V;
-      float* dst = rbuf0 + static_cast<size_t>(cb ^ 1) * V;
+    }
+    // the child tested after this pass, and its rows (loads in flight during the pass)
+    int cand = -1;
+    tv::u32x4 w{0u, 0u, 0u, 0u};
+    float lx_c = 0.f, qx_c = 0.f;
+    if (mss && U) {
+      w = tv::mss_words(a.seed, a.offset, b, u + 1, j);
+      cand = nth_bit(U, tv::pick_index(w.x, __builtin_popcountll(U)));
+      const float* qrow_c = sbase + static_cast<size_t>(s_qrow[cand]) * V;
+      load8(qrow_c, qn);
+      load8(lbase + static_cast<size_t>(cand + 1) * V, lvn);
+      if (t == 0) {
+        lx_c = lrow[s_tok[cand]];
+        qx_c = qrow_c[s_tok[cand]];
+      }
+    }
+    const uint32_t tag = static_cast<uint32_t>(ex_no + 1);
+    const int par = ex_no & 1;
+    uint64_t* bank = hdr + static_cast<size_t>(par) * G * kHdr;
+    int nread = 0;
+
+    if (pass == P_ENTER) {
+      // ---- statistics of u's row over this slice ----
+      float mx = -INFINITY;
+      int arg = 0x7FFFFFFF, flags = 0;
+#pragma unroll
+      for (int k = 0; k < kElem; ++k) {
+        if (k < nx) {
+          const float f = lv[k];
+          if (f != f) flags |= FLAG_NAN;
+          else if (f == INFINITY) flags |= FLAG_PINF;
+          else if (f != -INFINITY) flags |= FLAG_FINITE;
+          if (f > mx || (f == mx && arg == 0x7FFFFFFF)) {   // first index of the max
+            mx = f;
+            arg = xa + k;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(mx, o, 64);
+        const int a2 = __shfl_xor(arg, o, 64);
+        if (m2 > mx || (m2 == mx && a2 < arg)) {
+          mx = m2;
+          arg = a2;
+        }
+        flags |= __shfl_xor(flags, o, 64);
+      }
+      if (lane == 0) {
+        s_wm[wave] = mx;
+        s_wa[wave] = arg;
+        s_wf[wave] = flags;
+      }
+      __syncthreads();
+      float M = s_wm[0];
+      int A = s_wa[0], F = s_wf[0];
+#pragma unroll
+      for (int w2 = 1; w2 < kCoThreads / 64; ++w2) {
+        if (s_wm[w2] > M || (s_wm[w2] == M && s_wa[w2] < A)) {
+          M = s_wm[w2];
+          A = s_wa[w2];
+        }
+        F |= s_wf[w2];
+      }
+      double S = 0.0;
+      if (mss && M != -INFINITY && M == M && M != INFINITY) {
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < kElem; ++k)
+          if (k < nx && lv[k] != -INFINITY) acc += static_cast<double>(tv::exp_acc(lv[k] - M));
+        S = block_sum(acc, red);
+      }
+      // slice argmax < 2^20, flags in bits 24..26
+      if (t == 0) {
+        uint64_t* p = bank + static_cast<size_t>(g) * kHdr;
+        put_tagged(p + 0, tag, __float_as_uint(M));
+        put_tagged(p + 1, tag, lo32(S));
+        put_tagged(p + 2, tag, hi32(S));
+        put_tagged(p + 3, tag, static_cast<uint32_t>(A) | (static_cast<uint32_t>(F) << 24));
+      }
+      nread = 4;
+    } else {
+      // ---- residual after rejecting the child whose draft row is in qv ----
+      const int md = s_mode;
+      const float mm = s_m;
+      const double ZZ = s_Z;
       double acc = 0.0;
       int bad = 0;
-      const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(q) & 15) == 0 &&
-                       (reinterpret_cast<uintptr_t>(lrow) & 15) == 0 &&
-                       (reinterpret_cast<uintptr_t>(src) & 15) == 0;
-      if (vec) {
-        for (int x4 = t; x4 < V / 4; x4 += kWalkThreads) {
-          const float4 qv = reinterpret_cast<const float4*>(q)[x4];
-          const float4 cv = mode == 0 ? reinterpret_cast<const float4*>(lrow)[x4]
-                                      : reinterpret_cast<const float4*>(src)[x4];
-          float c[4] = {cv.x, cv.y, cv.z, cv.w};
-          const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
-          float r[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (mode == 0) c[e] = c[e] == -INFINITY ? 0.f : tv::exp_acc(c[e] - mm);
-            if (!(qq[e] >= 0.f) || qq[e] == INFINITY) bad = 1;
-            r[e] = static_cast<float>(fmax(0.0, static_cast<double>(c[e]) - ZZ * static_cast<double>(qq[e])));
-            acc += static_cast<double>(r[e]);
+      for (int k = 0; k < kElem; ++k) {
+        if (k < nx) {
+          const float c = md == 0 ? (lv[k] == -INFINITY ? 0.f : tv::exp_acc(lv[k] - mm)) : cv[k];
+          if (q_bad(qv[k])) bad = 1;
+          rn[k] = static_cast<float>(fmax(0.0, static_cast<double>(c) - ZZ * static_cast<double>(qv[k])));
+          acc += static_cast<double>(rn[k]);
+        } else {
+          rn[k] = 0.f;
+        }
+      }
+      bad = __any(bad) ? 1 : 0;
+      if (lane == 0) s_wf[wave] = bad;
+      const double Zg = block_sum(acc, red);     // its barriers publish s_wf
+      int anyb = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kCoThreads / 64; ++w2) anyb |= s_wf[w2];
+      // the new residual at the remaining children's tokens: the owner of
+      // each child's token publishes it
+      {
+        uint64_t kk = U;
+        while (kk) {
+          const int c = __builtin_ctzll(kk);
+          kk &= kk - 1;
+          const int x = s_tok[c];
+          if (x >= xa && x < xa + nx) {
+            float v = 0.f;
+#pragma unroll
+            for (int k = 0; k < kElem; ++k) v = (xa + k == x) ? rn[k] : v;
+            put_tagged(kid + par * 64 + c, tag, __float_as_uint(v));
           }
-          reinterpret_cast<float4*>(dst)[x4] = make_float4(r[0], r[1], r[2], r[3]);
+        }
+      }
+      if (t == 0) {
+        uint64_t* p = bank + static_cast<size_t>(g) * kHdr;
+        put_tagged(p + 0, tag, lo32(Zg));
+        put_tagged(p + 1, tag, hi32(Zg));
+        put_tagged(p + 2, tag, static_cast<uint32_t>(anyb));
+      }
+      nread = 3;
+      if (t < N && ((U >> t) & 1ull)) {
+        uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
+        if (!take_tagged<1>(kid + par * 64 + t, tag, v)) s_timeout = 1;
+        s_rx2[t] = __uint_as_float(v[0]);
+      }
+    }
+    // ---- gather every workgroup's header words ----
+    for (int gg = t; gg < G; gg += kCoThreads) {
+      uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
+      const bool ok = nread == 4 ? take_tagged<4>(bank + static_cast<size_t>(gg) * kHdr, tag, v)
+                                 : take_tagged<3>(bank + static_cast<size_t>(gg) * kHdr, tag, v);
+      if (!ok) s_timeout = 1;
+#pragma unroll
+      for (int i = 0; i < kHdr; ++i) s_hw[gg][i] = v[i];
+    }
+    __syncthreads();
+    ++ex_no;
+
+    // ---- merge the slices (wave 0, in parallel) and decide (thread 0) ----
+    if (wave == 0) {
+      int next_pass = P_DONE;
+      float m_now = s_m;
+      double Z_now = s_Z;
+      int md_now = s_mode;
+      int take = 0;
+      bool fail = false;
+      if (pass == P_ENTER) {
+        // max with the lowest index on ties, flags, then the normaliser
+        float m = -INFINITY;
+        int am = 0x7FFFFFFF, fl = 0;
+        for (int gg = lane; gg < G; gg += 64) {
+          const float mg = __uint_as_float(s_hw[gg][0]);
+          const int ag = static_cast<int>(s_hw[gg][3] & 0xFFFFFFu);
+          fl |= static_cast<int>(s_hw[gg][3] >> 24);
+          if (mg > m || (mg == m && ag < am)) {
+            m = mg;
+            am = ag;
+          }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float m2 = __shfl_xor(m, o, 64);
+          const int a2 = __shfl_xor(am, o, 64);
+          if (m2 > m || (m2 == m && a2 < am)) {
+            m = m2;
+            am = a2;
+          }
+          fl |= __shfl_xor(fl, o, 64);
+        }
+        fail = (fl & (FLAG_NAN | FLAG_PINF)) || !(fl & FLAG_FINITE);
+        if (!fail && !mss) {
+          // greedy: the child whose token is the argmax, lowest node first
+          const uint64_t hit = __ballot(lane < N && ((U >> lane) & 1ull) && s_tok[lane] == am);
+          if (lane == 0) {
+            if (hit) {
+              const int nxt = __builtin_ctzll(hit);
+              s_acc[s_k++] = nxt;
+              s_u = nxt;
+              s_U = s_child[nxt + 1];
+              next_pass = P_ENTER;
+            } else {
+              s_bonus = am;
+              next_pass = P_DONE;
+            }
+          }
+        } else if (!fail) {
+          double part = 0.0;
+          for (int gg = lane; gg < G; gg += 64) {
+            const float mg = __uint_as_float(s_hw[gg][0]);
+            const double tg = mg == -INFINITY ? 0.0
+                              : join64(s_hw[gg][1], s_hw[gg][2]) *
+                                    exp(static_cast<double>(mg) - static_cast<double>(m));
+            s_tot[gg] = tg;
+            part += tg;
+          }
+          Z_now = tv::wave_sum(part);
+          m_now = m;
+          md_now = 0;
         }
       } else {
-        for (int x = t; x < V; x += kWalkThreads) {
-          const float c = cur_value(mode, lrow, mm, src, x);
-          const float qv = q[x];
-          if (!(qv >= 0.f) || qv == INFINITY) bad = 1;
-          const float r = static_cast<float>(fmax(0.0, static_cast<double>(c) - ZZ * static_cast<double>(qv)));
-          dst[x] = r;
-          acc += static_cast<double>(r);
+        double part = 0.0;
+        int anyb = 0;
+        for (int gg = lane; gg < G; gg += 64) {
+          part += join64(s_hw[gg][0], s_hw[gg][1]);
+          anyb |= static_cast<int>(s_hw[gg][2]);
+        }
+        const double Znew = tv::wave_sum(part);
+        fail = tv::wave_or(anyb) != 0;
+        take = !fail && Znew > 0.0;
+        if (take) {           // else the distribution stays (zero-normaliser guard)
+          for (int gg = lane; gg < G; gg += 64) s_tot[gg] = join64(s_hw[gg][0], s_hw[gg][1]);
+          if (lane < N && ((U >> lane) & 1ull)) s_rx[lane] = s_rx2[lane];
+          Z_now = Znew;
+          md_now = 1;
         }
       }
-      if (bad) atomicOr(&s_flag, 4);
-      const double Znew = block_sum(acc, red);
-      const int flag = s_flag;
-      __syncthreads();
-      const bool take = !(flag & 4) && Znew > 0.0;
-      if (take) {
-        // the remaining children's values under the new distribution
-        const uint64_t kids = s_untested;
-        if (t < N && ((kids >> t) & 1ull)) rx_s[t] = dst[R.tok[t]];
-      }
-      if (t == 0) {
-        if (flag & 4) {
-          s_status = TV_REQ_NONFINITE;
-        } else if (take) {
-          s_mode = 1;
-          s_cur = cb ^ 1;
-          s_Z = Znew;
-        }
-      }
-    } else {
-      // final sample: smallest x with cumsum >= u2 * total; thread t owns a
-      // contiguous chunk, chunk sums are scanned across the workgroup
-      const int chunk = (V + kWalkThreads - 1) / kWalkThreads;
-      const int xa = min(V, t * chunk), xb = min(V, xa + chunk);
-      double part = 0.0;
-      for (int x = xa; x < xb; ++x) part += static_cast<double>(cur_value(mode, lrow, mm, src, x));
-      const double wincl = wave_incl_scan(part);
-      const int wave = t >> 6, lane = t & 63;
-      if (lane == 63) red[wave] = wincl;
-      __syncthreads();
-      double wbase = 0.0, total = 0.0;
-      for (int w2 = 0; w2 < kWalkThreads / 64; ++w2) {
-        if (w2 < wave) wbase += red[w2];
-        total += red[w2];
-      }
-      const double incl = wbase + wincl;
-      // the previous thread's inclusive sum, bit for bit: the same wave base
-      // plus its wave-scan value (lane 0: the base itself, which equals the
-      // last lane of the previous wave summed in the same order)
-      const double prev_w = __shfl_up(wincl, 1, 64);
-      const double excl = lane > 0 ? wbase + prev_w : wbase;
-      if (t == 0) {
-        const tv::u32x4 w = tv::mss_words(a.seed, a.offset, b, s_slot, 0);
-        s_T = tv::unit_open0(w.z) * total;
-        s_found = -1;
-      }
-      __syncthreads();
-      const double T = s_T;
-      // exactly one owner: the first thread whose inclusive sum reaches T
-      if (excl < T && incl >= T) {
-        double accd = excl;
-        int xs = -1, last_pos = -1;
-        for (int x = xa; x < xb; ++x) {
-          const float c = cur_value(mode, lrow, mm, src, x);
-          if (c > 0.f) last_pos = x;
-          accd += static_cast<double>(c);
-          if (accd >= T) {
-            xs = x;
-            break;
+      if (mss && !fail) {
+        // ratio test of the candidate (thread 0), or the final sample's slice
+        if (cand >= 0) {
+          if (lane == 0) {
+            if (q_bad(qx_c)) {
+              fail = true;
+            } else {
+              const double px = md_now == 0
+                                    ? (lx_c == -INFINITY ? 0.0
+                                                         : exp(static_cast<double>(lx_c) - static_cast<double>(m_now)) / Z_now)
+                                    : static_cast<double>(s_rx[cand]) / Z_now;
+              const double ratio =
+                  qx_c > 0.f ? px / static_cast<double>(qx_c) : (px > 0.0 ? INFINITY : 0.0);
+              ++s_rounds;
+              if (tv::unit_open0(w.y) <= ratio) {
+                s_acc[s_k++] = cand;
+                s_u = cand;
+                s_U = s_child[cand + 1];
+                s_j = 0;
+                next_pass = P_ENTER;
+              } else {
+                s_U = U & ~(1ull << cand);
+                s_j = j + 1;
+                next_pass = P_RESID;
+              }
+            }
           }
-        }
-        s_found = xs >= 0 ? xs : last_pos;   // rounding left the chunk short: last positive entry
-      }
-      __syncthreads();
-      if (t == 0) {
-        s_action = 3;   // done
-      }
-      __syncthreads();
-      break;
-    }
-    __syncthreads();
-
-    // ---- thread 0: ratio tests until a full-vocab pass is needed ----
-    if (t == 0 && s_status == TV_REQ_OK) {
-      int uu = s_u;
-      uint64_t untested = s_untested;
-      int md = s_mode;
-      float m_ = s_m;
-      double Z = s_Z;
-      int k = s_k, rounds = s_rounds, slot = s_slot;
-      int next = 2;     // default: final sample
-      while (untested) {
-        const tv::u32x4 w = tv::mss_words(a.seed, a.offset, b, slot, j);
-        const int mcnt = __builtin_popcountll(untested);
-        int idx = tv::pick_index(w.x, mcnt);
-        uint64_t bits = untested;
-        while (idx--) bits &= bits - 1;
-        const int sidx = __builtin_ctzll(bits);
-        const float qx = qx_s[sidx];
-        if (!(qx >= 0.f) || qx == INFINITY) {
-          s_status = TV_REQ_NONFINITE;
-          next = -1;
-          break;
-        }
-        double px;
-        if (md == 0) {
-          const float lx = lx_s[sidx];
-          px = lx == -INFINITY ? 0.0 : exp(static_cast<double>(lx) - static_cast<double>(m_)) / Z;
         } else {
-          px = static_cast<double>(rx_s[sidx]) / Z;
-        }
-        const double ratio = qx > 0.f ? px / static_cast<double>(qx) : (px > 0.0 ? INFINITY : 0.0);
-        const double u1 = tv::unit_open0(w.y);
-        ++rounds;
-        if (u1 <= ratio) {
-          s_acc[k++] = sidx;
-          uu = sidx;
-          slot = sidx + 1;
-          j = 0;
-          if (!R.ok[slot]) {
-            s_status = TV_REQ_NONFINITE;
-            next = -1;
-            break;
+          // no child left: the slice holding u2 * total, from the slice
+          // totals in index order; the threshold inside it
+          const tv::u32x4 w0 = tv::mss_words(a.seed, a.offset, b, u + 1, 0);
+          double run = 0.0;
+          for (int base = 0; base < G; base += 64) {
+            const double v = base + lane < G ? s_tot[base + lane] : 0.0;
+            run += __shfl(wave_incl_scan(v), 63, 64);
           }
-          s_m = R.m[slot];
-          s_Z = R.s[slot];
-          s_mode = 0;
-          untested = R.child[slot];
-          next = 0;     // enter the new node: fetch its children's values
-          break;
+          const double T = tv::unit_open0(w0.z) * run;
+          double carry = 0.0;
+          int owner = -1, last = -1;
+          double ex_owner = 0.0, ex_last = 0.0;
+          for (int base = 0; base < G && owner < 0; base += 64) {
+            const double v = base + lane < G ? s_tot[base + lane] : 0.0;
+            const double incl = carry + wave_incl_scan(v);
+            double excl = __shfl_up(incl, 1, 64);
+            if (lane == 0) excl = carry;
+            const uint64_t hit = __ballot(v > 0.0 && excl < T && incl >= T);
+            const uint64_t pos = __ballot(v > 0.0);
+            if (hit) {
+              const int l = __builtin_ctzll(hit);
+              owner = base + l;
+              ex_owner = __shfl(excl, l, 64);
+            } else if (pos) {
+              const int l = 63 - __builtin_clzll(pos);
+              last = base + l;
+              ex_last = __shfl(excl, l, 64);
+            }
+            carry = __shfl(incl, 63, 64);
+          }
+          if (owner < 0) {     // rounding left the total short: last non-empty slice
+            owner = last;
+            ex_owner = ex_last;
+          }
+          if (lane == 0) {
+            s_owner = owner;
+            s_Tloc = fmax(T - ex_owner, 1e-300);
+          }
+          next_pass = P_FINAL;
         }
-        untested &= ~(1ull << sidx);
-        ++j;
-        s_qrow = R.qrow[sidx];
-        next = 1;
-        break;
       }
-      s_u = uu;
-      s_untested = untested;
-      s_k = k;
-      s_rounds = rounds;
-      s_slot = slot;
-      s_flag = 0;
-      if (next >= 0) s_action = next;
+      if (lane == 0) {
+        if (fail) s_status = TV_REQ_NONFINITE;
+        s_pass = next_pass;
+        s_take = take;
+        s_m = m_now;
+        s_Z = Z_now;
+        s_mode = md_now;
+      }
     }
     __syncthreads();
   }
+
+  // ---- final sample: the owner slice's workgroup finds the token ----
+  if (s_pass == P_FINAL && s_status == TV_REQ_OK && !s_timeout && g == s_owner) {
+    if (s_take) {
+#pragma unroll
+      for (int k = 0; k < kElem; ++k) cv[k] = rn[k];
+    }
+    const int md = s_mode;
+    const float mm = s_m;
+    float cur[kElem];
+    double part = 0.0;
+#pragma unroll
+    for (int k = 0; k < kElem; ++k) {
+      cur[k] = k < nx ? (md == 0 ? (lv[k] == -INFINITY ? 0.f : tv::exp_acc(lv[k] - mm)) : cv[k]) : 0.f;
+      part += static_cast<double>(cur[k]);
+    }
+    const double wincl = wave_incl_scan(part);
+    if (lane == 63) red[wave] = wincl;
+    if (t == 0) s_found = -1;
+    __syncthreads();
+    double wbase = 0.0, total = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < kCoThreads / 64; ++w2) {
+      if (w2 < wave) wbase += red[w2];
+      total += red[w2];
+    }
+    const double incl = wbase + wincl;
+    const double prev_w = __shfl_up(wincl, 1, 64);
+    const double excl = lane > 0 ? wbase + prev_w : wbase;   // the previous thread's incl, bit for bit
+    // threshold in (0, slice total]: exactly one thread has excl < T <= incl
+    const double T = fmin(s_Tloc, total);
+    if (excl < T && incl >= T) {
+#pragma unroll
+      for (int k = 0; k < kElem; ++k) own_s[k] = cur[k];
+      double accd = excl;
+      int xs = -1, last_pos = -1;
+      for (int k = 0; k < nx; ++k) {
+        const float c = own_s[k];
+        if (c > 0.f) last_pos = xa + k;
+        accd += static_cast<double>(c);
+        if (accd >= T) {
+          xs = xa + k;
+          break;
+        }
+      }
+      s_found = xs >= 0 ? xs : last_pos;   // rounding left the chunk short: last positive entry
+    }
+    __syncthreads();
+    if (t == 0) a.bonus[b] = s_found;
+  }
+
+  // ---- results: workgroup 0 writes the path (and the greedy bonus) ----
+  if (g == 0) {
+    const bool ok = s_status == TV_REQ_OK && !s_timeout;
+    if (t == 0) {
+      int stt = s_status;
+      if (stt == TV_REQ_OK && s_timeout) stt = TV_REQ_TIMEOUT;
+      if (stt != TV_REQ_OK) {
+        a.status[b] = stt;
+        a.num_accepted[b] = -1;
+        a.bonus[b] = -1;
+        if (a.rounds) a.rounds[b] = -1;
+      } else {
+        a.num_accepted[b] = s_k;
+        if (!mss || s_owner < 0) a.bonus[b] = s_bonus;   // MSS: the owner slice writes it
+        if (a.rounds) a.rounds[b] = s_rounds;
+      }
+    }
+    const int k = ok ? s_k : 0;
+    for (int i = t; i < N; i += kCoThreads) a.accepted[static_cast<size_t>(b) * N + i] = i < k ? s_acc[i] : -1;
+  }
+
+  // ---- leave the workspace zeroed: the last workgroup out clears it ----
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have completed
   __syncthreads();
   if (t == 0) {
-    const int stt = s_status;
-    if (stt != TV_REQ_OK) {
-      a.status[b] = stt;
-      a.num_accepted[b] = -1;
-      a.bonus[b] = -1;
-      if (a.rounds) a.rounds[b] = -1;
-      s_k = 0;
-    } else {
-      a.num_accepted[b] = s_k;
-      a.bonus[b] = s_found;
-      if (a.rounds) a.rounds[b] = s_rounds;
-    }
+    const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == static_cast<uint32_t>(G - 1);
   }
   __syncthreads();
-  for (int i = t; i < N; i += kWalkThreads)
-    a.accepted[static_cast<size_t>(b) * N + i] = i < s_k ? s_acc[i] : -1;
+  if (s_last) {          // every workgroup has finished reading
+    for (int i = t; i < 2 * G * kHdr; i += kCoThreads) st_u64(hdr + i, 0ull);
+    if (t < 128) st_u64(kid + t, 0ull);
+    if (t == 0) st_u32(done, 0u);
+  }
 }
 
 tv_status check_verify_args(int B, int N, int V) {
@@ -644,11 +702,66 @@ tv_status check_verify_args(int B, int N, int V) {
   return TV_OK;
 }
 
+// Workgroups of the walk kernel that fit on the device at once (cached per
+// device: it depends only on the kernel and the device).
+int walk_capacity(int dev) {
+  static int cache[64];
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(walk_kernel),
+                                                   kCoThreads, 0) != hipSuccess)
+    return 0;
+  const int cap = cus * std::max(1, per_cu);
+  if (dev >= 0 && dev < 64) cache[dev] = cap;
+  return cap;
+}
+
+// Launch the walk in request batches whose workgroups all fit on the device
+// at once, so the workgroups of a request never wait for one another's
+// residency (the waits are bounded regardless).
+tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
+  const int G = a.G;
+  if (G == 1) {          // a request's only workgroup waits on nobody else
+    a.b0 = 0;
+    hipLaunchKernelGGL(walk_kernel, dim3(B), dim3(kCoThreads), 0, stream, a);
+    return tv::launch_status();
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TV_EHIP;
+  const int capacity = walk_capacity(dev);
+  if (capacity <= 0) return TV_EHIP;
+  if (G > capacity) return TV_EINVAL;
+  const int per_launch = capacity / G;
+  for (int b0 = 0; b0 < B; b0 += per_launch) {
+    const int nb = std::min(per_launch, B - b0);
+    a.b0 = b0;
+    hipLaunchKernelGGL(walk_kernel, dim3(nb * G), dim3(kCoThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return TV_EHIP;
+  }
+  return TV_OK;
+}
+
+WalkArgs make_args(int mode, int N, int V, int R, void* workspace, int B) {
+  WalkArgs a{};
+  a.mode = mode;
+  a.N = N;
+  a.V = V;
+  a.R = R;
+  a.G = (V + kSlice - 1) / kSlice;
+  const WsLayout w = ws_layout(B, V);
+  uint8_t* p = static_cast<uint8_t*>(workspace);
+  a.done = reinterpret_cast<uint32_t*>(p);
+  a.hdr = reinterpret_cast<uint64_t*>(p + w.off_hdr);
+  a.kid = reinterpret_cast<uint64_t*>(p + w.off_kid);
+  return a;
+}
+
 }  // namespace
 
 extern "C" size_t tree_verify_workspace(int B, int N, int V) {
   if (check_verify_args(B, N, V) != TV_OK || B == 0) return 0;
-  return ws_layout(B, N, V).total;
+  return ws_layout(B, V).total;
 }
 
 extern "C" tv_status tree_verify_greedy(int B, int N, int V, const float* target_logits,
@@ -661,15 +774,16 @@ extern "C" tv_status tree_verify_greedy(int B, int N, int V, const float* target
   if (!target_logits || !child || !status || !num_accepted || !bonus ||
       (N > 0 && (!token || !accepted)))
     return TV_EINVAL;
-  const WsLayout w = ws_layout(B, N, V);
-  if (!workspace || ws_bytes < w.total) return TV_EWORKSPACE;
-  const Stats st = stats_view(workspace, w, V);
-  hipLaunchKernelGGL(row_stats_kernel<false>, dim3(B * (N + 1), st.P), dim3(kStatThreads), 0, stream,
-                     target_logits, V, st);
-  if (hipGetLastError() != hipSuccess) return TV_EHIP;
-  hipLaunchKernelGGL(greedy_walk_kernel, dim3(B), dim3(64), 0, stream, N, V, token, child, status,
-                     accepted, num_accepted, bonus, st);
-  return tv::launch_status();
+  if (!workspace || ws_bytes < ws_layout(B, V).total) return TV_EWORKSPACE;
+  WalkArgs a = make_args(MODE_GREEDY, N, V, 1, workspace, B);
+  a.logits = target_logits;
+  a.token = token;
+  a.child = child;
+  a.status = status;
+  a.accepted = accepted;
+  a.num_accepted = num_accepted;
+  a.bonus = bonus;
+  return launch_walk(a, B, stream);
 }
 
 extern "C" tv_status tree_verify_mss(int B, int N, int V, int R, const float* target_logits,
@@ -685,19 +799,19 @@ extern "C" tv_status tree_verify_mss(int B, int N, int V, int R, const float* ta
   if (!target_logits || !ssm_probs || !child || !status || !num_accepted || !bonus ||
       (N > 0 && (!token || !accepted || !q_row)))
     return TV_EINVAL;
-  const WsLayout w = ws_layout(B, N, V);
-  if (!workspace || ws_bytes < w.total) return TV_EWORKSPACE;
-  const Stats st = stats_view(workspace, w, V);
-  hipLaunchKernelGGL(row_stats_kernel<true>, dim3(B * (N + 1), st.P), dim3(kStatThreads), 0, stream,
-                     target_logits, V, st);
-  if (hipGetLastError() != hipSuccess) return TV_EHIP;
-  MssArgs a;
-  a.N = N; a.V = V; a.R = R;
-  a.logits = target_logits; a.ssm = ssm_probs; a.q_row = q_row; a.token = token; a.child = child;
-  a.status = status; a.seed = seed; a.offset = offset;
-  a.accepted = accepted; a.num_accepted = num_accepted; a.bonus = bonus; a.rounds = rounds;
-  a.st = st;
-  a.resid = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + w.off_res);
-  hipLaunchKernelGGL(mss_walk_kernel, dim3(B), dim3(kWalkThreads), 0, stream, a);
-  return tv::launch_status();
+  if (!workspace || ws_bytes < ws_layout(B, V).total) return TV_EWORKSPACE;
+  WalkArgs a = make_args(MODE_MSS, N, V, R, workspace, B);
+  a.logits = target_logits;
+  a.ssm = ssm_probs;
+  a.q_row = q_row;
+  a.token = token;
+  a.child = child;
+  a.status = status;
+  a.seed = seed;
+  a.offset = offset;
+  a.accepted = accepted;
+  a.num_accepted = num_accepted;
+  a.bonus = bonus;
+  a.rounds = rounds;
+  return launch_walk(a, B, stream);
 }
