@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU sample time")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run warmup + steps eager steps and exit (for counter collection)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run 5 device-to-device copies of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -65,6 +69,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.copy_calibration_mb:
+        copy_calibration(torch, args.copy_calibration_mb)
+        return
 
     import synth
     import tree_speculative_verification_attn_amd as tv
@@ -125,6 +133,12 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.profile_only:
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        print(f"ran {args.warmup} + {args.steps} eager steps of {w.name}")
+        return
 
     # Eager pass with HIP events between the calls: per-call times on the
     # launch stream (the attention figure feeds the roofline).
@@ -213,7 +227,8 @@ def main():
                    "input_copies_rotated": n_copies},
         "roofline": {"bound": "hbm", "kernel": "tree_attn_verify", "achieved": round(attn_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": a_bytes, "ms_per_launch": round(t_attn, 5)},
+                     "traffic": measured_traffic(w.name), "algorithmic_bytes": a_bytes,
+                     "ms_per_launch": round(t_attn, 5)},
         "eager_components_ms": {k: round(v, 5) for k, v in comp.items()},
         "launch": "eager" if args.eager else "hip_graph_per_step",
         "eager_ms_per_step": round(eager_ms, 5),
@@ -225,6 +240,52 @@ def main():
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, value)
     print(json.dumps(res))
+
+
+def copy_calibration(torch, mib):
+    """Five plain device-to-device copies of `mib` MiB: the reference that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB 5 times")
+
+
+ATTN_SOURCES = ("tree_speculative_verification_attn_amd/csrc/attn.hip",
+                "tree_speculative_verification_attn_amd/csrc/tv_common.h")
+
+
+def attn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per tree_attn_verify launch from the committed counter
+    summary of this workload, or None when there is none or the attention
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"tree_attn_verify_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("attn_source_sha256") != attn_source_hash():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, budget_s, gpu_value):

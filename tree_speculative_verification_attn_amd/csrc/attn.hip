@@ -11,22 +11,21 @@
 // key chunk s).  A chunk is a contiguous range of logical key slots; every
 // key K/V row is read from HBM exactly once and reused by all N tree queries
 // of that (b, h), which is what makes the tree pass cheaper than per-path
-// decoding.  Long prefixes are cut into several chunks so that the grid has
-// enough workgroups; each chunk leaves an unnormalised partial (O, max, sum)
-// and a second kernel merges them with log-sum-exp weights.
+// decoding.  The pass is bound by HBM bandwidth, so the bf16 kernel runs one
+// workgroup per CU with a deep ring of K/V stages in LDS (128 KB of loads in
+// flight per CU).  The number of chunks per (b, h) comes from a small cost
+// model: as few as keep every CU busy, because each extra chunk leaves an
+// unnormalised partial (O, max, sum) that a second kernel reads back and
+// merges with log-sum-exp weights.
 //
-// bf16 path (matrix cores): each wave walks 32-key steps of the chunk (the
-// 4 waves interleave steps) and keeps, for all N queries, the running max,
-// sum and O in registers.
-//   S^T[key][query] = K . Q^T   on v_mfma_f32_16x16x32_bf16
-//     (A = 16 keys x 32 dims of K straight from the paged cache,
-//      B = 32 dims x 16 queries of Q)
-//   O^T[dim][query] += V^T . P^T on the same instruction
-//     (A = 16 dims x 32 keys of V^T, B = 32 keys x 16 queries of P^T)
-// P^T comes out of the S^T accumulator already in the B-operand layout.  V^T
-// is produced without LDS: multiplying the row-major V tile (A operand) by a
-// 0/1 selection matrix on the matrix cores is exact and leaves each lane
-// holding 4 keys of one dim, the layout the V^T operand needs.
+// bf16 path (matrix cores): K/V stages of 64 keys go HBM -> LDS with
+// direct-to-LDS loads; wave w < ceil(N/16) owns query tile w for the whole
+// chunk and keeps its running max, sum and O in registers.  Per 32 keys:
+//   S^T[key][query] = K . Q^T     on v_mfma_f32_16x16x32_bf16
+//     (A = 16 keys x 32 dims of K from LDS, B = 32 dims x 16 queries of Q)
+//   O^T[dim][query] += V^T . P^T  on the same instruction
+//     (A = V^T from LDS transpose reads, B = P^T straight from the S^T
+//      accumulator, which already has the B-operand layout)
 //
 // fp32 path (vector ALU): same chunking, K/V tiles staged in LDS, all
 // queries of the (b, h) per workgroup.
@@ -42,7 +41,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
 constexpr int kMaxSplits = 64;                      // chunks per (request, head)
-constexpr int kMaxChunkKeys = 16384;                // keys per workgroup chunk (bf16 path)
+constexpr int kMaxChunkKeys = 32768;                // keys per workgroup chunk (bf16 path)
 constexpr int kMaxChunkBlocks = kMaxChunkKeys / TV_BLOCK + 1;
 
 struct AttnArgs {
@@ -147,39 +146,54 @@ __device__ __forceinline__ int tile_off(int r, int c16) {   // byte offset
   return r * (2 * D) + swz<D>(r, c16) * 16;
 }
 
-// One workgroup = 4 waves per (request b, head h, key chunk s).  K/V stages of
-// 64 keys are copied HBM -> LDS with direct-to-LDS loads (no registers), two
-// stages in flight; all 4 waves load, waves 0..NQT-1 each own one 16-query
-// tile of the tree for the whole chunk.  Per 32 keys and query tile:
+// One workgroup per (request b, head h, key chunk s), made of NG groups of 4
+// waves.  The chunk is cut into stages of 32 keys; group g takes stages
+// g, g + NG, g + 2 NG, ... and runs as if it were a workgroup of its own: a
+// two-buffer ring of K/V stages filled HBM -> LDS with direct-to-LDS loads
+// (no registers), one stage in flight while the other is read, and its own
+// barrier (an LDS counter), so the groups drift independently and one
+// group's loads overlap another's matrix work.  Waves 0..NQT-1 of a group
+// each own one 16-query tile of the tree.  Per 32 keys and query tile:
 //   S^T[key][query] = K . Q^T     (A = K rows from LDS, B = Q^T in registers)
 //   O^T[dim][query] += V^T . P^T  (A = V^T via LDS transpose reads,
 //                                  B = P^T straight from the S^T accumulator)
-// With several chunks, each workgroup leaves an unnormalised partial and the
-// last one to finish (counter in the workspace) merges them.
+// At the end the groups' softmax states are merged through LDS; with several
+// chunks per (b, h) the merged state is written as an unnormalised partial
+// that attn_merge_kernel combines.
+constexpr int kGroups = 4;                  // 4-wave groups per workgroup
+constexpr int kGroupThreads = 256;
+constexpr int kAttnThreads = kGroups * kGroupThreads;
+constexpr unsigned kGroupSpinLimit = 1u << 26;
+
 template <int D, int NQT>
-__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KC = D / 32;               // contraction steps over D
   constexpr int DT = D / 16;               // output dim tiles
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
-  constexpr int SK = 64;                   // keys per stage
+  constexpr int SK = 32;                   // keys per stage
   constexpr int TILE = SK * D * 2;         // bytes of one K or V stage tile
   constexpr int LPW = (2 * TILE / 1024) / 4;   // 1 KB wave-loads per wave per stage
+  static_assert(LPW == 4 || LPW == 2, "stage size");
+  constexpr int SLOT = (DT * 4 + 2) * 64;       // floats of one merge slot (see the end)
+  static_assert((kGroups - 1) * NQT * SLOT * 4 <= kGroups * 2 * 2 * TILE, "merge area");
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = wave >> 2, gw = wave & 3;          // group, wave within the group
   const int lr = lane & 15, lg = lane >> 4;
 
-  // two stage buffers, each [K tile | V tile]; separate arrays so the
-  // compiler can tell the in-flight stage from the one being read
-  __shared__ __attribute__((aligned(16))) uint8_t stage_buf0[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_buf1[2 * TILE];
-  __shared__ int s_gate, s_badblk;
+  // per group: two stage buffers, each [K tile | V tile]
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kGroups * 2 * 2 * TILE];
+  __shared__ int s_gate, s_badblk, s_hung;
+  __shared__ int s_gbar[kGroups];
   __shared__ int s_blk[kMaxChunkBlocks];
 
   if (threadIdx.x == 0) {
     s_gate = request_gate(a, b);
     s_badblk = 0;
+    s_hung = 0;
   }
+  if (threadIdx.x < kGroups) s_gbar[threadIdx.x] = 0;
   __syncthreads();
   const int gate = s_gate;
   if (gate != TV_REQ_OK) {
@@ -194,7 +208,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a) {
   const int k_begin = s * a.chunk;
   if (k_begin >= T) return;                 // empty chunk: not counted by the merge
   const int k_end = min(T, k_begin + a.chunk);
-  const int nst = (k_end - k_begin + SK - 1) / SK;
+  const int nst = (k_end - k_begin + SK - 1) / SK;                // stages of the chunk
+  const int nloc = nst > grp ? (nst - grp + kGroups - 1) / kGroups : 0;   // this group's
 
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
   const uint8_t* __restrict__ kg = static_cast<const uint8_t*>(a.kc);
@@ -205,8 +220,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a) {
   const int last_blk = (T - 1) / TV_BLOCK, last_row = (T - 1) % TV_BLOCK;
 
   // Q^T operand of this wave's query tile, and the tile's ancestor masks
-  const bool computes = wave < NQT;
-  const int n_q = 16 * wave + lr;
+  const bool computes = gw < NQT;
+  const int n_q = 16 * gw + lr;
   bf16x8 qv[KC];
   uint64_t ancq = 0;
 #pragma unroll
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a) {
   // Block ids of the chunk, validated once and kept in LDS.
   const int blk_first = k_begin / TV_BLOCK;
   const int nblk = (k_end - 1) / TV_BLOCK - blk_first + 1;      // <= kMaxChunkBlocks
-  for (int i = threadIdx.x; i < nblk; i += kThreads) {
+  for (int i = threadIdx.x; i < nblk; i += kAttnThreads) {
     int blk = bt[blk_first + i];
     if (blk < 0 || blk >= a.num_blocks) {
       s_badblk = 1;
@@ -232,15 +247,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Issue this wave's share of stage `st` into `dst` (K tile then V tile).
-  // Each 1 KB load covers 64/CPR consecutive keys of one cache block, so its
-  // block id is uniform across the wave.  The loads go HBM -> LDS directly;
-  // they are issued and awaited by hand (see the pipeline below).
+  uint8_t* gring = ring + grp * 2 * 2 * TILE;     // this group's two stage buffers
+
+  // Issue this wave's share of chunk stage `st` into `dst` (K tile then V
+  // tile).  Each 1 KB load covers 64/CPR consecutive keys of one cache
+  // block, so its block id is uniform across the wave.  The loads go HBM ->
+  // LDS directly; they are issued and awaited by hand (see below).
   auto issue = [&](int st, uint8_t* dst) {
     const int t0 = k_begin + SK * st;
 #pragma unroll
     for (int r = 0; r < LPW; ++r) {
-      const int li = wave * LPW + r;                 // 1 KB load index within the stage
+      const int li = gw * LPW + r;                   // 1 KB load index within the stage
       const int which = li / (TILE / 1024);          // 0 = K, 1 = V
       const int lt = li % (TILE / 1024);
       const int key0 = lt * (64 / CPR);              // first key of this load
@@ -270,125 +287,181 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a) {
     const int t0 = k_begin + SK * st;
     const uint8_t* kt_base = cur;
     const uint8_t* vt_base = cur + TILE;
+    // ---- scores S^T for the stage's 32 keys ----
+    f32x4 sc[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      // ---- scores S^T for 32 keys ----
-      f32x4 sc[2];
+    for (int kt = 0; kt < 2; ++kt) {
+      const int r = 16 * kt + lr;
+      f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int r = 32 * sub + 16 * kt + lr;
-        f32x4 acc{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(kt_base + tile_off<D>(r, 4 * c + lg)));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[c], acc, 0, 0, 0);
-        }
-        sc[kt] = acc;
+      for (int c = 0; c < KC; ++c) {
+        const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(kt_base + tile_off<D>(r, 4 * c + lg)));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[c], acc, 0, 0, 0);
       }
-      float mx = -INFINITY;
+      sc[kt] = acc;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 32 * sub + 16 * kt + 4 * lg + i;
-          bool vis = t < T;
-          if (t >= L) vis = vis && ((ancq >> ((t - L) & 63)) & 1ull);
-          const float v = vis ? sc[kt][i] * a.scale_log2 : -INFINITY;
-          sc[kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * kt + 4 * lg + i;
+        bool vis = t < T;
+        if (t >= L) vis = vis && ((ancq >> ((t - L) & 63)) & 1ull);
+        const float v = vis ? sc[kt][i] * a.scale_log2 : -INFINITY;
+        sc[kt][i] = v;
+        mx = fmaxf(mx, v);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Lazy rescaling: the running max moves (and O is rescaled) only when
-      // this tile's max exceeds it by more than 2^8; otherwise probabilities
-      // up to 256 are accumulated against the old max (exact in O / l).
-      const int rescale = __any(mx > mrun + 8.f);
-      float corr = 1.f;
-      if (rescale) {
-        const float m_new = fmaxf(mrun, mx);
-        corr = tv::exp2_fast(mrun - (m_new == -INFINITY ? 0.f : m_new));
-        mrun = m_new;
-        lrun *= corr;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          o[dt][0] *= corr; o[dt][1] *= corr; o[dt][2] *= corr; o[dt][3] *= corr;
-        }
-      }
-      const float m_use = mrun == -INFINITY ? 0.f : mrun;
-      f32x4 p[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = tv::exp2_fast(sc[kt][i] - m_use);
-          const float eb = tv::bf16_to_f32(tv::f32_to_bf16(e));   // the value the PV product uses
-          p[kt][i] = eb;
-          lrun += eb;
-        }
-      }
-      const bf16x8 pb = pack8(p[0], p[1]);
-      // ---- O^T += V^T P^T: V^T operand from two LDS transpose reads ----
-      // lane s of group lg supplies row 32sub + 16*half + 4lg + s/4, dims
-      // 16dt + 4(s%4) .. +3; lane j then holds those 4 rows at dim 16dt + j
-      const int vrow0 = 32 * sub + 4 * lg + (lr >> 2);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Lazy rescaling: the running max moves (and O is rescaled) only when
+    // this stage's max exceeds it by more than 2^8; otherwise probabilities
+    // up to 256 are accumulated against the old max (exact in O / l).
+    const int rescale = __any(mx > mrun + 8.f);
+    if (rescale) {
+      const float m_new = fmaxf(mrun, mx);
+      const float corr = tv::exp2_fast(mrun - (m_new == -INFINITY ? 0.f : m_new));
+      mrun = m_new;
+      lrun *= corr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d0 = 16 * dt + 4 * (lr & 3);
-        const int c16 = d0 >> 3, within = (d0 & 7) * 2;
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0, c16) + within));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0 + 16, c16) + within));
-        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-        const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[dt], 0, 0, 0);
+        o[dt][0] *= corr; o[dt][1] *= corr; o[dt][2] *= corr; o[dt][3] *= corr;
       }
+    }
+    const float m_use = mrun == -INFINITY ? 0.f : mrun;
+    f32x4 p[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = tv::exp2_fast(sc[kt][i] - m_use);
+        const float eb = tv::bf16_to_f32(tv::f32_to_bf16(e));   // the value the PV product uses
+        p[kt][i] = eb;
+        lrun += eb;
+      }
+    }
+    const bf16x8 pb = pack8(p[0], p[1]);
+    // ---- O^T += V^T P^T: V^T operand from two LDS transpose reads ----
+    // lane s of group lg supplies row 16*half + 4lg + s/4, dims
+    // 16dt + 4(s%4) .. +3; lane j then holds those 4 rows at dim 16dt + j
+    const int vrow0 = 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d0 = 16 * dt + 4 * (lr & 3);
+      const int c16 = d0 >> 3, within = (d0 & 7) * 2;
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0, c16) + within));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0 + 16, c16) + within));
+      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+      const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[dt], 0, 0, 0);
     }
   };
 
-  // ---- pipeline: two stages in flight ----
-  // Each wave waits for its own loads of the stage it is about to read
-  // (vmcnt: at most LPW loads - the next stage's - may still be in flight),
-  // then a barrier makes the whole stage visible; a second barrier after
-  // the compute frees the buffer for the stage after next.
+  // ---- the group's pipeline: two stage buffers, one stage in flight ----
+  // Group barrier: the 4 waves of the group count into an LDS word; a wave
+  // leaves once all 4 have arrived at this barrier (the count only grows).
+  // A wave arrives only after its LDS reads and its stage loads it waited
+  // for are complete, so a stage is read only after all its loads landed
+  // and refilled only after every wave of the group has read it.  The
+  // waits are explicit (the atomics are relaxed: acquire/release would also
+  // drain the loads of the stage in flight); the asm statements keep the
+  // compiler from moving LDS accesses across the barrier.
+  int phase = 0;
+  auto group_barrier = [&]() {
+    ++phase;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(&s_gbar[grp], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    unsigned polls = 0;
+    while (__hip_atomic_load(&s_gbar[grp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 4 * phase) {
+      if (++polls > kGroupSpinLimit) {
+        s_hung = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+  };
   auto wait_stage = [&](bool next_in_flight) {
     if (next_in_flight) {
-      if constexpr (LPW == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      if constexpr (LPW == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
-  auto step = [&](int it, uint8_t* cur) {
-    wait_stage(it + 1 < nst);
-    asm volatile("s_barrier" ::: "memory");
-    if (computes) compute(it, cur);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (it + 2 < nst) issue(it + 2, cur);
-  };
-  issue(0, stage_buf0);
+  if (nloc > 0) issue(grp, gring);
   // A wait the compiler can see: the Q and mask loads above are complete
   // from here on, so it adds no wait of its own inside the loop (such a
   // wait would also drain the next stage's loads, which it does not know).
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
-  if (nst > 1) issue(1, stage_buf1);
-  for (int it = 0; it < nst; it += 2) {
-    step(it, stage_buf0);
-    if (it + 1 < nst) step(it + 1, stage_buf1);
+  if (nloc > 1) issue(grp + kGroups, gring + 2 * TILE);
+  for (int it = 0; it < nloc; ++it) {
+    uint8_t* cur = gring + (it & 1) * 2 * TILE;
+    wait_stage(it + 1 < nloc);
+    group_barrier();
+    if (computes) compute(grp + kGroups * it, cur);
+    group_barrier();
+    if (it + 2 < nloc) issue(grp + kGroups * (it + 2), cur);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
   lrun += __shfl_xor(lrun, 16, 64);
   lrun += __shfl_xor(lrun, 32, 64);
   __syncthreads();
+
+  // ---- merge the groups' states through LDS (the ring is free now) ----
+  // Slot layout [group - 1][query tile][DT*4 + 2][lane] floats: each lane
+  // writes and reads only its own column, so there are no bank conflicts.
+  float* mg = reinterpret_cast<float*>(ring);
+  if (grp > 0 && computes) {
+    float* dst = mg + ((grp - 1) * NQT + gw) * SLOT + lane;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(dt * 4 + i) * 64] = o[dt][i];
+    dst[(DT * 4) * 64] = mrun;
+    dst[(DT * 4 + 1) * 64] = lrun;
+  }
+  __syncthreads();
   if (s_badblk && threadIdx.x == 0) a.status[b] = TV_REQ_BAD_BLOCK;
+  if (s_hung && threadIdx.x == 0) a.status[b] = TV_REQ_TIMEOUT;
+  if (grp != 0 || !computes) return;
+  float mo[kGroups], lo_[kGroups];
+  mo[0] = mrun;
+  lo_[0] = lrun;
+#pragma unroll
+  for (int g2 = 1; g2 < kGroups; ++g2) {
+    const float* src = mg + ((g2 - 1) * NQT + gw) * SLOT + lane;
+    mo[g2] = src[(DT * 4) * 64];
+    lo_[g2] = src[(DT * 4 + 1) * 64];
+  }
+  float M = mo[0];
+#pragma unroll
+  for (int g2 = 1; g2 < kGroups; ++g2) M = fmaxf(M, mo[g2]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float wgt[kGroups];
+  float lsum = 0.f;
+#pragma unroll
+  for (int g2 = 0; g2 < kGroups; ++g2) {
+    wgt[g2] = tv::exp2_fast(mo[g2] - Mu);
+    lsum += wgt[g2] * lo_[g2];
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float acc = wgt[0] * o[dt][i];
+#pragma unroll
+      for (int g2 = 1; g2 < kGroups; ++g2) acc += wgt[g2] * mg[((g2 - 1) * NQT + gw) * SLOT + (dt * 4 + i) * 64 + lane];
+      o[dt][i] = acc;
+    }
 
   if (a.splits == 1) {
-    if (computes && n_q < N) {
+    if (n_q < N) {
       uint16_t* out = static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(b) * N + n_q) * a.H + h) * D;
-      const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         uint2 v;
@@ -403,13 +476,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a) {
   // (merged by attn_merge_kernel after this kernel; the kernel boundary makes
   // the partials of every XCD's L2 visible, no device-scope fence is needed)
   const size_t pbase = ((static_cast<size_t>(b) * a.H + h) * a.splits + s) * a.npad;
-  if (computes && n_q < N) {
+  if (n_q < N) {
     float* po = a.part_o + (pbase + n_q) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lg) = o[dt];
     if (lg == 0) {
-      a.part_ml[(pbase + n_q) * 2 + 0] = mrun;
-      a.part_ml[(pbase + n_q) * 2 + 1] = lrun;
+      a.part_ml[(pbase + n_q) * 2 + 0] = M;
+      a.part_ml[(pbase + n_q) * 2 + 1] = lsum;
     }
   }
 }
@@ -601,21 +674,65 @@ struct Plan {
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Chunking of the key range: about 512 workgroups (two per CU) when the
-// prefixes are long enough, chunks of at least 256 keys, a multiple of 64.
-Plan make_plan(int B, int N, int H, int D, int max_blocks) {
+// bf16 attention workgroups resident at once on the current device
+// (compute units x workgroups per CU at head dim D; cached per device).
+int attn_slots(int D) {
+  static int cache[64][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const int di = D == 128 ? 1 : 0;
+  if (dev >= 0 && dev < 64 && cache[dev][di] > 0) return cache[dev][di];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const void* fn = D == 128 ? reinterpret_cast<const void*>(attn_mfma_kernel<128, 4>)
+                            : reinterpret_cast<const void*>(attn_mfma_kernel<64, 4>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kAttnThreads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int slots = cus * per_cu;
+  if (dev >= 0 && dev < 64) cache[dev][di] = slots;
+  return slots;
+}
+
+// Chunking of the key range.
+// bf16: a launch runs in rounds of as many workgroups as are resident at
+// once (one per CU at D = 128); the chunk count minimises rounds x (chunk keys + the partial
+// written and read back, 2 * npad key-equivalents) + the merge launch
+// (about 4 us, ~19000 / D key-loads of one CU).
+// fp32: about 512 workgroups, chunks of at least 256 keys.
+Plan make_plan(tv_dtype dt, int B, int N, int H, int D, int max_blocks) {
   Plan p;
   const long keys_max = static_cast<long>(max_blocks) * TV_BLOCK;
-  const long bh = static_cast<long>(B) * H;
-  long s = (512 + bh - 1) / bh;
-  s = std::min(s, (keys_max + 255) / 256);
-  s = std::max(1L, std::min(s, static_cast<long>(kMaxSplits)));
-  s = std::max(s, (keys_max + kMaxChunkKeys - 1) / kMaxChunkKeys);
-  long c = (keys_max + s - 1) / s;
-  c = (c + 63) / 64 * 64;
+  const long pairs = static_cast<long>(B) * H;
+  p.npad = (N + 15) / 16 * 16;
+  long c = 0;
+  if (dt == TV_BF16) {
+    const long slots = attn_slots(D);
+    const double merge_keys = 19000.0 / D;
+    const long s_min = (keys_max + kMaxChunkKeys - 1) / kMaxChunkKeys;
+    double best = 0.0;
+    for (long s = s_min; s <= std::max<long>(s_min, kMaxSplits); ++s) {
+      long cs = (keys_max + s - 1) / s;
+      cs = (cs + 63) / 64 * 64;
+      const long se = (keys_max + cs - 1) / cs;
+      if (se != s) continue;                          // same chunking as a smaller s
+      const long rounds = (pairs * se + slots - 1) / slots;
+      const double cost = static_cast<double>(rounds) * (static_cast<double>(cs) + (se > 1 ? 2.0 * p.npad : 0.0)) +
+                          (se > 1 ? merge_keys : 0.0);
+      if (c == 0 || cost < best) {
+        best = cost;
+        c = cs;
+      }
+    }
+  } else {
+    long s = (512 + pairs - 1) / pairs;
+    s = std::min(s, (keys_max + 255) / 256);
+    s = std::max(1L, std::min(s, static_cast<long>(kMaxSplits)));
+    c = (keys_max + s - 1) / s;
+    c = (c + 63) / 64 * 64;
+  }
   p.chunk = static_cast<int>(c);
   p.splits = static_cast<int>((keys_max + c - 1) / c);
-  p.npad = (N + 15) / 16 * 16;
   if (p.splits > 1) {
     const size_t rows = static_cast<size_t>(B) * H * p.splits * p.npad;
     p.off_ml = align256(rows * D * sizeof(float));
@@ -629,14 +746,14 @@ Plan make_plan(int B, int N, int H, int D, int max_blocks) {
 }  // namespace
 
 extern "C" size_t tree_attn_verify_workspace(tv_dtype dt, int B, int N, int H, int D, int max_blocks) {
-  (void)dt;
   if (B <= 0 || N <= 0 || H <= 0 || max_blocks <= 0) return 0;
-  return make_plan(B, N, H, D, max_blocks).ws_bytes;
+  if (dt != TV_F32 && dt != TV_BF16) return 0;
+  return make_plan(dt, B, N, H, D, max_blocks).ws_bytes;
 }
 
 template <int D, int NQT>
 static void launch_mfma(dim3 grid, hipStream_t st, const AttnArgs& a) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NQT>), grid, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NQT>), grid, dim3(kAttnThreads), 0, st, a);
 }
 
 extern "C" tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
@@ -654,7 +771,7 @@ extern "C" tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, f
   if (B == 0 || N == 0) return TV_OK;
   if (!q || !k_cache || !v_cache || !block_table || !prefix_len || !anc || !status || !out)
     return TV_EINVAL;
-  const Plan p = make_plan(B, N, H, D, max_blocks);
+  const Plan p = make_plan(dt, B, N, H, D, max_blocks);
   if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes)) return TV_EWORKSPACE;
 
   AttnArgs a;
