@@ -116,19 +116,20 @@ def main():
 
     def step(i, ev=None):
         c = copies[i % n_copies]
+        cur = torch.cuda.current_stream()              # the capture stream inside a graph
         pl.copy_(pl0)                                  # the commit of the last step grew it
-        if ev: ev[0].record(stream)
+        if ev: ev[0].record(cur)
         tv.tree_build_mask(parent, anc, child, depth, status)
-        if ev: ev[1].record(stream)
+        if ev: ev[1].record(cur)
         tv.tree_attn_verify(c["q"], c["k"], c["v"], bt, pl, anc, status, out, ws_attn, scale=w.scale)
-        if ev: ev[2].record(stream)
+        if ev: ev[2].record(cur)
         tv.tree_verify_greedy(c["tl"], token, child, status, g_acc, g_num, g_bonus, ws_v)
-        if ev: ev[3].record(stream)
+        if ev: ev[3].record(cur)
         tv.tree_verify_mss(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset + i, m_acc,
                            m_num, m_bonus, m_rounds, ws_v)
-        if ev: ev[4].record(stream)
+        if ev: ev[4].record(cur)
         tv.kv_commit_accepted(c["k"], c["v"], bt, pl, m_acc, m_num, status)
-        if ev: ev[5].record(stream)
+        if ev: ev[5].record(cur)
 
     for i in range(args.warmup):
         step(i)

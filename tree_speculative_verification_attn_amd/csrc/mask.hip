@@ -48,11 +48,17 @@ __global__ __launch_bounds__(64) void build_mask_kernel(int N, const int32_t* __
     anc[static_cast<size_t>(b) * N + i] = a;
     depth[static_cast<size_t>(b) * N + i] = d;
   }
-  // child[u + 1] = set of nodes whose parent is u, u = -1 .. N-1
-  for (int u = -1; u < N; ++u) {
-    const uint64_t m = bad ? 0ull : static_cast<uint64_t>(__ballot(live && p == u));
-    if (i == 0) child[static_cast<size_t>(b) * (N + 1) + (u + 1)] = m;
-  }
+  // child[u + 1] = set of nodes whose parent is u, u = -1 .. N-1: each node
+  // ORs its bit into its parent's word (LDS), then lane u + 1 stores word u + 1
+  __shared__ unsigned long long s_child[TV_MAX_NODES + 1];
+  s_child[i] = 0ull;
+  if (i == 0) s_child[TV_MAX_NODES] = 0ull;
+  __syncthreads();
+  if (!bad && node) atomicOr(&s_child[p + 1], 1ull << i);
+  __syncthreads();
+  uint64_t* crow = child + static_cast<size_t>(b) * (N + 1);
+  if (i <= N) crow[i] = s_child[i];
+  if (i == 0 && N == TV_MAX_NODES) crow[N] = s_child[N];
   if (i == 0) status[b] = bad ? TV_REQ_BAD_PARENT : TV_REQ_OK;
 }
 

@@ -111,4 +111,92 @@ __device__ __forceinline__ int wave_or(int v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Wave64 reductions and scans on DPP lane moves (VALU, no LDS round trip).
+// gfx9 DPP controls: quad_perm [1,0,3,2] and [2,3,0,1] pair lanes 1 and 2
+// apart, row_half_mirror / row_mirror pair lanes across 8- and 16-lane
+// groups, row_bcast:15 / row_bcast:31 carry a row's last lane into the next
+// row(s), row_shr:n shifts within a row, wave_shr:1 shifts the whole wave.
+// Reductions leave the result in lane 63 and return it to every lane.
+// ---------------------------------------------------------------------------
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowMirror = 0x140, kRowHalfMirror = 0x141,
+              kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+}
+
+template <int ctrl, int row_mask = 0xF>
+__device__ __forceinline__ int dpp_mov(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, ctrl, row_mask, 0xF, false);
+}
+template <int ctrl, int row_mask = 0xF>
+__device__ __forceinline__ double dpp_mov_f64(double old, double v) {
+  const int lo = dpp_mov<ctrl, row_mask>(__double2loint(old), __double2loint(v));
+  const int hi = dpp_mov<ctrl, row_mask>(__double2hiint(old), __double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                          __builtin_amdgcn_readlane(__double2loint(v), lane));
+}
+
+// sum of a double over the wave (same value, bit for bit, in every lane)
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v += dpp_mov_f64<dpp::kQuadXor1>(0.0, v);
+  v += dpp_mov_f64<dpp::kQuadXor2>(0.0, v);
+  v += dpp_mov_f64<dpp::kRowHalfMirror>(0.0, v);
+  v += dpp_mov_f64<dpp::kRowMirror>(0.0, v);
+  v += dpp_mov_f64<dpp::kRowBcast15, 0xA>(0.0, v);
+  v += dpp_mov_f64<dpp::kRowBcast31, 0xC>(0.0, v);
+  return readlane_f64(v, 63);
+}
+
+// OR of an int over the wave
+__device__ __forceinline__ int wave_or_dpp(int v) {
+  v |= dpp_mov<dpp::kQuadXor1>(0, v);
+  v |= dpp_mov<dpp::kQuadXor2>(0, v);
+  v |= dpp_mov<dpp::kRowHalfMirror>(0, v);
+  v |= dpp_mov<dpp::kRowMirror>(0, v);
+  v |= dpp_mov<dpp::kRowBcast15, 0xA>(0, v);
+  v |= dpp_mov<dpp::kRowBcast31, 0xC>(0, v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// max over the wave with the lowest index among equal maxima; NaN values
+// never win (callers flag them separately)
+__device__ __forceinline__ void argmax_merge(float& m, int& a, float m2, int a2) {
+  if (m2 > m || (m2 == m && a2 < a)) {
+    m = m2;
+    a = a2;
+  }
+}
+template <int ctrl, int row_mask = 0xF>
+__device__ __forceinline__ void argmax_step(float& m, int& a) {
+  const float m2 = __int_as_float(dpp_mov<ctrl, row_mask>(__float_as_int(-INFINITY), __float_as_int(m)));
+  const int a2 = dpp_mov<ctrl, row_mask>(0x7FFFFFFF, a);
+  argmax_merge(m, a, m2, a2);
+}
+__device__ __forceinline__ void wave_argmax_dpp(float& m, int& a) {
+  argmax_step<dpp::kQuadXor1>(m, a);
+  argmax_step<dpp::kQuadXor2>(m, a);
+  argmax_step<dpp::kRowHalfMirror>(m, a);
+  argmax_step<dpp::kRowMirror>(m, a);
+  argmax_step<dpp::kRowBcast15, 0xA>(m, a);
+  argmax_step<dpp::kRowBcast31, 0xC>(m, a);
+  m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+  a = __builtin_amdgcn_readlane(a, 63);
+}
+
+// inclusive prefix sum of a double over the wave (lane order); *excl gets
+// the previous lane's inclusive value, bit for bit (0 in lane 0)
+__device__ __forceinline__ double wave_scan_dpp(double v, double* excl) {
+  v += dpp_mov_f64<0x111>(0.0, v);        // row_shr:1
+  v += dpp_mov_f64<0x112>(0.0, v);        // row_shr:2
+  v += dpp_mov_f64<0x114>(0.0, v);        // row_shr:4
+  v += dpp_mov_f64<0x118>(0.0, v);        // row_shr:8
+  v += dpp_mov_f64<dpp::kRowBcast15, 0xA>(0.0, v);
+  v += dpp_mov_f64<dpp::kRowBcast31, 0xC>(0.0, v);
+  *excl = dpp_mov_f64<dpp::kWaveShr1>(0.0, v);
+  return v;
+}
+
 }  // namespace tv

@@ -158,24 +158,14 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int i) {
   return __builtin_ctzll(m);
 }
 
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  return v;
-}
-
 __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(v), o, 64));
-  return v;
+  const uint32_t lo = static_cast<uint32_t>(tv::wave_or_dpp(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(tv::wave_or_dpp(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ double block_sum(double v, double* red) {
-  v = tv::wave_sum(v);
+  v = tv::wave_sum_dpp(v);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
   if (lane == 0) red[wave] = v;
@@ -343,16 +333,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
           }
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(mx, o, 64);
-        const int a2 = __shfl_xor(arg, o, 64);
-        if (m2 > mx || (m2 == mx && a2 < arg)) {
-          mx = m2;
-          arg = a2;
-        }
-        flags |= __shfl_xor(flags, o, 64);
-      }
+      tv::wave_argmax_dpp(mx, arg);
+      flags = tv::wave_or_dpp(flags);
       if (lane == 0) {
         s_wm[wave] = mx;
         s_wa[wave] = arg;
@@ -472,16 +454,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
             am = ag;
           }
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float m2 = __shfl_xor(m, o, 64);
-          const int a2 = __shfl_xor(am, o, 64);
-          if (m2 > m || (m2 == m && a2 < am)) {
-            m = m2;
-            am = a2;
-          }
-          fl |= __shfl_xor(fl, o, 64);
-        }
+        tv::wave_argmax_dpp(m, am);
+        fl = tv::wave_or_dpp(fl);
         fail = (fl & (FLAG_NAN | FLAG_PINF)) || !(fl & FLAG_FINITE);
         if (!fail && !mss) {
           // greedy: the child whose token is the argmax, lowest node first
@@ -508,7 +482,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
             s_tot[gg] = tg;
             part += tg;
           }
-          Z_now = tv::wave_sum(part);
+          Z_now = tv::wave_sum_dpp(part);
           m_now = m;
           md_now = 0;
         }
@@ -519,8 +493,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
           part += join64(s_hw[gg][0], s_hw[gg][1]);
           anyb |= static_cast<int>(s_hw[gg][2]);
         }
-        const double Znew = tv::wave_sum(part);
-        fail = tv::wave_or(anyb) != 0;
+        const double Znew = tv::wave_sum_dpp(part);
+        fail = tv::wave_or_dpp(anyb) != 0;
         take = !fail && Znew > 0.0;
         if (take) {           // else the distribution stays (zero-normaliser guard)
           for (int gg = lane; gg < G; gg += 64) s_tot[gg] = join64(s_hw[gg][0], s_hw[gg][1]);
@@ -561,9 +535,10 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
           // totals in index order; the threshold inside it
           const tv::u32x4 w0 = tv::mss_words(a.seed, a.offset, b, u + 1, 0);
           double run = 0.0;
-          for (int base = 0; base < G; base += 64) {
+          for (int base = 0; base < G; base += 64) {     // the same sums as the search below
             const double v = base + lane < G ? s_tot[base + lane] : 0.0;
-            run += __shfl(wave_incl_scan(v), 63, 64);
+            double ex;
+            run = tv::readlane_f64(run + tv::wave_scan_dpp(v, &ex), 63);
           }
           const double T = tv::unit_open0(w0.z) * run;
           double carry = 0.0;
@@ -571,25 +546,21 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
           double ex_owner = 0.0, ex_last = 0.0;
           for (int base = 0; base < G && owner < 0; base += 64) {
             const double v = base + lane < G ? s_tot[base + lane] : 0.0;
-            const double incl = carry + wave_incl_scan(v);
-            double excl = __shfl_up(incl, 1, 64);
-            if (lane == 0) excl = carry;
+            double excl;
+            const double incl = carry + tv::wave_scan_dpp(v, &excl);
+            excl += carry;
             const uint64_t hit = __ballot(v > 0.0 && excl < T && incl >= T);
             const uint64_t pos = __ballot(v > 0.0);
             if (hit) {
               const int l = __builtin_ctzll(hit);
               owner = base + l;
-              ex_owner = __shfl(excl, l, 64);
+              ex_owner = tv::readlane_f64(excl, l);
             } else if (pos) {
               const int l = 63 - __builtin_clzll(pos);
               last = base + l;
-              ex_last = __shfl(excl, l, 64);
+              ex_last = tv::readlane_f64(excl, l);
             }
-            carry = __shfl(incl, 63, 64);
-          }
-          if (owner < 0) {     // rounding left the total short: last non-empty slice
-            owner = last;
-            ex_owner = ex_last;
+            carry = tv::readlane_f64(incl, 63);
           }
           if (lane == 0) {
             s_owner = owner;
@@ -625,7 +596,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       cur[k] = k < nx ? (md == 0 ? (lv[k] == -INFINITY ? 0.f : tv::exp_acc(lv[k] - mm)) : cv[k]) : 0.f;
       part += static_cast<double>(cur[k]);
     }
-    const double wincl = wave_incl_scan(part);
+    double wexcl;
+    const double wincl = tv::wave_scan_dpp(part, &wexcl);
     if (lane == 63) red[wave] = wincl;
     if (t == 0) s_found = -1;
     __syncthreads();
@@ -636,8 +608,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       total += red[w2];
     }
     const double incl = wbase + wincl;
-    const double prev_w = __shfl_up(wincl, 1, 64);
-    const double excl = lane > 0 ? wbase + prev_w : wbase;   // the previous thread's incl, bit for bit
+    const double excl = wbase + wexcl;     // the previous thread's incl, bit for bit (wexcl = 0 in lane 0)
     // threshold in (0, slice total]: exactly one thread has excl < T <= incl
     const double T = fmin(s_Tloc, total);
     if (excl < T && incl >= T) {
