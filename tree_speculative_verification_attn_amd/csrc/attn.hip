@@ -37,6 +37,8 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
@@ -161,6 +163,7 @@ __device__ __forceinline__ int tile_off(int r, int c16) {   // byte offset
 // chunks per (b, h) the merged state is written as an unnormalised partial
 // that attn_merge_kernel combines.
 constexpr int kGroups = 4;                  // 4-wave groups per workgroup
+constexpr int kRing = 2;                    // stage buffers per group
 constexpr int kGroupThreads = 256;
 constexpr int kAttnThreads = kGroups * kGroupThreads;
 constexpr unsigned kGroupSpinLimit = 1u << 26;
@@ -175,51 +178,30 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   constexpr int LPW = (2 * TILE / 1024) / 4;   // 1 KB wave-loads per wave per stage
   static_assert(LPW == 4 || LPW == 2, "stage size");
   constexpr int SLOT = (DT * 4 + 2) * 64;       // floats of one merge slot (see the end)
-  static_assert((kGroups - 1) * NQT * SLOT * 4 <= kGroups * 2 * 2 * TILE, "merge area");
+  static_assert((kGroups - 1) * NQT * SLOT * 4 <= kGroups * kRing * 2 * TILE, "merge area");
+  static_assert(kRing >= 2 && kRing <= 4, "ring depth");
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = wave >> 2, gw = wave & 3;          // group, wave within the group
   const int lr = lane & 15, lg = lane >> 4;
 
-  // per group: two stage buffers, each [K tile | V tile]
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kGroups * 2 * 2 * TILE];
-  __shared__ int s_gate, s_badblk, s_hung;
+  // per group: kRing stage buffers, each [K tile | V tile]
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kGroups * kRing * 2 * TILE];
+  __shared__ int s_hung;
   __shared__ int s_gbar[kGroups];
   __shared__ int s_blk[kMaxChunkBlocks];
 
-  if (threadIdx.x == 0) {
-    s_gate = request_gate(a, b);
-    s_badblk = 0;
-    s_hung = 0;
-  }
-  if (threadIdx.x < kGroups) s_gbar[threadIdx.x] = 0;
-  __syncthreads();
-  const int gate = s_gate;
-  if (gate != TV_REQ_OK) {
-    if (gate == TV_REQ_KV_CAPACITY && threadIdx.x == 0 && a.status[b] == TV_REQ_OK)
-      a.status[b] = TV_REQ_KV_CAPACITY;
-    if (s == 0) zero_out<uint16_t>(a, b, h);
-    return;
-  }
-  const int L = a.prefix_len[b];
+  // Every load that depends on nothing goes out first, in every thread:
+  // the request's status and prefix length (same address in all threads),
+  // and this wave's Q tile and ancestor masks.  The prefix length is not
+  // written during the launch, so every thread sees the same value; the
+  // status can be (another workgroup of the request may flag a bad block),
+  // so the workgroup agrees on it at its first barrier below.
   const int N = a.N;
-  const int T = L + N;
-  const int k_begin = s * a.chunk;
-  if (k_begin >= T) return;                 // empty chunk: not counted by the merge
-  const int k_end = min(T, k_begin + a.chunk);
-  const int nst = (k_end - k_begin + SK - 1) / SK;                // stages of the chunk
-  const int nloc = nst > grp ? (nst - grp + kGroups - 1) / kGroups : 0;   // this group's
-
+  const int st = a.status[b];
+  const int L = a.prefix_len[b];
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
-  const uint8_t* __restrict__ kg = static_cast<const uint8_t*>(a.kc);
-  const uint8_t* __restrict__ vg = static_cast<const uint8_t*>(a.vc);
-  const int32_t* __restrict__ bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
-  const size_t head_bytes = static_cast<size_t>(TV_BLOCK) * D * 2;
-  const size_t blk_bytes = static_cast<size_t>(a.H) * head_bytes;
-  const int last_blk = (T - 1) / TV_BLOCK, last_row = (T - 1) % TV_BLOCK;
-
-  // Q^T operand of this wave's query tile, and the tile's ancestor masks
   const bool computes = gw < NQT;
   const int n_q = 16 * gw + lr;
   bf16x8 qv[KC];
@@ -233,21 +215,48 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       qv[c] = as_bf16x8(*reinterpret_cast<const uint4*>(
           qg + ((static_cast<size_t>(b) * N + n_q) * a.H + h) * D + 32 * c + 8 * lg));
   }
+  if (L < 0 || static_cast<int64_t>(L) + N > static_cast<int64_t>(a.max_blocks) * TV_BLOCK) {
+    // no workgroup of this request gets further, so no bad-block flag can race this
+    if (threadIdx.x == 0 && st == TV_REQ_OK) a.status[b] = TV_REQ_KV_CAPACITY;
+    if (s == 0) zero_out<uint16_t>(a, b, h);
+    return;
+  }
+  const int T = L + N;
+  const int k_begin = s * a.chunk;
+  if (k_begin >= T) return;                 // empty chunk (never chunk 0): not counted by the merge
+  const int k_end = min(T, k_begin + a.chunk);
+  const int nst = (k_end - k_begin + SK - 1) / SK;                // stages of the chunk
+  const int nloc = nst > grp ? (nst - grp + kGroups - 1) / kGroups : 0;   // this group's
+
+  const uint8_t* __restrict__ kg = static_cast<const uint8_t*>(a.kc);
+  const uint8_t* __restrict__ vg = static_cast<const uint8_t*>(a.vc);
+  const int32_t* __restrict__ bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  const size_t head_bytes = static_cast<size_t>(TV_BLOCK) * D * 2;
+  const size_t blk_bytes = static_cast<size_t>(a.H) * head_bytes;
+  const int last_blk = (T - 1) / TV_BLOCK, last_row = (T - 1) % TV_BLOCK;
 
   // Block ids of the chunk, validated once and kept in LDS.
   const int blk_first = k_begin / TV_BLOCK;
   const int nblk = (k_end - 1) / TV_BLOCK - blk_first + 1;      // <= kMaxChunkBlocks
+  int bad = 0;
   for (int i = threadIdx.x; i < nblk; i += kAttnThreads) {
     int blk = bt[blk_first + i];
     if (blk < 0 || blk >= a.num_blocks) {
-      s_badblk = 1;
+      bad = 1;
       blk = 0;
     }
     s_blk[i] = blk;
   }
-  __syncthreads();
+  if (threadIdx.x < kGroups) s_gbar[threadIdx.x] = 0;
+  if (threadIdx.x == 0) s_hung = 0;
+  // (__syncthreads_or is a logical OR: one call per flag)
+  if (__syncthreads_or(st != TV_REQ_OK)) {  // a skipped request: zero output
+    if (s == 0) zero_out<uint16_t>(a, b, h);
+    return;
+  }
+  const int badblk = __syncthreads_or(bad);
 
-  uint8_t* gring = ring + grp * 2 * 2 * TILE;     // this group's two stage buffers
+  uint8_t* gring = ring + grp * kRing * 2 * TILE;   // this group's stage buffers
 
   // Issue this wave's share of chunk stage `st` into `dst` (K tile then V
   // tile).  Each 1 KB load covers 64/CPR consecutive keys of one cache
@@ -300,26 +309,39 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       }
       sc[kt] = acc;
     }
+    // scale and mask: a stage of prefix keys only (all but the last one or
+    // two of a chunk) is visible to every node, so only the others test the
+    // ancestor bits (branch-free: one select per score)
     float mx = -INFINITY;
+    if (t0 + SK <= L) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * kt + 4 * lg + i;
-        bool vis = t < T;
-        if (t >= L) vis = vis && ((ancq >> ((t - L) & 63)) & 1ull);
-        const float v = vis ? sc[kt][i] * a.scale_log2 : -INFINITY;
-        sc[kt][i] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int i = 0; i < 4; ++i) {
+          sc[kt][i] *= a.scale_log2;
+          mx = fmaxf(mx, sc[kt][i]);
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * kt + 4 * lg + i;
+          const int rel = t - L;
+          const bool vis = (t < T) & ((rel < 0) | (((ancq >> (rel & 63)) & 1ull) != 0ull));
+          const float v = vis ? sc[kt][i] * a.scale_log2 : -INFINITY;
+          sc[kt][i] = v;
+          mx = fmaxf(mx, v);
+        }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescaling: the running max moves (and O is rescaled) only when
-    // this stage's max exceeds it by more than 2^8; otherwise probabilities
-    // up to 256 are accumulated against the old max (exact in O / l).
-    const int rescale = __any(mx > mrun + 8.f);
-    if (rescale) {
+    // Lazy rescaling: the running max (one per query column, uniform over
+    // the column's 4 lane groups) moves, and O is rescaled, only when a score
+    // exceeds it by more than 2^8; otherwise probabilities up to 256 are
+    // accumulated against the old max (exact in O / l).  Only then is the
+    // column max formed across lane groups.
+    if (__any(mx > mrun + 8.f)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(mrun, mx);
       const float corr = tv::exp2_fast(mrun - (m_new == -INFINITY ? 0.f : m_new));
       mrun = m_new;
@@ -330,18 +352,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       }
     }
     const float m_use = mrun == -INFINITY ? 0.f : mrun;
-    f32x4 p[2];
+    // P in bf16 (the value the PV product uses, rounded by the hardware
+    // convert), and l accumulated from the same rounded values
+    uint32_t pk[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = tv::exp2_fast(sc[kt][i] - m_use);
-        const float eb = tv::bf16_to_f32(tv::f32_to_bf16(e));   // the value the PV product uses
-        p[kt][i] = eb;
-        lrun += eb;
+      for (int i = 0; i < 4; i += 2) {
+        const f32x2 e2 = {tv::exp2_fast(sc[kt][i] - m_use), tv::exp2_fast(sc[kt][i + 1] - m_use)};
+        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(e2, bf16x2));
+        pk[kt * 2 + i / 2] = u;
+        lrun += __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
       }
-    }
-    const bf16x8 pb = pack8(p[0], p[1]);
+    const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
     // ---- O^T += V^T P^T: V^T operand from two LDS transpose reads ----
     // lane s of group lg supplies row 16*half + 4lg + s/4, dims
     // 16dt + 4(s%4) .. +3; lane j then holds those 4 rows at dim 16dt + j
@@ -360,7 +383,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     }
   };
 
-  // ---- the group's pipeline: two stage buffers, one stage in flight ----
+  // ---- the group's pipeline: kRing stage buffers, kRing - 1 stages in flight ----
   // Group barrier: the 4 waves of the group count into an LDS word; a wave
   // leaves once all 4 have arrived at this barrier (the count only grows).
   // A wave arrives only after its LDS reads and its stage loads it waited
@@ -384,27 +407,32 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     }
     asm volatile("" ::: "memory");
   };
-  auto wait_stage = [&](bool next_in_flight) {
-    if (next_in_flight) {
-      if constexpr (LPW == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  auto wait_stage = [&](int later) {        // later stages allowed in flight
+    if constexpr (LPW == 4) {
+      if (later >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else if (later == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (later >= 3) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else if (later == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
-  if (nloc > 0) issue(grp, gring);
   // A wait the compiler can see: the Q and mask loads above are complete
-  // from here on, so it adds no wait of its own inside the loop (such a
-  // wait would also drain the next stage's loads, which it does not know).
+  // from here on (they went out first and have long arrived), so it adds
+  // no wait of its own inside the loop, where a wait would also drain the
+  // stage loads in flight, which it does not know about.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
-  if (nloc > 1) issue(grp + kGroups, gring + 2 * TILE);
+  for (int r = 0; r < kRing && r < nloc; ++r) issue(grp + kGroups * r, gring + r * 2 * TILE);
   for (int it = 0; it < nloc; ++it) {
-    uint8_t* cur = gring + (it & 1) * 2 * TILE;
-    wait_stage(it + 1 < nloc);
+    uint8_t* cur = gring + (it % kRing) * 2 * TILE;
+    wait_stage(min(kRing - 1, nloc - 1 - it));
     group_barrier();
     if (computes) compute(grp + kGroups * it, cur);
     group_barrier();
-    if (it + 2 < nloc) issue(grp + kGroups * (it + 2), cur);
+    if (it + kRing < nloc) issue(grp + kGroups * (it + kRing), cur);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lrun += __shfl_xor(lrun, 16, 64);
@@ -425,7 +453,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     dst[(DT * 4 + 1) * 64] = lrun;
   }
   __syncthreads();
-  if (s_badblk && threadIdx.x == 0) a.status[b] = TV_REQ_BAD_BLOCK;
+  if (badblk && threadIdx.x == 0) a.status[b] = TV_REQ_BAD_BLOCK;
   if (s_hung && threadIdx.x == 0) a.status[b] = TV_REQ_TIMEOUT;
   if (grp != 0 || !computes) return;
   float mo[kGroups], lo_[kGroups];

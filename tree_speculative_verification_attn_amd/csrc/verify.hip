@@ -477,8 +477,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
           for (int gg = lane; gg < G; gg += 64) {
             const float mg = __uint_as_float(s_hw[gg][0]);
             const double tg = mg == -INFINITY ? 0.0
-                              : join64(s_hw[gg][1], s_hw[gg][2]) *
-                                    exp(static_cast<double>(mg) - static_cast<double>(m));
+                              : join64(s_hw[gg][1], s_hw[gg][2]) * static_cast<double>(tv::exp_acc(mg - m));
             s_tot[gg] = tg;
             part += tg;
           }
@@ -510,14 +509,13 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
             if (q_bad(qx_c)) {
               fail = true;
             } else {
-              const double px = md_now == 0
-                                    ? (lx_c == -INFINITY ? 0.0
-                                                         : exp(static_cast<double>(lx_c) - static_cast<double>(m_now)) / Z_now)
-                                    : static_cast<double>(s_rx[cand]) / Z_now;
-              const double ratio =
-                  qx_c > 0.f ? px / static_cast<double>(qx_c) : (px > 0.0 ? INFINITY : 0.0);
+              // u1 <= p(x) / q(x) with p(x) = e / Z, tested as u1 * q(x) * Z <= e
+              // (no division); q(x) = 0 accepts exactly when p(x) > 0
+              const double e = md_now == 0 ? (lx_c == -INFINITY ? 0.0 : static_cast<double>(tv::exp_acc(lx_c - m_now)))
+                                           : static_cast<double>(s_rx[cand]);
+              const bool accept = qx_c > 0.f ? tv::unit_open0(w.y) * static_cast<double>(qx_c) * Z_now <= e : e > 0.0;
               ++s_rounds;
-              if (tv::unit_open0(w.y) <= ratio) {
+              if (accept) {
                 s_acc[s_k++] = cand;
                 s_u = cand;
                 s_U = s_child[cand + 1];
