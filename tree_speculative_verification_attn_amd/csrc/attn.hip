@@ -194,10 +194,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
 
   // Every load that depends on nothing goes out first, in every thread:
   // the request's status and prefix length (same address in all threads),
-  // and this wave's Q tile and ancestor masks.  The prefix length is not
-  // written during the launch, so every thread sees the same value; the
-  // status can be (another workgroup of the request may flag a bad block),
-  // so the workgroup agrees on it at its first barrier below.
+  // this wave's Q tile and ancestor masks, and the chunk's block ids.  The
+  // prefix length is not written during the launch, so every thread sees
+  // the same value; the status can be (another workgroup of the request may
+  // flag a bad block), so the workgroup agrees on it at a barrier below.
   const int N = a.N;
   const int st = a.status[b];
   const int L = a.prefix_len[b];
@@ -215,6 +215,30 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       qv[c] = as_bf16x8(*reinterpret_cast<const uint4*>(
           qg + ((static_cast<size_t>(b) * N + n_q) * a.H + h) * D + 32 * c + 8 * lg));
   }
+  // Block ids of every block the chunk can cover, before the prefix length
+  // is known (the table index is clamped to the table).  Ids outside
+  // [0, num_blocks) are stored as 0, so every K/V load stays in bounds; the
+  // ones that matter (blocks covering the chunk's keys) are reported below.
+  const int32_t* __restrict__ bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  const int k_begin = s * a.chunk;          // < max_blocks * 16 (the plan's last chunk starts inside)
+  const int blk_first = k_begin / TV_BLOCK;
+  const int nblk_max = min(a.chunk / TV_BLOCK + 1, a.max_blocks - blk_first);   // <= kMaxChunkBlocks
+  constexpr int kPer = (kMaxChunkBlocks + kAttnThreads - 1) / kAttnThreads;
+  int raw[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kAttnThreads;
+    raw[r] = i < nblk_max ? bt[blk_first + i] : 0;
+  }
+  // A wait the compiler can see: every load above is complete from here on,
+  // so it adds no wait of its own inside the stage loop, where a wait would
+  // also drain the stage loads in flight, which it does not know about.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kAttnThreads;
+    if (i < nblk_max) s_blk[i] = (raw[r] < 0 || raw[r] >= a.num_blocks) ? 0 : raw[r];
+  }
   if (L < 0 || static_cast<int64_t>(L) + N > static_cast<int64_t>(a.max_blocks) * TV_BLOCK) {
     // no workgroup of this request gets further, so no bad-block flag can race this
     if (threadIdx.x == 0 && st == TV_REQ_OK) a.status[b] = TV_REQ_KV_CAPACITY;
@@ -222,30 +246,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     return;
   }
   const int T = L + N;
-  const int k_begin = s * a.chunk;
   if (k_begin >= T) return;                 // empty chunk (never chunk 0): not counted by the merge
   const int k_end = min(T, k_begin + a.chunk);
   const int nst = (k_end - k_begin + SK - 1) / SK;                // stages of the chunk
   const int nloc = nst > grp ? (nst - grp + kGroups - 1) / kGroups : 0;   // this group's
+  const int nblk = (k_end - 1) / TV_BLOCK - blk_first + 1;        // blocks covering the chunk's keys
 
   const uint8_t* __restrict__ kg = static_cast<const uint8_t*>(a.kc);
   const uint8_t* __restrict__ vg = static_cast<const uint8_t*>(a.vc);
-  const int32_t* __restrict__ bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
   const size_t head_bytes = static_cast<size_t>(TV_BLOCK) * D * 2;
   const size_t blk_bytes = static_cast<size_t>(a.H) * head_bytes;
   const int last_blk = (T - 1) / TV_BLOCK, last_row = (T - 1) % TV_BLOCK;
 
-  // Block ids of the chunk, validated once and kept in LDS.
-  const int blk_first = k_begin / TV_BLOCK;
-  const int nblk = (k_end - 1) / TV_BLOCK - blk_first + 1;      // <= kMaxChunkBlocks
   int bad = 0;
-  for (int i = threadIdx.x; i < nblk; i += kAttnThreads) {
-    int blk = bt[blk_first + i];
-    if (blk < 0 || blk >= a.num_blocks) {
-      bad = 1;
-      blk = 0;
-    }
-    s_blk[i] = blk;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kAttnThreads;
+    if (i < nblk && (raw[r] < 0 || raw[r] >= a.num_blocks)) bad = 1;
   }
   if (threadIdx.x < kGroups) s_gbar[threadIdx.x] = 0;
   if (threadIdx.x == 0) s_hung = 0;
@@ -420,19 +437,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
-  // A wait the compiler can see: the Q and mask loads above are complete
-  // from here on (they went out first and have long arrived), so it adds
-  // no wait of its own inside the loop, where a wait would also drain the
-  // stage loads in flight, which it does not know about.
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
+  // The ring's buffers all start filling now.  In the loop, one barrier
+  // per stage: after it, the stage's loads have landed for every wave, and
+  // every wave has finished reading the buffer of the stage before, which is
+  // then refilled with the stage kRing - 1 further on, so that stage is in
+  // flight during this stage's compute.
   for (int r = 0; r < kRing && r < nloc; ++r) issue(grp + kGroups * r, gring + r * 2 * TILE);
   for (int it = 0; it < nloc; ++it) {
     uint8_t* cur = gring + (it % kRing) * 2 * TILE;
-    wait_stage(min(kRing - 1, nloc - 1 - it));
+    // stages issued so far: 0 .. min(nloc, it + kRing - 1) - 1 (it = 0: 0 .. kRing - 1)
+    const int issued = it == 0 ? min(kRing, nloc) : min(nloc, it + kRing - 1);
+    wait_stage(issued - 1 - it);
     group_barrier();
+    if (it >= 1 && it + kRing - 1 < nloc)
+      issue(grp + kGroups * (it + kRing - 1), gring + ((it + kRing - 1) % kRing) * 2 * TILE);
     if (computes) compute(grp + kGroups * it, cur);
-    group_barrier();
-    if (it + kRing < nloc) issue(grp + kGroups * (it + kRing), cur);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lrun += __shfl_xor(lrun, 16, 64);

@@ -164,15 +164,29 @@ __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-__device__ __forceinline__ double block_sum(double v, double* red) {
+// Sum of a double and OR of an int over the workgroup with one barrier.  The
+// per-wave partials go to one of two banks; callers alternate banks, so a
+// call never overwrites partials that a wave may still be reading from the
+// previous call (every wave has left that call before it can pass this
+// call's barrier).
+__device__ __forceinline__ double block_sum_or(double v, int f, double (*red)[kCoThreads / 64],
+                                               int (*redf)[kCoThreads / 64], int bank, int* f_out) {
   v = tv::wave_sum_dpp(v);
+  f = tv::wave_or_dpp(f);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
+  if (lane == 0) {
+    red[bank][wave] = v;
+    redf[bank][wave] = f;
+  }
   __syncthreads();
   double s = 0.0;
+  int o = 0;
 #pragma unroll
-  for (int w = 0; w < kCoThreads / 64; ++w) s += red[w];
+  for (int w = 0; w < kCoThreads / 64; ++w) {
+    s += red[bank][w];
+    o |= redf[bank][w];
+  }
+  *f_out = o;
   return s;
 }
 
@@ -180,8 +194,14 @@ __device__ __forceinline__ bool q_bad(float q) { return !(q >= 0.f) || q == INFI
 
 // ---------------------------------------------------------------------------
 // The walk kernel.  grid = (requests in this launch) * G, block = 256.
+//
+// Every wave of every workgroup of a request reads the same exchanged words
+// and makes the same decisions from them with the same operations, so the
+// walk state lives in registers and a pass needs no barrier beyond those of
+// its workgroup reductions.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
+  constexpr int NW = kCoThreads / 64;
   const int G = a.G;
   const int b = a.b0 + static_cast<int>(blockIdx.x) / G;
   const int g = static_cast<int>(blockIdx.x) % G;
@@ -200,18 +220,18 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
 
   __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES];
   __shared__ uint64_t s_child[TV_MAX_NODES + 1];
-  __shared__ float s_rx[TV_MAX_NODES], s_rx2[TV_MAX_NODES];
-  __shared__ double red[kCoThreads / 64];
-  __shared__ uint32_t s_hw[kMaxG][kHdr];   // header words of every workgroup, last exchange
-  __shared__ double s_tot[kMaxG];          // slice totals of the current distribution
-  __shared__ float s_wm[kCoThreads / 64];  // per-wave max / argmax / flags
-  __shared__ int s_wa[kCoThreads / 64], s_wf[kCoThreads / 64];
-  // walk state, written by thread 0 between passes
-  __shared__ int s_status, s_timeout, s_pass, s_u, s_j, s_k, s_rounds, s_mode, s_take, s_bonus;
-  __shared__ int s_owner, s_found, s_last;
-  __shared__ uint64_t s_U;
-  __shared__ float s_m;
-  __shared__ double s_Z, s_Tloc;
+  __shared__ double s_red[2][NW];
+  __shared__ int s_redf[2][NW];
+  __shared__ float s_wm[2][NW];                  // per-wave max / argmax / flags, two banks
+  __shared__ int s_wa[2][NW], s_wf[2][NW];
+  // gathered slice values, two banks by exchange parity (wave 0 writes them)
+  __shared__ float s_gm[2][kMaxG];
+  __shared__ double s_gs[2][kMaxG];
+  __shared__ int s_ga[2][kMaxG];
+  __shared__ float s_rx2[2][TV_MAX_NODES];
+  __shared__ double s_gt[NW][kMaxG];             // slice totals of the current distribution (per wave)
+  __shared__ double s_scan[NW];
+  __shared__ int s_status0, s_timeout, s_found, s_last;
   __shared__ float own_s[kElem];
 
   auto load8 = [&](const float* row, float (&dst)[kElem]) {
@@ -249,51 +269,59 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         if (bad_tok & real) st = TV_REQ_BAD_TOKEN;
         else if (bad_q & real) st = TV_REQ_BAD_QROW;
       }
-      s_status = st;
+      s_status0 = st;
       s_timeout = 0;
-      s_pass = P_ENTER;
-      s_u = -1;
-      s_U = cm;            // children of the root
-      s_j = 0;
-      s_k = 0;
-      s_rounds = 0;
-      s_mode = 0;
-      s_take = 0;
-      s_bonus = -1;
-      s_owner = -1;
     }
   }
   __syncthreads();
 
-  float cv[kElem], rn[kElem];   // residual in use / residual of the last pass
+  // ---- walk state: registers, identical in every thread of the request ----
+  int status = s_status0;
+  int pass = P_ENTER, u = -1, j = 0, k = 0, rounds = 0, mode = 0, bonus = -1;
+  uint64_t U = s_child[0];
+  float m = 0.f;           // max of the current node's row
+  double Z = 1.0;          // normaliser of the current distribution
+  float rx = 0.f;          // lane c: the residual at child c's token (mode 1)
+  int owner = -1;          // final sample: the slice holding the threshold
+  double Tloc = 0.0;       //   and the threshold inside it
+  bool timed_out = false;  // wave-uniform
+
+  float cv[kElem], rn[kElem];   // residual in use / residual of this pass
   float qv[kElem], qn[kElem];   // draft row of the rejected child / of the next candidate
   float lvn[kElem];             // logits row of the next candidate
 #pragma unroll
-  for (int k = 0; k < kElem; ++k) cv[k] = rn[k] = qv[k] = qn[k] = lvn[k] = 0.f;
+  for (int e = 0; e < kElem; ++e) cv[e] = rn[e] = qv[e] = qn[e] = lvn[e] = 0.f;
 
-  int ex_no = 0;                // exchanges done (identical in every workgroup)
+  int ex_no = 0;                // exchanges done
+  int rs_no = 0;                // workgroup sums done (bank parity)
+  int pre = 0;                  // greedy: the entered node's row is in lvn (1), qn (2), or not loaded (0)
   for (;;) {
-    // ---- pass state (read before the pass's first barrier) ----
-    const int pass = s_pass;
-    if (pass >= P_FINAL || s_status != TV_REQ_OK || s_timeout) break;
-    const int u = s_u;
-    const uint64_t U = s_U;
-    const int j = s_j;
-    if (s_take) {
-#pragma unroll
-      for (int k = 0; k < kElem; ++k) cv[k] = rn[k];
-    }
+    if (status != TV_REQ_OK || pass >= P_FINAL || timed_out) break;
     if (pass == P_RESID) {
 #pragma unroll
-      for (int k = 0; k < kElem; ++k) qv[k] = qn[k];
+      for (int e = 0; e < kElem; ++e) qv[e] = qn[e];
     }
     const float* lrow = lbase + static_cast<size_t>(u + 1) * V;
     if (pass == P_ENTER && u >= 0) {
-      if (mss) {
+      if (mss || pre == 1) {
 #pragma unroll
-        for (int k = 0; k < kElem; ++k) lv[k] = lvn[k];
+        for (int e = 0; e < kElem; ++e) lv[e] = lvn[e];
+      } else if (pre == 2) {
+#pragma unroll
+        for (int e = 0; e < kElem; ++e) lv[e] = qn[e];
       } else {
         load8(lrow, lv);
+      }
+    }
+    // greedy: the rows of the first two children, in case the walk enters one
+    int c1 = -1, c2 = -1;
+    if (!mss && pass == P_ENTER && U) {
+      c1 = __builtin_ctzll(U);
+      load8(lbase + static_cast<size_t>(c1 + 1) * V, lvn);
+      const uint64_t rest = U & (U - 1);
+      if (rest) {
+        c2 = __builtin_ctzll(rest);
+        load8(lbase + static_cast<size_t>(c2 + 1) * V, qn);
       }
     }
     // the child tested after this pass, and its rows (loads in flight during the pass)
@@ -306,58 +334,54 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       const float* qrow_c = sbase + static_cast<size_t>(s_qrow[cand]) * V;
       load8(qrow_c, qn);
       load8(lbase + static_cast<size_t>(cand + 1) * V, lvn);
-      if (t == 0) {
-        lx_c = lrow[s_tok[cand]];
-        qx_c = qrow_c[s_tok[cand]];
-      }
+      lx_c = lrow[s_tok[cand]];
+      qx_c = qrow_c[s_tok[cand]];
     }
     const uint32_t tag = static_cast<uint32_t>(ex_no + 1);
     const int par = ex_no & 1;
     uint64_t* bank = hdr + static_cast<size_t>(par) * G * kHdr;
-    int nread = 0;
 
     if (pass == P_ENTER) {
       // ---- statistics of u's row over this slice ----
       float mx = -INFINITY;
       int arg = 0x7FFFFFFF, flags = 0;
 #pragma unroll
-      for (int k = 0; k < kElem; ++k) {
-        if (k < nx) {
-          const float f = lv[k];
+      for (int e = 0; e < kElem; ++e) {
+        if (e < nx) {
+          const float f = lv[e];
           if (f != f) flags |= FLAG_NAN;
           else if (f == INFINITY) flags |= FLAG_PINF;
           else if (f != -INFINITY) flags |= FLAG_FINITE;
           if (f > mx || (f == mx && arg == 0x7FFFFFFF)) {   // first index of the max
             mx = f;
-            arg = xa + k;
+            arg = xa + e;
           }
         }
       }
       tv::wave_argmax_dpp(mx, arg);
       flags = tv::wave_or_dpp(flags);
       if (lane == 0) {
-        s_wm[wave] = mx;
-        s_wa[wave] = arg;
-        s_wf[wave] = flags;
+        s_wm[par][wave] = mx;
+        s_wa[par][wave] = arg;
+        s_wf[par][wave] = flags;
       }
       __syncthreads();
-      float M = s_wm[0];
-      int A = s_wa[0], F = s_wf[0];
+      float M = s_wm[par][0];
+      int A = s_wa[par][0], F = s_wf[par][0];
 #pragma unroll
-      for (int w2 = 1; w2 < kCoThreads / 64; ++w2) {
-        if (s_wm[w2] > M || (s_wm[w2] == M && s_wa[w2] < A)) {
-          M = s_wm[w2];
-          A = s_wa[w2];
-        }
-        F |= s_wf[w2];
+      for (int w2 = 1; w2 < NW; ++w2) {
+        tv::argmax_merge(M, A, s_wm[par][w2], s_wa[par][w2]);
+        F |= s_wf[par][w2];
       }
       double S = 0.0;
       if (mss && M != -INFINITY && M == M && M != INFINITY) {
         double acc = 0.0;
 #pragma unroll
-        for (int k = 0; k < kElem; ++k)
-          if (k < nx && lv[k] != -INFINITY) acc += static_cast<double>(tv::exp_acc(lv[k] - M));
-        S = block_sum(acc, red);
+        for (int e = 0; e < kElem; ++e)
+          if (e < nx && lv[e] != -INFINITY) acc += static_cast<double>(tv::exp_acc(lv[e] - M));
+        int unused;
+        S = block_sum_or(acc, 0, s_red, s_redf, rs_no & 1, &unused);
+        ++rs_no;
       }
       // slice argmax < 2^20, flags in bits 24..26
       if (t == 0) {
@@ -367,31 +391,24 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         put_tagged(p + 2, tag, hi32(S));
         put_tagged(p + 3, tag, static_cast<uint32_t>(A) | (static_cast<uint32_t>(F) << 24));
       }
-      nread = 4;
     } else {
       // ---- residual after rejecting the child whose draft row is in qv ----
-      const int md = s_mode;
-      const float mm = s_m;
-      const double ZZ = s_Z;
       double acc = 0.0;
       int bad = 0;
 #pragma unroll
-      for (int k = 0; k < kElem; ++k) {
-        if (k < nx) {
-          const float c = md == 0 ? (lv[k] == -INFINITY ? 0.f : tv::exp_acc(lv[k] - mm)) : cv[k];
-          if (q_bad(qv[k])) bad = 1;
-          rn[k] = static_cast<float>(fmax(0.0, static_cast<double>(c) - ZZ * static_cast<double>(qv[k])));
-          acc += static_cast<double>(rn[k]);
+      for (int e = 0; e < kElem; ++e) {
+        if (e < nx) {
+          const float c = mode == 0 ? (lv[e] == -INFINITY ? 0.f : tv::exp_acc(lv[e] - m)) : cv[e];
+          if (q_bad(qv[e])) bad = 1;
+          rn[e] = static_cast<float>(fmax(0.0, static_cast<double>(c) - Z * static_cast<double>(qv[e])));
+          acc += static_cast<double>(rn[e]);
         } else {
-          rn[k] = 0.f;
+          rn[e] = 0.f;
         }
       }
-      bad = __any(bad) ? 1 : 0;
-      if (lane == 0) s_wf[wave] = bad;
-      const double Zg = block_sum(acc, red);     // its barriers publish s_wf
-      int anyb = 0;
-#pragma unroll
-      for (int w2 = 0; w2 < kCoThreads / 64; ++w2) anyb |= s_wf[w2];
+      int anyb;
+      const double Zg = block_sum_or(acc, bad, s_red, s_redf, rs_no & 1, &anyb);
+      ++rs_no;
       // the new residual at the remaining children's tokens: the owner of
       // each child's token publishes it
       {
@@ -403,7 +420,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
           if (x >= xa && x < xa + nx) {
             float v = 0.f;
 #pragma unroll
-            for (int k = 0; k < kElem; ++k) v = (xa + k == x) ? rn[k] : v;
+            for (int e = 0; e < kElem; ++e) v = (xa + e == x) ? rn[e] : v;
             put_tagged(kid + par * 64 + c, tag, __float_as_uint(v));
           }
         }
@@ -414,212 +431,205 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         put_tagged(p + 1, tag, hi32(Zg));
         put_tagged(p + 2, tag, static_cast<uint32_t>(anyb));
       }
-      nread = 3;
-      if (t < N && ((U >> t) & 1ull)) {
-        uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
-        if (!take_tagged<1>(kid + par * 64 + t, tag, v)) s_timeout = 1;
-        s_rx2[t] = __uint_as_float(v[0]);
-      }
     }
-    // ---- gather every workgroup's header words ----
-    for (int gg = t; gg < G; gg += kCoThreads) {
-      uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
-      const bool ok = nread == 4 ? take_tagged<4>(bank + static_cast<size_t>(gg) * kHdr, tag, v)
-                                 : take_tagged<3>(bank + static_cast<size_t>(gg) * kHdr, tag, v);
-      if (!ok) s_timeout = 1;
-#pragma unroll
-      for (int i = 0; i < kHdr; ++i) s_hw[gg][i] = v[i];
+
+    // ---- wave 0 gathers every workgroup's words into LDS ----
+    // (A wave reads a bank only between this exchange's barrier and the next
+    // pass's first barrier, and wave 0 refills the bank two exchanges later,
+    // after that barrier.)
+    if (wave == 0) {
+      bool to = false;
+      if (pass == P_RESID && lane < N && ((U >> lane) & 1ull)) {
+        uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
+        if (!take_tagged<1>(kid + par * 64 + lane, tag, v)) to = true;
+        s_rx2[par][lane] = __uint_as_float(v[0]);
+      }
+      for (int gg = lane; gg < G; gg += 64) {
+        uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
+        const bool okp = pass == P_ENTER ? take_tagged<4>(bank + static_cast<size_t>(gg) * kHdr, tag, v)
+                                         : take_tagged<3>(bank + static_cast<size_t>(gg) * kHdr, tag, v);
+        if (!okp) to = true;
+        if (pass == P_ENTER) {
+          s_gm[par][gg] = __uint_as_float(v[0]);
+          s_gs[par][gg] = join64(v[1], v[2]);
+          s_ga[par][gg] = static_cast<int>(v[3]);
+        } else {
+          s_gs[par][gg] = join64(v[0], v[1]);
+          s_ga[par][gg] = static_cast<int>(v[2]);
+        }
+      }
+      if (__any(to) && lane == 0) s_timeout = 1;
     }
     __syncthreads();
     ++ex_no;
+    if (s_timeout) {
+      timed_out = true;
+      break;
+    }
 
-    // ---- merge the slices (wave 0, in parallel) and decide (thread 0) ----
-    if (wave == 0) {
-      int next_pass = P_DONE;
-      float m_now = s_m;
-      double Z_now = s_Z;
-      int md_now = s_mode;
-      int take = 0;
-      bool fail = false;
-      if (pass == P_ENTER) {
-        // max with the lowest index on ties, flags, then the normaliser
-        float m = -INFINITY;
-        int am = 0x7FFFFFFF, fl = 0;
-        for (int gg = lane; gg < G; gg += 64) {
-          const float mg = __uint_as_float(s_hw[gg][0]);
-          const int ag = static_cast<int>(s_hw[gg][3] & 0xFFFFFFu);
-          fl |= static_cast<int>(s_hw[gg][3] >> 24);
-          if (mg > m || (mg == m && ag < am)) {
-            m = mg;
-            am = ag;
-          }
+    // ---- merge the slices and decide (every wave, same values) ----
+    bool fail = false;
+    if (pass == P_ENTER) {
+      // max with the lowest index on ties, flags, then the normaliser
+      float mm = -INFINITY;
+      int am = 0x7FFFFFFF, fl = 0;
+      for (int gg = lane; gg < G; gg += 64) {
+        fl |= static_cast<int>(static_cast<uint32_t>(s_ga[par][gg]) >> 24);
+        tv::argmax_merge(mm, am, s_gm[par][gg], s_ga[par][gg] & 0xFFFFFF);
+      }
+      tv::wave_argmax_dpp(mm, am);
+      fl = tv::wave_or_dpp(fl);
+      fail = (fl & (FLAG_NAN | FLAG_PINF)) || !(fl & FLAG_FINITE);
+      if (!fail && !mss) {
+        // greedy: the child whose token is the argmax, lowest node first
+        const uint64_t hit = __ballot(lane < N && ((U >> lane) & 1ull) && s_tok[lane] == am);
+        if (hit) {
+          const int nxt = __builtin_ctzll(hit);
+          if (t == 0) s_acc[k] = nxt;
+          ++k;
+          u = nxt;
+          U = s_child[nxt + 1];
+          pre = nxt == c1 ? 1 : (nxt == c2 ? 2 : 0);
+          pass = P_ENTER;
+        } else {
+          bonus = am;
+          pass = P_DONE;
         }
-        tv::wave_argmax_dpp(m, am);
-        fl = tv::wave_or_dpp(fl);
-        fail = (fl & (FLAG_NAN | FLAG_PINF)) || !(fl & FLAG_FINITE);
-        if (!fail && !mss) {
-          // greedy: the child whose token is the argmax, lowest node first
-          const uint64_t hit = __ballot(lane < N && ((U >> lane) & 1ull) && s_tok[lane] == am);
-          if (lane == 0) {
-            if (hit) {
-              const int nxt = __builtin_ctzll(hit);
-              s_acc[s_k++] = nxt;
-              s_u = nxt;
-              s_U = s_child[nxt + 1];
-              next_pass = P_ENTER;
-            } else {
-              s_bonus = am;
-              next_pass = P_DONE;
-            }
+      } else if (!fail) {
+        double part = 0.0;
+        for (int gg = lane; gg < G; gg += 64) {
+          const float mg = s_gm[par][gg];
+          const double tg = mg == -INFINITY ? 0.0 : s_gs[par][gg] * static_cast<double>(tv::exp_acc(mg - mm));
+          s_gt[wave][gg] = tg;
+          part += tg;
+        }
+        Z = tv::wave_sum_dpp(part);
+        m = mm;
+        mode = 0;
+      }
+    } else {
+      double part = 0.0;
+      int ab = 0;
+      for (int gg = lane; gg < G; gg += 64) {
+        part += s_gs[par][gg];
+        ab |= s_ga[par][gg];
+      }
+      const double Znew = tv::wave_sum_dpp(part);
+      fail = tv::wave_or_dpp(ab) != 0;
+      if (!fail && Znew > 0.0) {       // else the distribution stays (zero-normaliser guard)
+        for (int gg = lane; gg < G; gg += 64) s_gt[wave][gg] = s_gs[par][gg];
+        if (lane < N && ((U >> lane) & 1ull)) rx = s_rx2[par][lane];
+#pragma unroll
+        for (int e = 0; e < kElem; ++e) cv[e] = rn[e];
+        Z = Znew;
+        mode = 1;
+      }
+    }
+    if (fail) {
+      status = TV_REQ_NONFINITE;
+    } else if (mss) {
+      if (cand >= 0) {
+        // ratio test: u1 <= p(x) / q(x) with p(x) = e / Z, tested as
+        // u1 * q(x) * Z <= e (no division); q(x) = 0 accepts exactly when p(x) > 0
+        if (q_bad(qx_c)) {
+          status = TV_REQ_NONFINITE;
+        } else {
+          const double e = mode == 0 ? (lx_c == -INFINITY ? 0.0 : static_cast<double>(tv::exp_acc(lx_c - m)))
+                                     : static_cast<double>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(rx), cand)));
+          const bool accept = qx_c > 0.f ? tv::unit_open0(w.y) * static_cast<double>(qx_c) * Z <= e : e > 0.0;
+          ++rounds;
+          if (accept) {
+            if (t == 0) s_acc[k] = cand;
+            ++k;
+            u = cand;
+            U = s_child[cand + 1];
+            j = 0;
+            pass = P_ENTER;
+          } else {
+            U &= ~(1ull << cand);
+            ++j;
+            pass = P_RESID;
           }
-        } else if (!fail) {
-          double part = 0.0;
-          for (int gg = lane; gg < G; gg += 64) {
-            const float mg = __uint_as_float(s_hw[gg][0]);
-            const double tg = mg == -INFINITY ? 0.0
-                              : join64(s_hw[gg][1], s_hw[gg][2]) * static_cast<double>(tv::exp_acc(mg - m));
-            s_tot[gg] = tg;
-            part += tg;
-          }
-          Z_now = tv::wave_sum_dpp(part);
-          m_now = m;
-          md_now = 0;
         }
       } else {
-        double part = 0.0;
-        int anyb = 0;
-        for (int gg = lane; gg < G; gg += 64) {
-          part += join64(s_hw[gg][0], s_hw[gg][1]);
-          anyb |= static_cast<int>(s_hw[gg][2]);
+        // no child left: the slice holding u2 * total, from the slice
+        // totals in index order, and the threshold inside it
+        const tv::u32x4 w0 = tv::mss_words(a.seed, a.offset, b, u + 1, 0);
+        double run = 0.0;
+        for (int base = 0; base < G; base += 64) {     // the same sums as the search below
+          const double v = base + lane < G ? s_gt[wave][base + lane] : 0.0;
+          double ex;
+          run = tv::readlane_f64(run + tv::wave_scan_dpp(v, &ex), 63);
         }
-        const double Znew = tv::wave_sum_dpp(part);
-        fail = tv::wave_or_dpp(anyb) != 0;
-        take = !fail && Znew > 0.0;
-        if (take) {           // else the distribution stays (zero-normaliser guard)
-          for (int gg = lane; gg < G; gg += 64) s_tot[gg] = join64(s_hw[gg][0], s_hw[gg][1]);
-          if (lane < N && ((U >> lane) & 1ull)) s_rx[lane] = s_rx2[lane];
-          Z_now = Znew;
-          md_now = 1;
+        const double T = tv::unit_open0(w0.z) * run;
+        double carry = 0.0, ex_owner = 0.0, ex_last = 0.0;
+        int last = -1;
+        owner = -1;
+        for (int base = 0; base < G && owner < 0; base += 64) {
+          const double v = base + lane < G ? s_gt[wave][base + lane] : 0.0;
+          double excl;
+          const double incl = carry + tv::wave_scan_dpp(v, &excl);
+          excl += carry;
+          const uint64_t hit = __ballot(v > 0.0 && excl < T && incl >= T);
+          const uint64_t pos = __ballot(v > 0.0);
+          if (hit) {
+            const int l = __builtin_ctzll(hit);
+            owner = base + l;
+            ex_owner = tv::readlane_f64(excl, l);
+          } else if (pos) {
+            const int l = 63 - __builtin_clzll(pos);
+            last = base + l;
+            ex_last = tv::readlane_f64(excl, l);
+          }
+          carry = tv::readlane_f64(incl, 63);
         }
-      }
-      if (mss && !fail) {
-        // ratio test of the candidate (thread 0), or the final sample's slice
-        if (cand >= 0) {
-          if (lane == 0) {
-            if (q_bad(qx_c)) {
-              fail = true;
-            } else {
-              // u1 <= p(x) / q(x) with p(x) = e / Z, tested as u1 * q(x) * Z <= e
-              // (no division); q(x) = 0 accepts exactly when p(x) > 0
-              const double e = md_now == 0 ? (lx_c == -INFINITY ? 0.0 : static_cast<double>(tv::exp_acc(lx_c - m_now)))
-                                           : static_cast<double>(s_rx[cand]);
-              const bool accept = qx_c > 0.f ? tv::unit_open0(w.y) * static_cast<double>(qx_c) * Z_now <= e : e > 0.0;
-              ++s_rounds;
-              if (accept) {
-                s_acc[s_k++] = cand;
-                s_u = cand;
-                s_U = s_child[cand + 1];
-                s_j = 0;
-                next_pass = P_ENTER;
-              } else {
-                s_U = U & ~(1ull << cand);
-                s_j = j + 1;
-                next_pass = P_RESID;
-              }
-            }
-          }
-        } else {
-          // no child left: the slice holding u2 * total, from the slice
-          // totals in index order; the threshold inside it
-          const tv::u32x4 w0 = tv::mss_words(a.seed, a.offset, b, u + 1, 0);
-          double run = 0.0;
-          for (int base = 0; base < G; base += 64) {     // the same sums as the search below
-            const double v = base + lane < G ? s_tot[base + lane] : 0.0;
-            double ex;
-            run = tv::readlane_f64(run + tv::wave_scan_dpp(v, &ex), 63);
-          }
-          const double T = tv::unit_open0(w0.z) * run;
-          double carry = 0.0;
-          int owner = -1, last = -1;
-          double ex_owner = 0.0, ex_last = 0.0;
-          for (int base = 0; base < G && owner < 0; base += 64) {
-            const double v = base + lane < G ? s_tot[base + lane] : 0.0;
-            double excl;
-            const double incl = carry + tv::wave_scan_dpp(v, &excl);
-            excl += carry;
-            const uint64_t hit = __ballot(v > 0.0 && excl < T && incl >= T);
-            const uint64_t pos = __ballot(v > 0.0);
-            if (hit) {
-              const int l = __builtin_ctzll(hit);
-              owner = base + l;
-              ex_owner = tv::readlane_f64(excl, l);
-            } else if (pos) {
-              const int l = 63 - __builtin_clzll(pos);
-              last = base + l;
-              ex_last = tv::readlane_f64(excl, l);
-            }
-            carry = tv::readlane_f64(incl, 63);
-          }
-          if (lane == 0) {
-            s_owner = owner;
-            s_Tloc = fmax(T - ex_owner, 1e-300);
-          }
-          next_pass = P_FINAL;
+        if (owner < 0) {       // rounding left the total short: last non-empty slice
+          owner = last;
+          ex_owner = ex_last;
         }
-      }
-      if (lane == 0) {
-        if (fail) s_status = TV_REQ_NONFINITE;
-        s_pass = next_pass;
-        s_take = take;
-        s_m = m_now;
-        s_Z = Z_now;
-        s_mode = md_now;
+        Tloc = fmax(T - ex_owner, 1e-300);
+        pass = P_FINAL;
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
+  const bool ok = status == TV_REQ_OK && !s_timeout;
 
   // ---- final sample: the owner slice's workgroup finds the token ----
-  if (s_pass == P_FINAL && s_status == TV_REQ_OK && !s_timeout && g == s_owner) {
-    if (s_take) {
-#pragma unroll
-      for (int k = 0; k < kElem; ++k) cv[k] = rn[k];
-    }
-    const int md = s_mode;
-    const float mm = s_m;
+  if (ok && pass == P_FINAL && g == owner) {
     float cur[kElem];
     double part = 0.0;
 #pragma unroll
-    for (int k = 0; k < kElem; ++k) {
-      cur[k] = k < nx ? (md == 0 ? (lv[k] == -INFINITY ? 0.f : tv::exp_acc(lv[k] - mm)) : cv[k]) : 0.f;
-      part += static_cast<double>(cur[k]);
+    for (int e = 0; e < kElem; ++e) {
+      cur[e] = e < nx ? (mode == 0 ? (lv[e] == -INFINITY ? 0.f : tv::exp_acc(lv[e] - m)) : cv[e]) : 0.f;
+      part += static_cast<double>(cur[e]);
     }
     double wexcl;
     const double wincl = tv::wave_scan_dpp(part, &wexcl);
-    if (lane == 63) red[wave] = wincl;
+    if (lane == 63) s_scan[wave] = wincl;
     if (t == 0) s_found = -1;
     __syncthreads();
     double wbase = 0.0, total = 0.0;
 #pragma unroll
-    for (int w2 = 0; w2 < kCoThreads / 64; ++w2) {
-      if (w2 < wave) wbase += red[w2];
-      total += red[w2];
+    for (int w2 = 0; w2 < NW; ++w2) {
+      if (w2 < wave) wbase += s_scan[w2];
+      total += s_scan[w2];
     }
     const double incl = wbase + wincl;
     const double excl = wbase + wexcl;     // the previous thread's incl, bit for bit (wexcl = 0 in lane 0)
     // threshold in (0, slice total]: exactly one thread has excl < T <= incl
-    const double T = fmin(s_Tloc, total);
+    const double T = fmin(Tloc, total);
     if (excl < T && incl >= T) {
 #pragma unroll
-      for (int k = 0; k < kElem; ++k) own_s[k] = cur[k];
+      for (int e = 0; e < kElem; ++e) own_s[e] = cur[e];
       double accd = excl;
       int xs = -1, last_pos = -1;
-      for (int k = 0; k < nx; ++k) {
-        const float c = own_s[k];
-        if (c > 0.f) last_pos = xa + k;
+      for (int e = 0; e < nx; ++e) {
+        const float c = own_s[e];
+        if (c > 0.f) last_pos = xa + e;
         accd += static_cast<double>(c);
         if (accd >= T) {
-          xs = xa + k;
+          xs = xa + e;
           break;
         }
       }
@@ -631,9 +641,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
 
   // ---- results: workgroup 0 writes the path (and the greedy bonus) ----
   if (g == 0) {
-    const bool ok = s_status == TV_REQ_OK && !s_timeout;
     if (t == 0) {
-      int stt = s_status;
+      int stt = status;
       if (stt == TV_REQ_OK && s_timeout) stt = TV_REQ_TIMEOUT;
       if (stt != TV_REQ_OK) {
         a.status[b] = stt;
@@ -641,13 +650,13 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         a.bonus[b] = -1;
         if (a.rounds) a.rounds[b] = -1;
       } else {
-        a.num_accepted[b] = s_k;
-        if (!mss || s_owner < 0) a.bonus[b] = s_bonus;   // MSS: the owner slice writes it
-        if (a.rounds) a.rounds[b] = s_rounds;
+        a.num_accepted[b] = k;
+        if (!mss || owner < 0) a.bonus[b] = bonus;   // MSS: the owner slice writes it
+        if (a.rounds) a.rounds[b] = rounds;
       }
     }
-    const int k = ok ? s_k : 0;
-    for (int i = t; i < N; i += kCoThreads) a.accepted[static_cast<size_t>(b) * N + i] = i < k ? s_acc[i] : -1;
+    const int kk = ok ? k : 0;
+    for (int i = t; i < N; i += kCoThreads) a.accepted[static_cast<size_t>(b) * N + i] = i < kk ? s_acc[i] : -1;
   }
 
   // ---- leave the workspace zeroed: the last workgroup out clears it ----
