@@ -148,21 +148,23 @@ __device__ __forceinline__ int tile_off(int r, int c16) {   // byte offset
   return r * (2 * D) + swz<D>(r, c16) * 16;
 }
 
-// One workgroup per (request b, head h, key chunk s), made of NG groups of 4
+// One workgroup per (request b, head h, key chunk s), made of kGroups groups of 4
 // waves.  The chunk is cut into stages of 32 keys; group g takes stages
-// g, g + NG, g + 2 NG, ... and runs as if it were a workgroup of its own: a
+// g, g + kGroups, g + 2 kGroups, ... and runs as if it were a workgroup of its own: a
 // two-buffer ring of K/V stages filled HBM -> LDS with direct-to-LDS loads
 // (no registers), one stage in flight while the other is read, and its own
 // barrier (an LDS counter), so the groups drift independently and one
-// group's loads overlap another's matrix work.  Waves 0..NQT-1 of a group
-// each own one 16-query tile of the tree.  Per 32 keys and query tile:
+// group's loads overlap another's matrix work.  NQT waves of a group each own
+// one 16-query tile of the tree; every LDS read of a stage is issued before
+// its products, so the reads' latency hides behind them.  Per 32 keys and
+// query tile:
 //   S^T[key][query] = K . Q^T     (A = K rows from LDS, B = Q^T in registers)
 //   O^T[dim][query] += V^T . P^T  (A = V^T via LDS transpose reads,
 //                                  B = P^T straight from the S^T accumulator)
 // At the end the groups' softmax states are merged through LDS; with several
 // chunks per (b, h) the merged state is written as an unnormalised partial
 // that attn_merge_kernel combines.
-constexpr int kGroups = 4;                  // 4-wave groups per workgroup
+constexpr int kGroups = 3;                  // 4-wave groups per workgroup
 constexpr int kRing = 2;                    // stage buffers per group
 constexpr int kGroupThreads = 256;
 constexpr int kAttnThreads = kGroups * kGroupThreads;
@@ -202,8 +204,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   const int st = a.status[b];
   const int L = a.prefix_len[b];
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
-  const bool computes = gw < NQT;
-  const int n_q = 16 * gw + lr;
+  // Query tile of this wave.  Wave gw of a group runs on SIMD gw, so the
+  // tile index is rotated by the group: with fewer tiles than waves, the
+  // idle waves of different groups sit on different SIMDs and every SIMD
+  // carries the same matrix work.
+  const int qt = (gw - grp) & 3;
+  const bool computes = qt < NQT;
+  const int n_q = 16 * qt + lr;
   bf16x8 qv[KC];
   uint64_t ancq = 0;
 #pragma unroll
@@ -313,17 +320,39 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     const int t0 = k_begin + SK * st;
     const uint8_t* kt_base = cur;
     const uint8_t* vt_base = cur + TILE;
+    // ---- every LDS read of the stage goes out first: K rows, then the V^T
+    // operands (two transpose reads per 16-dim tile: lane s of group lg
+    // supplies row 16*half + 4lg + s/4, dims 16dt + 4(s%4) .. +3; lane j then
+    // holds those 4 rows at dim 16dt + j), so the V latency hides behind the
+    // score products and the softmax ----
+    bf16x8 kop[2][KC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        kop[kt][c] = as_bf16x8(*reinterpret_cast<const uint4*>(kt_base + tile_off<D>(16 * kt + lr, 4 * c + lg)));
+    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+    s16x8 vop[DT];
+    {
+      const int vrow0 = 4 * lg + (lr >> 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d0 = 16 * dt + 4 * (lr & 3);
+        const int c16 = d0 >> 3, within = (d0 & 7) * 2;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0, c16) + within));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0 + 16, c16) + within));
+        vop[dt] = s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      }
+    }
     // ---- scores S^T for the stage's 32 keys ----
     f32x4 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int r = 16 * kt + lr;
       f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(kt_base + tile_off<D>(r, 4 * c + lg)));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[c], acc, 0, 0, 0);
-      }
+      for (int c = 0; c < KC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kt][c], qv[c], acc, 0, 0, 0);
       sc[kt] = acc;
     }
     // scale and mask: a stage of prefix keys only (all but the last one or
@@ -382,22 +411,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
         lrun += __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
       }
     const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    // ---- O^T += V^T P^T: V^T operand from two LDS transpose reads ----
-    // lane s of group lg supplies row 16*half + 4lg + s/4, dims
-    // 16dt + 4(s%4) .. +3; lane j then holds those 4 rows at dim 16dt + j
-    const int vrow0 = 4 * lg + (lr >> 2);
+    // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d0 = 16 * dt + 4 * (lr & 3);
-      const int c16 = d0 >> 3, within = (d0 & 7) * 2;
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0, c16) + within));
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vt_base + tile_off<D>(vrow0 + 16, c16) + within));
-      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-      const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < DT; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]), pb, o[dt], 0, 0, 0);
   };
 
   // ---- the group's pipeline: kRing stage buffers, kRing - 1 stages in flight ----
@@ -463,7 +480,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   // writes and reads only its own column, so there are no bank conflicts.
   float* mg = reinterpret_cast<float*>(ring);
   if (grp > 0 && computes) {
-    float* dst = mg + ((grp - 1) * NQT + gw) * SLOT + lane;
+    float* dst = mg + ((grp - 1) * NQT + qt) * SLOT + lane;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -480,7 +497,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   lo_[0] = lrun;
 #pragma unroll
   for (int g2 = 1; g2 < kGroups; ++g2) {
-    const float* src = mg + ((g2 - 1) * NQT + gw) * SLOT + lane;
+    const float* src = mg + ((g2 - 1) * NQT + qt) * SLOT + lane;
     mo[g2] = src[(DT * 4) * 64];
     lo_[g2] = src[(DT * 4 + 1) * 64];
   }
@@ -501,7 +518,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     for (int i = 0; i < 4; ++i) {
       float acc = wgt[0] * o[dt][i];
 #pragma unroll
-      for (int g2 = 1; g2 < kGroups; ++g2) acc += wgt[g2] * mg[((g2 - 1) * NQT + gw) * SLOT + (dt * 4 + i) * 64 + lane];
+      for (int g2 = 1; g2 < kGroups; ++g2) acc += wgt[g2] * mg[((g2 - 1) * NQT + qt) * SLOT + (dt * 4 + i) * 64 + lane];
       o[dt][i] = acc;
     }
 
