@@ -299,10 +299,44 @@ def test_empty_tree_verify():
     _check_mss(run, "empty tree")
 
 
-def test_verify_workspace_reuse():
-    # several workgroups per request (V = 5003: 3 slices, ragged tail, scalar
-    # loads); one workspace for every call, left all zero after each
-    w = _small("c3_small")
+@pytest.mark.parametrize("V", [8, 2048, 4097, 8193, 12000, 16384])
+def test_verify_row_vocab(V):
+    # vocabularies up to 16384 entries: one workgroup per request, 8, 16 or 32
+    # registers per row per thread; 4097 and 8193 take scalar loads
+    for cfg, kw in ((2, dict(B=3, L=20, H=1)), (4, dict(B=2, H=1))):
+        w = synth.make_workload(cfg, V=V, **kw)
+        _print_case("verify row", cfg, V)
+        run = GpuRun(w).mask().greedy()
+        torch.cuda.synchronize()
+        _check_greedy(run)
+        run = GpuRun(w).mask().mss()
+        torch.cuda.synchronize()
+        _check_mss(run, f"row cfg{cfg} V={V}")
+
+
+@pytest.mark.parametrize("V", [16385, 40000, 33001, 70001])
+def test_verify_sliced_vocab(V):
+    # vocabularies above 16384 entries take the kernel that splits a row over
+    # several workgroups (2048 entries each); 16385, 33001 and 70001 have
+    # ragged tails and take scalar loads
+    for cfg, kw in ((2, dict(B=3, L=20, H=1)), (4, dict(B=2, H=1))):
+        w = synth.make_workload(cfg, V=V, **kw)
+        _print_case("verify sliced", cfg, V)
+        run = GpuRun(w).mask().greedy()
+        torch.cuda.synchronize()
+        _check_greedy(run)
+        run = GpuRun(w).mask().mss()
+        torch.cuda.synchronize()
+        _check_mss(run, f"sliced cfg{cfg} V={V}")
+        assert int(run.ws_v.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("V", [5003, 40003])
+def test_verify_workspace_reuse(V):
+    # one workspace for every call, left all zero after each; V = 5003 takes
+    # one workgroup per request (ragged tail, scalar loads), V = 40003 splits
+    # rows over 20 workgroups that exchange through the workspace
+    w = synth.make_workload(3, B=3, L=77, H=3, V=V)
     run = GpuRun(w).mask()
     outs = []
     for rep in range(3):
@@ -318,10 +352,12 @@ def test_verify_workspace_reuse():
     _check_mss(run, "workspace reuse")
 
 
-def test_verify_many_requests():
-    # more requests than one cooperative launch holds: 20000-entry vocabulary
-    # (10 workgroups per request), 200 requests, a 7-node tree
-    w = synth.make_workload(dict(name="many", B=200, H=1, D=64, L=3, V=20000, dtype="f32",
+@pytest.mark.parametrize("V", [12000, 40000])
+def test_verify_many_requests(V):
+    # 200 requests with a 7-node tree: one workgroup each (V = 12000), or 20
+    # workgroups each, more than the device holds at once, so the requests
+    # go out in several launches (V = 40000)
+    w = synth.make_workload(dict(name="many", B=200, H=1, D=64, L=3, V=V, dtype="f32",
                                  tree=("parents", [-1, 0, 0, 1, -1, 4, 5]), sig_t=2.0, sig_s=1.0), 11)
     _print_case("verify many requests", w.B, w.V)
     run = GpuRun(w).mask().greedy().mss()

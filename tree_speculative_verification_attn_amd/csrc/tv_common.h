@@ -150,6 +150,18 @@ __device__ __forceinline__ double wave_sum_dpp(double v) {
   return readlane_f64(v, 63);
 }
 
+// max of a float over the wave (NaN inputs lose to any number)
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  auto step = [](float x, float y) { return fmaxf(x, y); };
+  v = step(v, __int_as_float(dpp_mov<dpp::kQuadXor1>(__float_as_int(-INFINITY), __float_as_int(v))));
+  v = step(v, __int_as_float(dpp_mov<dpp::kQuadXor2>(__float_as_int(-INFINITY), __float_as_int(v))));
+  v = step(v, __int_as_float(dpp_mov<dpp::kRowHalfMirror>(__float_as_int(-INFINITY), __float_as_int(v))));
+  v = step(v, __int_as_float(dpp_mov<dpp::kRowMirror>(__float_as_int(-INFINITY), __float_as_int(v))));
+  v = step(v, __int_as_float(dpp_mov<dpp::kRowBcast15, 0xA>(__float_as_int(-INFINITY), __float_as_int(v))));
+  v = step(v, __int_as_float(dpp_mov<dpp::kRowBcast31, 0xC>(__float_as_int(-INFINITY), __float_as_int(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // OR of an int over the wave
 __device__ __forceinline__ int wave_or_dpp(int v) {
   v |= dpp_mov<dpp::kQuadXor1>(0, v);

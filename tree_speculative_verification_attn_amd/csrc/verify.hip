@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   uint32_t* done = a.done + static_cast<size_t>(b) * 64;
   uint64_t* hdr = a.hdr + static_cast<size_t>(b) * 2 * G * kHdr;
   uint64_t* kid = a.kid + static_cast<size_t>(b) * 2 * 64;
-  const bool vec = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 &&
+  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 &&
                    (!mss || (reinterpret_cast<uintptr_t>(a.ssm) & 15) == 0);
 
   __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES];
@@ -234,12 +234,14 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   __shared__ int s_status0, s_timeout, s_found, s_last;
   __shared__ float own_s[kElem];
 
+  static_assert(kElem % 4 == 0 || kElem < 4, "entries per thread");
   auto load8 = [&](const float* row, float (&dst)[kElem]) {
-    if (vec && nx == kElem) {
-      const float4 f0 = *reinterpret_cast<const float4*>(row + xa);
-      const float4 f1 = *reinterpret_cast<const float4*>(row + xa + 4);
-      dst[0] = f0.x; dst[1] = f0.y; dst[2] = f0.z; dst[3] = f0.w;
-      dst[4] = f1.x; dst[5] = f1.y; dst[6] = f1.z; dst[7] = f1.w;
+    if (vec && nx == kElem && kElem % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < kElem; e += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(row + xa + e);
+        dst[e] = f.x; dst[e + 1] = f.y; dst[e + 2] = f.z; dst[e + 3] = f.w;
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < kElem; ++k) dst[k] = k < nx ? row[xa + k] : 0.f;
@@ -674,6 +676,509 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-resident walk, for V <= kRowThreads * kRowMaxE (16384): one workgroup
+// of 512 threads per request holds the whole current distribution in
+// registers, so a step of the walk synchronises one workgroup and never waits
+// for another.  Up to that size a walk step is cheaper on one CU than an
+// exchange between CUs, which costs two memory round trips plus the skew
+// between workgroups; beyond it, one CU's share of memory bandwidth (a few
+// tens of GB/s) makes streaming a whole row slower than splitting it.  Two
+// waves per SIMD leave room for the distribution row, the row being reduced
+// and the temporaries; the passes are independent per entry, so two waves
+// keep the vector units busy.  Every node's draft probability of its own
+// token is loaded while the request is staged, so a ratio test never waits
+// for memory.
+//
+// Entry x of a row lives in thread (x mod 2048) / 4, register
+// 4 * (x / 2048) + x mod 4, so each load instruction of a wave reads 1 KB of
+// contiguous row, and a thread's registers are in increasing x order.
+//
+// Loads are issued as soon as their rows are known.  The entered node's row
+// and the draft row of its first tested child are fetched together; each
+// residual pass first takes the draft row of the rejected child, then starts
+// fetching the draft row of the child tested after it (the random choice of
+// that child does not depend on any outcome still open), so every draft row
+// streams in during a whole pass before it is needed.  Greedy fetches the
+// rows of the entered node's first two children while it reduces the node's
+// row.  One of the prefetched rows goes to LDS through direct-to-LDS loads,
+// which hold no registers while in flight.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 512;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kRowQuad = 4 * kRowThreads;        // entries covered by one register quad
+constexpr int kRowMaxE = 32;                     // registers per row per thread
+
+template <int E, bool VEC>
+__global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
+  static_assert(E % 4 == 0 && E <= kRowMaxE, "row registers");
+  constexpr int C = E / 4;
+  const int b = a.b0 + static_cast<int>(blockIdx.x);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int N = a.N, V = a.V;
+  const bool mss = a.mode == MODE_MSS;
+  const float* lbase = a.logits + static_cast<size_t>(b) * (N + 1) * V;
+  const float* sbase = mss ? a.ssm + static_cast<size_t>(b) * a.R * V : nullptr;
+
+  __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES];
+  __shared__ float s_qx[TV_MAX_NODES];           // MSS: each node's draft probability of its token
+  __shared__ uint64_t s_child[TV_MAX_NODES + 1];
+  __shared__ float s_wm[2][kRowWaves];           // per-wave max, two banks
+  __shared__ int s_wa[2][kRowWaves], s_wf[2][kRowWaves];
+  __shared__ double s_ws[2][kRowWaves];          // per-wave sums, two banks
+  __shared__ float s_ex[2][2];                   // the next child's token: old / new residual
+  __shared__ double s_scan[C * kRowWaves];       // final sample: wave totals, quad-major
+  __shared__ int s_status0, s_found;
+  // the prefetched row (a draft row in MSS, the second child's logits in
+  // greedy), in x order, written by direct-to-LDS loads; each wave reads
+  // back only what its own loads wrote
+  __shared__ float s_row[VEC ? E * kRowThreads : 4];
+
+  // entry held by register e of this thread
+  auto xof = [&](int e) { return (e >> 2) * kRowQuad + 4 * t + (e & 3); };
+  // Registers past the end of the row get a neutral value (-inf for logits,
+  // 0 for draft rows), so the passes over a row need no bounds tests: -inf
+  // never wins a max and becomes 0 in the distribution, and a zero draft
+  // entry leaves a zero residual.
+  // (The quad's offset stays in the scalar base address and the bounds test
+  // is uniform except in the one quad that the row's end cuts, so no
+  // per-quad vector state lives across the walk.)
+  const int t4 = 4 * t;
+  auto load_row = [&](const float* row, float (&d)[E], float pad) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const float* rq = row + i * kRowQuad;
+      const int lim = V - i * kRowQuad;        // entries of this quad inside the row
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[4 * i + r] = pad;
+      if constexpr (VEC) {     // V % 4 == 0 and 16-byte aligned rows
+        if (lim >= kRowQuad || (lim > 0 && t4 < lim)) {
+          const float4 f = *reinterpret_cast<const float4*>(rq + t4);
+          d[4 * i] = f.x; d[4 * i + 1] = f.y; d[4 * i + 2] = f.z; d[4 * i + 3] = f.w;
+        }
+      } else {
+        if (lim >= kRowQuad) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d[4 * i + r] = rq[t4 + r];
+        } else if (lim > 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (t4 + r < lim) d[4 * i + r] = rq[t4 + r];
+        }
+      }
+    }
+  };
+  // Start loading a row into s_row (no registers held while it streams).
+  // Rows that vector loads cannot read (V % 4 != 0, or unaligned) are read
+  // straight into registers when they are taken instead.
+  const float* pf_row = nullptr;
+  auto dma_row = [&](const float* row) {
+    pf_row = row;
+    if constexpr (VEC) {
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const int lim = V - i * kRowQuad;
+        if (lim >= kRowQuad || (lim > 0 && t4 < lim)) {
+          const float* src = row + i * kRowQuad + t4;
+          // lane l's 16 bytes land at M0 + 16 l: this wave's 1 KB of the quad
+          const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_row + i * kRowQuad + 256 * wave));
+          asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(dst) : "memory");
+        }
+      }
+    }
+  };
+  // take the prefetched row into registers (past the row's end: pad)
+  auto lds_row = [&](float (&d)[E], float pad) {
+    if constexpr (VEC) {
+      // the row's loads have landed (they are this wave's oldest outstanding loads)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const int lim = V - i * kRowQuad;
+        float4 f = make_float4(pad, pad, pad, pad);
+        if (lim >= kRowQuad || (lim > 0 && t4 < lim))
+          f = *reinterpret_cast<const float4*>(s_row + i * kRowQuad + t4);
+        d[4 * i] = f.x; d[4 * i + 1] = f.y; d[4 * i + 2] = f.z; d[4 * i + 3] = f.w;
+      }
+      // every read of s_row is complete before a later load may overwrite it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else {
+      load_row(pf_row, d, pad);
+    }
+  };
+  // value of entry x in the thread that holds it
+  auto held = [&](const float (&d)[E], int x) {
+    const int r = 4 * (x / kRowQuad) + (x & 3);
+    float v = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) v = e == r ? d[e] : v;
+    return v;
+  };
+  auto holds = [&](int x) { return x >= 0 && ((x % kRowQuad) >> 2) == t; };
+  // workgroup sum of a double and OR of an int (one barrier, alternating banks)
+  int bank = 0;
+  auto block_sum = [&](double v, int f, int* f_out) {
+    v = tv::wave_sum_dpp(v);
+    f = tv::wave_or_dpp(f);
+    if (lane == 0) {
+      s_ws[bank][wave] = v;
+      s_wf[bank][wave] = f;
+    }
+    __syncthreads();
+    // lanes 0..15 take the wave partials; the same DPP reduction in every
+    // wave gives every thread the same sum
+    const double s = tv::wave_sum_dpp(lane < kRowWaves ? s_ws[bank][lane] : 0.0);
+    const int o = tv::wave_or_dpp(lane < kRowWaves ? s_wf[bank][lane] : 0);
+    bank ^= 1;
+    *f_out = o;
+    return s;
+  };
+  // workgroup max of the valid entries (lowest index among equal maxima) and
+  // whether any is NaN (one barrier)
+  auto block_argmax = [&](const float (&d)[E], float* m_out, int* a_out) {
+    float mx = -INFINITY;
+    int re = -1, nan = 0;          // register of the first maximum
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float f = d[e];
+      nan |= f != f;
+      if (f > mx || (f == mx && re < 0)) {
+        mx = f;
+        re = e;
+      }
+    }
+    int arg = (re >> 2) * kRowQuad + 4 * t + (re & 3);
+    tv::wave_argmax_dpp(mx, arg);
+    nan = tv::wave_or_dpp(nan);
+    if (lane == 0) {
+      s_wm[bank][wave] = mx;
+      s_wa[bank][wave] = arg;
+      s_wf[bank][wave] = nan;
+    }
+    __syncthreads();
+    float M = lane < kRowWaves ? s_wm[bank][lane] : -INFINITY;
+    int A = lane < kRowWaves ? s_wa[bank][lane] : 0x7FFFFFFF;
+    tv::wave_argmax_dpp(M, A);
+    const int F = tv::wave_or_dpp(lane < kRowWaves ? s_wf[bank][lane] : 0);
+    bank ^= 1;
+    *m_out = M;
+    *a_out = A;
+    return F;     // nonzero: some entry is NaN
+  };
+  // the same without the index (MSS needs only the maximum)
+  auto block_max = [&](const float (&d)[E], float* m_out) {
+    float mx = -INFINITY;
+    int nan = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      nan |= d[e] != d[e];
+      mx = fmaxf(mx, d[e]);
+    }
+    mx = tv::wave_max_dpp(mx);
+    nan = tv::wave_or_dpp(nan);
+    if (lane == 0) {
+      s_wm[bank][wave] = mx;
+      s_wf[bank][wave] = nan;
+    }
+    __syncthreads();
+    const float M = tv::wave_max_dpp(lane < kRowWaves ? s_wm[bank][lane] : -INFINITY);
+    const int F = tv::wave_or_dpp(lane < kRowWaves ? s_wf[bank][lane] : 0);
+    bank ^= 1;
+    *m_out = M;
+    return F;
+  };
+
+  // ---------------- first loads, staging ----------------
+  float lv[E];             // the entered node's logits; then its distribution (unnormalised)
+  float qa[E];             // MSS: the rejected child's draft row, then the residual; greedy: first child's row
+  load_row(lbase, lv, -INFINITY);
+  if (wave == 0) {
+    const size_t rb = static_cast<size_t>(b);
+    const int st0 = lane == 0 ? a.status[b] : 0;
+    const uint64_t cm = lane < N ? a.child[rb * (N + 1) + lane] & later_nodes(lane - 1, N) : 0ull;
+    const int tok = lane < N ? a.token[rb * N + lane] : 0;
+    const int qr = (mss && lane < N) ? a.q_row[rb * N + lane] : 0;
+    const uint64_t real = wave_or64(cm);
+    const uint64_t bad_tok = __ballot(lane < N && (tok < 0 || tok >= V));
+    const uint64_t bad_q = __ballot(mss && lane < N && (qr < 0 || qr >= a.R));
+    s_child[lane] = cm;
+    s_tok[lane] = tok;
+    s_qrow[lane] = qr;
+    // every tested child's ratio needs q(token): load them all now, in parallel
+    const bool ok_q = mss && lane < N && tok >= 0 && tok < V && qr >= 0 && qr < a.R;
+    s_qx[lane] = ok_q ? sbase[static_cast<size_t>(qr) * V + tok] : 0.f;
+    if (lane == 0) {
+      s_child[TV_MAX_NODES] = 0ull;
+      int st = st0;
+      if (st == TV_REQ_OK) {
+        if (bad_tok & real) st = TV_REQ_BAD_TOKEN;
+        else if (bad_q & real) st = TV_REQ_BAD_QROW;
+      }
+      s_status0 = st;
+    }
+  }
+  __syncthreads();
+
+  int status = s_status0;
+  int u = -1, k = 0, rounds = 0, bonus = -1;
+  uint64_t U = s_child[0];
+  double Z = 1.0;
+  bool final_sample = false;
+
+  if (status == TV_REQ_OK && !mss) {
+    // ---------------- greedy ----------------
+    int c1 = -1, c2 = -1;
+    auto fetch_children = [&]() {
+      c1 = U ? __builtin_ctzll(U) : -1;
+      const uint64_t rest = U & (U - 1);
+      c2 = rest ? __builtin_ctzll(rest) : -1;
+      if (c1 >= 0) load_row(lbase + static_cast<size_t>(c1 + 1) * V, qa, -INFINITY);
+      if (c2 >= 0) dma_row(lbase + static_cast<size_t>(c2 + 1) * V);
+    };
+    fetch_children();
+    for (;;) {
+      float M;
+      int A;
+      const int nan = block_argmax(lv, &M, &A);
+      if (nan || M == INFINITY || M == -INFINITY) {
+        status = TV_REQ_NONFINITE;
+        break;
+      }
+      const uint64_t hit = __ballot(lane < N && ((U >> lane) & 1ull) && s_tok[lane] == A);
+      if (!hit) {
+        bonus = A;
+        break;
+      }
+      const int nxt = __builtin_ctzll(hit);
+      if (t == 0) s_acc[k] = nxt;
+      ++k;
+      u = nxt;
+      U = s_child[nxt + 1];
+      if (nxt == c1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) lv[e] = qa[e];
+      } else if (nxt == c2) {
+        lds_row(lv, -INFINITY);
+      } else {
+        load_row(lbase + static_cast<size_t>(u + 1) * V, lv, -INFINITY);
+      }
+      fetch_children();
+    }
+  } else if (status == TV_REQ_OK) {
+    // ---------------- MSS ----------------
+    int j = 0, cand = -1;
+    float qx = 0.f;          // draft probability of the candidate's token
+    auto choose = [&]() {    // candidate of round j among U; start fetching its draft row
+      cand = -1;
+      if (U) {
+        const tv::u32x4 w = tv::mss_words(a.seed, a.offset, b, u + 1, j);
+        cand = nth_bit(U, tv::pick_index(w.x, __builtin_popcountll(U)));
+        dma_row(sbase + static_cast<size_t>(s_qrow[cand]) * V);
+        qx = s_qx[cand];
+      }
+    };
+    choose();
+    float ex = 0.f;          // current distribution at the candidate's token (unnormalised)
+    bool enter = true;
+    for (;;) {
+      if (enter) {
+        // ---- statistics of u's row; lv becomes exp(l - max) ----
+        float M;
+        const int nan = block_max(lv, &M);
+        if (nan || M == INFINITY || M == -INFINITY) {
+          status = TV_REQ_NONFINITE;
+          break;
+        }
+        double acc = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          lv[e] = lv[e] != -INFINITY ? tv::exp_acc(lv[e] - M) : 0.f;
+          acc += static_cast<double>(lv[e]);
+        }
+        if (cand >= 0 && holds(s_tok[cand])) s_ex[bank][0] = held(lv, s_tok[cand]);
+        const int eb = bank;
+        int unused;
+        Z = block_sum(acc, 0, &unused);
+        ex = s_ex[eb][0];
+        enter = false;
+      }
+      if (cand < 0) {
+        final_sample = true;
+        break;
+      }
+      // ---- ratio test: u1 <= p(x) / q(x) with p(x) = ex / Z, tested as
+      // u1 * q(x) * Z <= ex; q(x) = 0 accepts exactly when p(x) > 0 ----
+      if (q_bad(qx)) {
+        status = TV_REQ_NONFINITE;
+        break;
+      }
+      const tv::u32x4 w = tv::mss_words(a.seed, a.offset, b, u + 1, j);
+      const double e = static_cast<double>(ex);
+      const bool accept = qx > 0.f ? tv::unit_open0(w.y) * static_cast<double>(qx) * Z <= e : e > 0.0;
+      ++rounds;
+      if (accept) {
+        if (t == 0) s_acc[k] = cand;
+        ++k;
+        u = cand;
+        U = s_child[cand + 1];
+        j = 0;
+        load_row(lbase + static_cast<size_t>(u + 1) * V, lv, -INFINITY);
+        choose();
+        enter = true;
+        continue;
+      }
+      // ---- rejection: residual max(0, p - q) with the rejected child's draft row ----
+      U &= ~(1ull << cand);
+      ++j;
+      lds_row(qa, 0.f);
+      choose();                         // the next candidate's draft row now streams into s_row
+      double acc = 0.0;
+      int bad = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (q_bad(qa[e])) bad = 1;
+        qa[e] = static_cast<float>(fmax(0.0, static_cast<double>(lv[e]) - Z * static_cast<double>(qa[e])));
+        acc += static_cast<double>(qa[e]);
+      }
+      if (cand >= 0 && holds(s_tok[cand])) {
+        s_ex[bank][0] = held(lv, s_tok[cand]);
+        s_ex[bank][1] = held(qa, s_tok[cand]);
+      }
+      const int eb = bank;
+      int anyb;
+      const double Znew = block_sum(acc, bad, &anyb);
+      if (anyb) {
+        status = TV_REQ_NONFINITE;
+        break;
+      }
+      if (Znew > 0.0) {                 // else the distribution stays (zero-normaliser guard)
+#pragma unroll
+        for (int e = 0; e < E; ++e) lv[e] = qa[e];
+        Z = Znew;
+        ex = s_ex[eb][1];
+      } else {
+        ex = s_ex[eb][0];
+      }
+    }
+  }
+
+  // ---------------- final sample: smallest x with cumsum >= u2 * total ----------------
+  // Cumulative sums run in x order: quad by quad, within a quad wave by wave,
+  // within a wave lane by lane (four entries per lane).  Every wave publishes
+  // its scanned total per quad; a scan over those totals (the same in every
+  // wave) finds the (quad, wave) whose range brackets the threshold, and only
+  // that wave repeats its lane scan (the same operations on the same values,
+  // so the same sums) to find the lane and the entry.  Inside one wave each
+  // inclusive sum equals the next lane's exclusive sum bit for bit, so with
+  // the threshold clamped to the wave's top exactly one lane brackets it.
+  if (final_sample) {
+    constexpr int K = C * kRowWaves;                 // (quad, wave) ranges
+    constexpr int NB = (K + 63) / 64;
+    const tv::u32x4 w0 = tv::mss_words(a.seed, a.offset, b, u + 1, 0);
+    auto quad_sum = [&](int i) {
+      double s = 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += static_cast<double>(lv[4 * i + r]);
+      return s;
+    };
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      double ex;
+      const double inc = tv::wave_scan_dpp(quad_sum(i), &ex);
+      if (lane == 63) s_scan[i * kRowWaves + wave] = inc;
+    }
+    if (t == 0) s_found = -1;
+    __syncthreads();
+    // prefix sums over the ranges, 64 per batch (every wave alike)
+    double lo[NB], hi[NB], carry = 0.0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int kk = nb * 64 + lane;
+      const double v = kk < K ? s_scan[kk] : 0.0;
+      double ex;
+      const double in = tv::wave_scan_dpp(v, &ex);
+      lo[nb] = carry + ex;
+      hi[nb] = carry + in;
+      carry = tv::readlane_f64(hi[nb], 63);
+    }
+    const double T = tv::unit_open0(w0.z) * carry;   // in (0, total]
+    int kstar = -1;
+    double Astar = 0.0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint64_t hit = __ballot(lo[nb] < T && hi[nb] >= T);
+      if (kstar < 0 && hit) {
+        const int l = __builtin_ctzll(hit);
+        kstar = nb * 64 + l;
+        Astar = tv::readlane_f64(lo[nb], l);
+      }
+    }
+    if (kstar < 0) {            // rounding left the total short: the last non-empty range
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint64_t pos = __ballot(hi[nb] > lo[nb]);
+        if (pos) {
+          const int l = 63 - __builtin_clzll(pos);
+          kstar = nb * 64 + l;
+          Astar = tv::readlane_f64(lo[nb], l);
+        }
+      }
+    }
+    const int qi = kstar / kRowWaves, qw = kstar % kRowWaves;
+    if (kstar >= 0 && wave == qw) {
+      double sq = 0.0;
+#pragma unroll
+      for (int i = 0; i < C; ++i)
+        if (i == qi) sq = quad_sum(i);
+      double exl;
+      const double inl = tv::wave_scan_dpp(sq, &exl);
+      const double Tw = fmin(T, Astar + tv::readlane_f64(inl, 63));
+      const double l0 = Astar + exl, l1 = Astar + inl;
+      if (l0 < Tw && l1 >= Tw) {
+        double accd = l0;
+        int xs = -1, last_pos = -1;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          if (i == qi) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float c = lv[4 * i + r];
+              if (xs < 0) {
+                if (c > 0.f) last_pos = xof(4 * i + r);
+                accd += static_cast<double>(c);
+                if (accd >= Tw) xs = xof(4 * i + r);
+              }
+            }
+          }
+        }
+        s_found = xs >= 0 ? xs : last_pos;   // rounding left the lane short: its last positive entry
+      }
+    }
+    __syncthreads();
+    bonus = s_found;
+  }
+
+  // ---------------- results ----------------
+  // a prefetched row that was never taken may still be landing in LDS: let
+  // it land before the workgroup's LDS can go to another workgroup
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();       // s_acc complete
+  if (t == 0) {
+    if (status != TV_REQ_OK) {
+      a.status[b] = status;
+      a.num_accepted[b] = -1;
+      a.bonus[b] = -1;
+      if (a.rounds) a.rounds[b] = -1;
+    } else {
+      a.num_accepted[b] = k;
+      a.bonus[b] = bonus;
+      if (a.rounds) a.rounds[b] = rounds;
+    }
+  }
+  const int kk = status == TV_REQ_OK ? k : 0;
+  for (int i = t; i < N; i += kRowThreads) a.accepted[static_cast<size_t>(b) * N + i] = i < kk ? s_acc[i] : -1;
+}
+
 tv_status check_verify_args(int B, int N, int V) {
   if (B < 0 || N < 0 || V < 1 || V > (1 << 20)) return TV_EINVAL;
   if (N > TV_MAX_NODES) return TV_ETOOBIG;
@@ -695,10 +1200,27 @@ int walk_capacity(int dev) {
   return cap;
 }
 
+template <int E>
+void launch_row(const WalkArgs& a, int B, bool vec, hipStream_t stream) {
+  if (vec)
+    hipLaunchKernelGGL((walk_row_kernel<E, true>), dim3(B), dim3(kRowThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((walk_row_kernel<E, false>), dim3(B), dim3(kRowThreads), 0, stream, a);
+}
+
 // Launch the walk in request batches whose workgroups all fit on the device
 // at once, so the workgroups of a request never wait for one another's
 // residency (the waits are bounded regardless).
 tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
+  if (a.V <= kRowThreads * kRowMaxE) {     // one workgroup per request
+    a.b0 = 0;
+    const bool vec = (a.V & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 &&
+                     (a.mode != MODE_MSS || (reinterpret_cast<uintptr_t>(a.ssm) & 15) == 0);
+    if (a.V <= kRowThreads * 8) launch_row<8>(a, B, vec, stream);
+    else if (a.V <= kRowThreads * 16) launch_row<16>(a, B, vec, stream);
+    else launch_row<32>(a, B, vec, stream);
+    return tv::launch_status();
+  }
   const int G = a.G;
   if (G == 1) {          // a request's only workgroup waits on nobody else
     a.b0 = 0;
