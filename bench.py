@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (2 = LLaMA-7B layer)")
+    ap.add_argument("--config", type=int, default=None, help="workload id 1..5 (default 2 = LLaMA-7B layer)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU sample time")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
@@ -44,6 +44,8 @@ def parse():
                     help="run warmup + steps eager steps and exit (for counter collection)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (counter calibration)")
+    ap.add_argument("--compare-sequence", action="store_true",
+                    help="only time tree against per-path attention on workloads 2..5, one JSON line each")
     return ap.parse_args()
 
 
@@ -73,6 +75,9 @@ def main():
     if args.copy_calibration_mb:
         copy_calibration(torch, args.copy_calibration_mb)
         return
+    if args.compare_sequence:
+        compare_sequence_all(torch, [args.config] if args.config else [2, 3, 4, 5])
+        return
 
     import synth
     import tree_speculative_verification_attn_amd as tv
@@ -80,7 +85,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
-    w = synth.make_config(args.config)
+    w = synth.make_config(args.config or 2)
     bf = w.dtype == "bf16"
     B, N, H, D, V, R = w.B, w.N, w.H, w.D, w.V, w.R
     step_bytes = w.k_cache.nbytes * 2 + w.target_logits.nbytes + w.ssm_probs.nbytes
@@ -238,9 +243,111 @@ def main():
                 "tree_attn_plus_mss_tokens_per_s": round(B * N / ((t_attn + t_mss) * 1e-3), 1),
                 "mean_tokens_emitted_per_request": round(acc_tokens, 3)},
     }
+    res["tree_vs_sequence"] = tree_vs_sequence(torch, tv, w, copies, bt, t_attn, stream)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, value)
     print(json.dumps(res))
+
+
+def compare_sequence_all(torch, cfgs):
+    """Tree against per-path attention on the given workloads (one JSON line each)."""
+    import synth
+    import tree_speculative_verification_attn_amd as tv
+    from tests.gpu_util import to_dev
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    for cfg in cfgs:
+        w = synth.make_config(cfg)
+        bf = w.dtype == "bf16"
+        n_copies = max(2, int(np.ceil(2 * MALL_BYTES / max(1, w.k_cache.nbytes * 2))) + 1)
+        copies = [dict(q=to_dev(w.q, bf), k=to_dev(w.k_cache, bf), v=to_dev(w.v_cache, bf))
+                  for _ in range(n_copies)]
+        bt, pl = to_dev(w.block_table), to_dev(w.prefix_len)
+        anc = torch.zeros((w.B, w.N), dtype=torch.int64, device=dev)
+        child = torch.zeros((w.B, w.N + 1), dtype=torch.int64, device=dev)
+        depth = torch.zeros((w.B, w.N), dtype=torch.int32, device=dev)
+        st = torch.zeros((w.B,), dtype=torch.int32, device=dev)
+        tv.tree_build_mask(to_dev(w.parent), anc, child, depth, st)
+        code = tv.TV_BF16 if bf else tv.TV_F32
+        n = tv.tree_attn_verify_workspace(code, w.B, w.N, w.H, w.D, w.max_blocks)
+        ws = torch.zeros(n, dtype=torch.uint8, device=dev) if n else None
+        out = torch.empty_like(copies[0]["q"])
+
+        def call(c):
+            tv.tree_attn_verify(c["q"], c["k"], c["v"], bt, pl, anc, st, out, ws, scale=w.scale)
+
+        for c in copies:
+            call(c)
+        torch.cuda.synchronize()
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            for c in copies * 2:
+                call(c)
+        gph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            gph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_tree = e0.elapsed_time(e1) / (5 * 2 * n_copies)
+        assert int((st != 0).sum()) == 0
+        del gph
+        r = tree_vs_sequence(torch, tv, w, copies, bt, t_tree, stream, reps=5)
+        r["workload"] = f"{w.name}: B={w.B} H={w.H} D={w.D} N={w.N} L_max={int(w.prefix_len.max())}"
+        print(json.dumps(r), flush=True)
+        del copies, ws, out
+        torch.cuda.empty_cache()
+
+
+def tree_vs_sequence(torch, tv, w, copies, bt, t_tree, stream, reps=10):
+    """Tree attention against sequence-based verification of the same tree
+    (SpecInfer summary, "Evaluation", Figure 11): every root-to-leaf path as a
+    chain of its own over the same prefix blocks, through the same attention
+    kernel, timed like the tree call (a graph of back-to-back calls over the
+    rotating input copies)."""
+    from tree_speculative_verification_attn_amd import per_sequence
+    dev = "cuda:0"
+    sbs = [per_sequence.build(w.parent, w.prefix_len, c["q"], c["k"], c["v"], bt) for c in copies]
+    S, N2 = sbs[0].S, sbs[0].N
+    anc = torch.zeros((S, N2), dtype=torch.int64, device=dev)
+    child = torch.zeros((S, N2 + 1), dtype=torch.int64, device=dev)
+    depth = torch.zeros((S, N2), dtype=torch.int32, device=dev)
+    st = torch.zeros((S,), dtype=torch.int32, device=dev)
+    tv.tree_build_mask(sbs[0].parent, anc, child, depth, st)
+    code = tv.TV_BF16 if w.dtype == "bf16" else tv.TV_F32
+    n = tv.tree_attn_verify_workspace(code, S, N2, w.H, w.D, sbs[0].block_table.shape[1])
+    ws = torch.zeros(n, dtype=torch.uint8, device=dev) if n else None
+    out = torch.empty_like(sbs[0].q)
+
+    def call(sb):
+        tv.tree_attn_verify(sb.q, sb.k_cache, sb.v_cache, sb.block_table, sb.prefix_len, anc, st, out, ws,
+                            scale=w.scale)
+
+    for sb in sbs:
+        call(sb)
+    torch.cuda.synchronize()
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph):
+        for sb in sbs * 2:
+            call(sb)
+    gph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        gph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_seq = e0.elapsed_time(e1) / (reps * 2 * len(sbs))
+    assert int((st != 0).sum()) == 0, "a per-path request failed"
+    esz = 2 if w.dtype == "bf16" else 4
+    tree_kv = int(np.sum(w.prefix_len.astype(np.int64) + w.N)) * w.H * w.D * esz * 2
+    return {"paths": S, "longest_path": N2, "tree_ms": round(t_tree, 5), "sequence_ms": round(t_seq, 5),
+            "tree_speedup": round(t_seq / t_tree, 3), "tree_kv_bytes": tree_kv,
+            "sequence_kv_bytes": sbs[0].kv_bytes,
+            "kernel": "tree_attn_verify for both; paths share the physical prefix blocks"}
 
 
 def copy_calibration(torch, mib):
