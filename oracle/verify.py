@@ -273,3 +273,57 @@ def naive_reject_prob(p, child_tokens):
     rejects with probability 1 - (mass of the distinct child tokens)."""
     toks = sorted(set(int(t) for t in child_tokens))
     return 1.0 - float(sum(p[t] for t in toks))
+
+
+def naive_one(b, parent, token, logits, seed, offset):
+    """Naive sampling verification for request b (Theorem 4.3's comparator):
+    at node u draw x from P_LLM(.|u); if a child of u carries token x, move to
+    the lowest such child, otherwise x is the bonus token and the walk stops.
+
+    Readings: the draw uses the same word as MSS's final sample (word 2 of
+    round 0 at u's slot, inverse CDF as in sample_from), and a miss emits the
+    drawn token, so every emitted token is distributed as P_LLM given the
+    tokens before it; the pages' remark that naive sampling never emits a
+    token outside the tree describes a variant that would be biased.
+    Returns (accepted, bonus, status, trace)."""
+    accepted = []
+    trace = []
+    u = -1
+    while True:
+        if not row_ok(logits[u + 1]):
+            return accepted, -1, ST_NONFINITE, trace
+        p = softmax_row(logits[u + 1])
+        w = philox.words(seed, offset, b, u + 1, 0)
+        x, margin = sample_from(p, philox.unit_open0(w[2]))
+        trace.append(("sample", margin))
+        nxt = next((c for c in children_of(parent, u) if int(token[c]) == x), None)
+        if nxt is None:
+            return accepted, x, ST_OK, trace
+        accepted.append(nxt)
+        u = nxt
+
+
+def verify_naive(parent, token, target_logits, status, seed, offset=0):
+    """Batched naive sampling verification; same outputs as verify_greedy plus
+    traces."""
+    B, N = token.shape
+    V = target_logits.shape[2]
+    acc = np.full((B, N), -1, dtype=np.int64)
+    num = np.full(B, -1, dtype=np.int64)
+    bonus = np.full(B, -1, dtype=np.int64)
+    st = [int(s) for s in status]
+    traces = [[] for _ in range(B)]
+    for b in range(B):
+        if st[b] == ST_OK:
+            st[b] = _request_checks(parent[b], token[b], V)
+        if st[b] != ST_OK:
+            continue
+        path, bn, s_b, tr = naive_one(b, parent[b], token[b], target_logits[b], seed, offset)
+        traces[b] = tr
+        st[b] = s_b
+        if s_b != ST_OK:
+            continue
+        acc[b, : len(path)] = path
+        num[b] = len(path)
+        bonus[b] = bn
+    return dict(accepted=acc, num_accepted=num, bonus=bonus, status=np.array(st), traces=traces)
