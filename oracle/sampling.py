@@ -19,28 +19,38 @@ the usual definitions:
     depend on T);
   * -inf entries have probability 0 and are never kept; a row with a NaN or
     +inf entry, or with no finite entry, becomes all NaN.
-Outputs: kind "logits" gives l / T where kept and -inf elsewhere (a softmax of
-it is the transformed distribution); kind "probs" gives the normalised kept
-probabilities and 0 elsewhere.
+Outputs: kind "logits" gives the scaled logits where kept and -inf elsewhere
+(a softmax of them is the transformed distribution); kind "probs" gives the
+normalised kept probabilities and 0 elsewhere.
+
+Precision reading: the rows are fp32, so the scaled logit is the fp32 product
+l' = fp32(l * fp32(1 / T)) (exact for T = 1), and ranks, masses and outputs
+are taken from l'.  A consumer of the "logits" output then sees exactly these
+fp32 values.
 """
 import numpy as np
 
 
-def _f64(logits_row):
-    return np.asarray(logits_row, dtype=np.float32).astype(np.float64)
+def scaled(logits_row, temperature):
+    """l' = fp32(l * fp32(1/T)) as float64 (non-finite entries pass through)."""
+    l32 = np.asarray(logits_row, dtype=np.float32)
+    inv = np.float32(1.0) / np.float32(temperature)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return (l32 * inv).astype(np.float32).astype(np.float64)
 
 
 def kept_in_rank_order(logits_row, temperature=1.0, top_k=0, top_p=1.0):
     """The kept entries, largest first (ties: lower index first), or None for
     an invalid row."""
-    l = _f64(logits_row)
-    if np.isnan(l).any() or np.isposinf(l).any() or not np.isfinite(l).any():
+    raw = np.asarray(logits_row, dtype=np.float32)
+    if np.isnan(raw).any() or np.isposinf(raw).any() or not np.isfinite(raw).any():
         return None
-    order = sorted(np.nonzero(np.isfinite(l))[0].tolist(), key=lambda x: (-l[x], x))
+    l = scaled(raw, temperature)
+    order = sorted(np.nonzero(np.isfinite(raw))[0].tolist(), key=lambda x: (-l[x], x))
     if top_k > 0:
         order = order[:top_k]
     if top_p < 1.0:
-        mass = np.exp((l[order] - l[order[0]]) / temperature)
+        mass = np.exp(l[order] - l[order[0]])
         target = top_p * mass.sum()
         csum = np.cumsum(mass)
         reach = np.nonzero(csum >= target)[0]
@@ -50,17 +60,18 @@ def kept_in_rank_order(logits_row, temperature=1.0, top_k=0, top_p=1.0):
 
 def transform_row(logits_row, temperature=1.0, top_k=0, top_p=1.0, kind="logits"):
     """One transformed row (float64)."""
-    l = _f64(logits_row)
-    keep = kept_in_rank_order(l, temperature, top_k, top_p)
+    raw = np.asarray(logits_row, dtype=np.float32)
+    keep = kept_in_rank_order(raw, temperature, top_k, top_p)
     if keep is None:
-        return np.full(l.shape, np.nan)
+        return np.full(raw.shape, np.nan)
     keep = np.asarray(keep, dtype=np.int64)
+    l = scaled(raw, temperature)
     if kind == "logits":
-        out = np.full(l.shape, -np.inf)
-        out[keep] = l[keep] / temperature
+        out = np.full(raw.shape, -np.inf)
+        out[keep] = l[keep]
         return out
-    e = np.exp((l[keep] - l[keep].max()) / temperature)
-    out = np.zeros(l.shape)
+    e = np.exp(l[keep] - l[keep].max())
+    out = np.zeros(raw.shape)
     out[keep] = e / e.sum()
     return out
 
@@ -76,10 +87,10 @@ def transform(rows, temperature=1.0, top_k=0, top_p=1.0, kind="logits"):
 def top_p_margin(logits_row, temperature, top_k, top_p):
     """Distance, relative to the kept mass, of the top-p target to the nearest
     cumulative mass in rank order (rounding can move the cut when it is tiny)."""
-    l = _f64(logits_row)
-    keep = kept_in_rank_order(l, temperature, top_k, 1.0)
+    keep = kept_in_rank_order(logits_row, temperature, top_k, 1.0)
     if keep is None or top_p >= 1.0:
         return np.inf
-    mass = np.exp((l[keep] - l[keep[0]]) / temperature)
+    l = scaled(logits_row, temperature)
+    mass = np.exp(l[keep] - l[keep[0]])
     csum = np.cumsum(mass)
     return float(np.min(np.abs(csum - top_p * csum[-1])) / csum[-1])

@@ -27,11 +27,12 @@ def _beats(l, x):
 
 
 def _kept_by_rank(l, T, k, p):
+    l = sampling.scaled(l, T)          # ranks and masses on fp32(l * fp32(1/T))
     fin = [x for x in range(len(l)) if np.isfinite(l[x])]
     keep = [x for x in fin if k == 0 or len(_beats(l, x)) < k]
     if p < 1.0:
         top = max(l[x] for x in keep)
-        m = {x: math.exp((l[x] - top) / T) for x in keep}
+        m = {x: math.exp(l[x] - top) for x in keep}
         tot = sum(m.values())
         keep = [x for x in keep if sum(m[y] for y in _beats(l, x) if y in m) < p * tot]
     return sorted(keep)
@@ -45,9 +46,13 @@ def test_plain_softmax_and_temperature():
     for T in (0.3, 0.7, 2.5):
         p = sampling.transform_row(l, temperature=T, kind="probs")
         i, j = 3, 17
-        assert math.isclose(p[i] / p[j], math.exp((float(l[i]) - float(l[j])) / T), rel_tol=1e-12)
+        # the ratio of two probabilities is exp of the logit difference over T
+        # (up to the fp32 rounding of the scaled logits)
+        assert math.isclose(p[i] / p[j], math.exp((float(l[i]) - float(l[j])) / T), rel_tol=1e-6)
         lg = sampling.transform_row(l, temperature=T, kind="logits")
-        np.testing.assert_allclose(lg, l.astype(np.float64) / T)
+        np.testing.assert_allclose(lg, l.astype(np.float64) / T, rtol=1.2e-7)
+        assert (lg.astype(np.float32).astype(np.float64) == lg).all()      # fp32 values
+    assert (sampling.transform_row(l, kind="logits") == l.astype(np.float64)).all()
     # low temperature concentrates on the argmax, high temperature flattens
     assert sampling.transform_row(l, temperature=0.01, kind="probs")[int(np.argmax(l))] > 0.999
     assert np.ptp(sampling.transform_row(l, temperature=1e4, kind="probs")) < 1e-3
@@ -82,7 +87,7 @@ def test_ties_invalid_rows_and_extremes():
     p = sampling.transform_row(l2, 1.0, 1, 1.0, kind="probs")
     assert p.tolist() == [0.0, 1.0, 0.0, 0.0, 0.0]
     lg = sampling.transform_row(l2, 2.0, 2, 1.0, kind="logits")
-    assert lg.tolist() == [-np.inf, 2.5, 2.5, -np.inf, -np.inf]
+    assert lg.tolist() == [-np.inf, 2.5, 2.5, -np.inf, -np.inf]       # 5 * 0.5 is exact in fp32
     for bad in ([0.0, np.nan], [0.0, np.inf], [-np.inf, -np.inf]):
         assert np.isnan(sampling.transform_row(np.array(bad, dtype=np.float32), kind="probs")).all()
     # a tiny top-p keeps only the largest entry
