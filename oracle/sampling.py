@@ -18,7 +18,8 @@ the usual definitions:
   * order: temperature, then top-k, then top-p (top-k on logits does not
     depend on T);
   * -inf entries have probability 0 and are never kept; a row with a NaN or
-    +inf entry, or with no finite entry, becomes all NaN.
+    +inf entry, or with no finite entry, becomes all NaN (judged on the scaled
+    values below, so a finite logit that the scaling overflows counts too).
 Outputs: kind "logits" gives the scaled logits where kept and -inf elsewhere
 (a softmax of them is the transformed distribution); kind "probs" gives the
 normalised kept probabilities and 0 elsewhere.
@@ -42,11 +43,10 @@ def scaled(logits_row, temperature):
 def kept_in_rank_order(logits_row, temperature=1.0, top_k=0, top_p=1.0):
     """The kept entries, largest first (ties: lower index first), or None for
     an invalid row."""
-    raw = np.asarray(logits_row, dtype=np.float32)
-    if np.isnan(raw).any() or np.isposinf(raw).any() or not np.isfinite(raw).any():
+    l = scaled(logits_row, temperature)
+    if np.isnan(l).any() or np.isposinf(l).any() or not np.isfinite(l).any():
         return None
-    l = scaled(raw, temperature)
-    order = sorted(np.nonzero(np.isfinite(raw))[0].tolist(), key=lambda x: (-l[x], x))
+    order = sorted(np.nonzero(np.isfinite(l))[0].tolist(), key=lambda x: (-l[x], x))
     if top_k > 0:
         order = order[:top_k]
     if top_p < 1.0:

@@ -90,6 +90,9 @@ def test_ties_invalid_rows_and_extremes():
     assert lg.tolist() == [-np.inf, 2.5, 2.5, -np.inf, -np.inf]       # 5 * 0.5 is exact in fp32
     for bad in ([0.0, np.nan], [0.0, np.inf], [-np.inf, -np.inf]):
         assert np.isnan(sampling.transform_row(np.array(bad, dtype=np.float32), kind="probs")).all()
+    # scaling that overflows a finite logit makes the row invalid
+    assert np.isnan(sampling.transform_row(np.array([3e38, 1.0], dtype=np.float32), 0.5)).all()
+    assert sampling.kept_in_rank_order(np.array([-3e38, 1.0], dtype=np.float32), 0.5) == [1]
     # a tiny top-p keeps only the largest entry
     assert sampling.kept_in_rank_order(l2, 1.0, 0, 1e-9) == [1]
 
