@@ -233,6 +233,40 @@ tv_status kv_commit_accepted(tv_dtype dt, int B, int N, int H, int D, void* k_ca
                              int32_t* status, hipStream_t stream);
 
 /* Human-readable name of a tv_status value (static storage). */
+/*
+ * tree_logits_transform - sampling transforms of rows of logits, applied
+ * before verification.
+ * Defines: wiki concept page "Speculative decoding", "Implementation sketch":
+ * the lossless acceptance rule is applied after temperature, top-k and top-p
+ * have been applied to both the target's and the draft's distribution.
+ *
+ *   rows, V        rows of V fp32 logits (V <= 2^20)
+ *   in  [rows][V]  fp32 logits (-inf allowed: probability 0)
+ *   out [rows][V]  fp32, may be the same array as in
+ *   temperature    T > 0; the scaled logit is the fp32 product l * fp32(1/T)
+ *   top_k          keep the top_k largest scaled logits (ties: lower index
+ *                  first); 0, or at least the number of finite entries, keeps all
+ *   top_p          in (0, 1]: then keep the smallest set of largest
+ *                  probabilities (ties: lower index first) whose mass reaches
+ *                  top_p times the mass top-k kept; 1 keeps all
+ *   out_kind       TV_OUT_LOGITS: the scaled logit where kept, -inf elsewhere
+ *                  (a softmax of the row is the transformed distribution, so
+ *                  it can go straight to tree_verify_greedy / tree_verify_mss);
+ *                  TV_OUT_PROBS: the kept probabilities normalised to sum 1, 0
+ *                  elsewhere (for draft rows, ssm_probs)
+ * A row whose scaled logits hold a NaN or +inf, or no finite value, becomes
+ * all NaN (verification then reports TV_REQ_NONFINITE if it reads the row).
+ * The kept set is exact: the top-p cut compares sums of per-entry masses held
+ * in 2^-32 fixed point, so a cut within about 1e-9 of the target may fall on
+ * the other entry than an exact computation.  Work: one workgroup per row.
+ * Errors: TV_EINVAL for rows < 0, V outside [1, 2^20], T not finite and > 0,
+ * top_k < 0, top_p outside (0, 1], an unknown out_kind or a null pointer;
+ * TV_EHIP if the launch fails.  rows = 0 launches nothing.
+ */
+enum { TV_OUT_LOGITS = 0, TV_OUT_PROBS = 1 };
+tv_status tree_logits_transform(int rows, int V, const float* in, float* out, float temperature,
+                                int top_k, float top_p, int out_kind, hipStream_t stream);
+
 const char* tv_status_string(tv_status s);
 
 #ifdef __cplusplus

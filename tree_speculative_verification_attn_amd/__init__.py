@@ -14,14 +14,16 @@ __all__ = [
     "TreeVerifyError", "lib", "lib_path", "TV_F32", "TV_BF16", "EXPORTS",
     "tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
     "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss", "kv_commit_accepted",
-    "tv_status_string",
+    "tree_logits_transform", "TV_OUT_LOGITS", "TV_OUT_PROBS", "tv_status_string",
 ]
 
 TV_F32 = 0
 TV_BF16 = 1
+TV_OUT_LOGITS = 0
+TV_OUT_PROBS = 1
 EXPORTS = ("tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
            "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss",
-           "kv_commit_accepted", "tv_status_string")
+           "kv_commit_accepted", "tree_logits_transform", "tv_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libtreeverify.so")
@@ -45,6 +47,7 @@ def _load():
         "tree_verify_greedy": ([I, I, I, P, P, P, P, P, P, P, P, SZ, P], I),
         "tree_verify_mss": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ, P], I),
         "kv_commit_accepted": ([I, I, I, I, I, P, P, I, I, P, I, P, P, P, P, P], I),
+        "tree_logits_transform": ([I, I, P, P, F, I, F, I, P], I),
         "tv_status_string": ([I], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -152,3 +155,13 @@ def kv_commit_accepted(k_cache, v_cache, block_table, prefix_len, accepted, num_
                                   bs, _ptr(block_table), block_table.shape[1], _ptr(prefix_len),
                                   _ptr(accepted), _ptr(num_accepted), _ptr(status), _stream(stream)),
            "kv_commit_accepted")
+
+
+def tree_logits_transform(logits, out, temperature=1.0, top_k=0, top_p=1.0, kind=TV_OUT_LOGITS,
+                          stream=None):
+    """logits / out: fp32 [..., V] (out may be logits itself); every row is transformed."""
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V else 0
+    _check(lib().tree_logits_transform(rows, V, _ptr(logits), _ptr(out), float(temperature), int(top_k),
+                                       float(top_p), int(kind), _stream(stream)),
+           "tree_logits_transform")

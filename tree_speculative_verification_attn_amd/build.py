@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtreeverify.so")
-SOURCES = ["mask.hip", "attn.hip", "verify.hip", "commit.hip"]
+SOURCES = ["mask.hip", "attn.hip", "verify.hip", "commit.hip", "sample.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

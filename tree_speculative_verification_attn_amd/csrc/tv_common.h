@@ -79,10 +79,13 @@ __device__ __forceinline__ int pick_index(uint32_t w, int m) {
 // carried as y + err (y = fp32 product, err = its rounding error plus the
 // low part of log2e) and 2^err ~ 1 + err*ln2 corrects the hardware exp2 of y.
 // Accurate to a couple of ulp for x <= 0, which is all this library needs.
+// Arguments below -200 give 0 (fp32 exp underflows long before), which also
+// keeps the split product finite for arguments near -FLT_MAX.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float exp_acc(float x) {
   const float L2E_HI = 1.44269502162933349609375f;        // fp32(log2 e)
   const float L2E_LO = 1.925963033500011079e-8f;          // log2 e - L2E_HI
+  x = fmaxf(x, -200.f);
   const float y = x * L2E_HI;
   const float err = fmaf(x, L2E_HI, -y) + x * L2E_LO;
   const float e = __builtin_amdgcn_exp2f(y);
