@@ -208,6 +208,7 @@ def main():
     t_mss = per_call_ms(lambda c: tv.tree_verify_mss(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset,
                                                      m_acc, m_num, m_bonus, m_rounds, ws_v))
     assert int((status != 0).sum()) == 0, "a request failed during the benchmark"
+    variants = verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status, ws_v, t_mss)
     a_bytes = attn_bytes(w)
     l_bytes = logit_bytes(w)
     attn_gbs = a_bytes / (t_attn * 1e-3) / 1e9
@@ -243,10 +244,48 @@ def main():
                 "tree_attn_plus_mss_tokens_per_s": round(B * N / ((t_attn + t_mss) * 1e-3), 1),
                 "mean_tokens_emitted_per_request": round(acc_tokens, 3)},
     }
+    res["verify_variants"] = variants
     res["tree_vs_sequence"] = tree_vs_sequence(torch, tv, w, copies, bt, t_attn, stream)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, value)
     print(json.dumps(res))
+
+
+def verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status, ws_v, t_mss):
+    """The Table 3 analogue on this synthetic workload (SpecInfer summary,
+    Theorem 4.3 and Table 3: MSS against naive sampling, tokens per step), the
+    greedy rule beside them, and the cost of a sampling transform of every
+    target row (temperature 0.8, top-k 50, top-p 0.9)."""
+    dev = "cuda:0"
+    B, N = w.B, w.N
+    acc = torch.empty((B, N), dtype=torch.int32, device=dev)
+    num = torch.empty((B,), dtype=torch.int32, device=dev)
+    bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    rounds = torch.empty((B,), dtype=torch.int32, device=dev)
+    reps = 64
+    tokens = {"mss": 0.0, "naive": 0.0, "greedy": 0.0}
+    for i in range(reps):                 # fresh random streams: offsets 1000 + i
+        c = copies[i % len(copies)]
+        tv.tree_verify_mss(c["tl"], c["sp"], qr, token, child, status, w.seed, 1000 + i, acc, num, bonus,
+                           rounds, ws_v)
+        tokens["mss"] += float((num.clamp(min=0) + 1).float().mean())
+        tv.tree_verify_naive(c["tl"], token, child, status, w.seed, 1000 + i, acc, num, bonus, ws_v)
+        tokens["naive"] += float((num.clamp(min=0) + 1).float().mean())
+    tv.tree_verify_greedy(copies[0]["tl"], token, child, status, acc, num, bonus, ws_v)
+    tokens["greedy"] = float((num.clamp(min=0) + 1).float().mean()) * reps
+    t_naive = per_call_ms(lambda c: tv.tree_verify_naive(c["tl"], token, child, status, w.seed, w.offset,
+                                                         acc, num, bonus, ws_v))
+    t_greedy = per_call_ms(lambda c: tv.tree_verify_greedy(c["tl"], token, child, status, acc, num, bonus, ws_v))
+    scratch = torch.empty_like(copies[0]["tl"])
+    t_tf = per_call_ms(lambda c: tv.tree_logits_transform(c["tl"], scratch, 0.8, 50, 0.9, tv.TV_OUT_LOGITS))
+    assert int((status != 0).sum()) == 0, "a request failed in the verify variants"
+    return {"tokens_per_step": {k: round(v / reps, 4) for k, v in tokens.items()},
+            "mss_over_naive": round(tokens["mss"] / tokens["naive"], 4),
+            "ms_per_launch": {"mss": round(t_mss, 5), "naive": round(t_naive, 5), "greedy": round(t_greedy, 5)},
+            "sampling_transform_ms": round(t_tf, 5),
+            "sampling_transform": f"tree_logits_transform of all {B * (N + 1)} target rows, T 0.8, top-k 50, top-p 0.9",
+            "note": "synthetic rows (draft = target + noise); tokens per step = accepted + bonus, mean over "
+                    f"{reps} random streams"}
 
 
 def compare_sequence_all(torch, cfgs):

@@ -234,6 +234,25 @@ tv_status kv_commit_accepted(tv_dtype dt, int B, int N, int H, int D, void* k_ca
 
 /* Human-readable name of a tv_status value (static storage). */
 /*
+ * tree_verify_naive - naive sampling verification (the comparator of
+ * SpecInfer's Theorem 4.3; Table 3 compares it with MSS).
+ * Defines: SpecInfer summary, "Token Verification" (the naive approach and
+ * Theorem 4.3): at the current node u draw x from P_LLM(.|u); if a child of u
+ * carries token x, accept the lowest such child and continue from it;
+ * otherwise x is the bonus token and the walk stops.  Every emitted token is
+ * distributed as P_LLM given the tokens before it, but fewer tokens are
+ * accepted than with MSS.  The draw is the inverse-CDF sample of
+ * tree_verify_mss's final step with word 2 of round 0 at u's slot.
+ *
+ * Arguments, outputs, status handling and workspace as tree_verify_greedy,
+ * plus seed and offset as tree_verify_mss.  Same errors as tree_verify_greedy.
+ */
+tv_status tree_verify_naive(int B, int N, int V, const float* target_logits, const int32_t* token,
+                            const uint64_t* child, int32_t* status, uint64_t seed, uint64_t offset,
+                            int32_t* accepted, int32_t* num_accepted, int32_t* bonus,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * tree_logits_transform - sampling transforms of rows of logits, applied
  * before verification.
  * Defines: wiki concept page "Speculative decoding", "Implementation sketch":

@@ -88,6 +88,16 @@ class GpuRun:
                            self.m_acc, self.m_num, self.m_bonus, self.m_rounds, self._ws_verify())
         return self
 
+    def naive(self, seed=None, offset=None):
+        w = self.w
+        self.n_acc = torch.empty((w.B, w.N), dtype=torch.int32, device=DEV)
+        self.n_num = torch.empty((w.B,), dtype=torch.int32, device=DEV)
+        self.n_bonus = torch.empty((w.B,), dtype=torch.int32, device=DEV)
+        tv.tree_verify_naive(self.tl, self.token, self.child, self.status,
+                             w.seed if seed is None else seed, w.offset if offset is None else offset,
+                             self.n_acc, self.n_num, self.n_bonus, self._ws_verify())
+        return self
+
     def commit(self, accepted, num_accepted):
         tv.kv_commit_accepted(self.k, self.v, self.bt, self.pl, accepted, num_accepted, self.status)
         return self
@@ -132,9 +142,27 @@ def compare_mss(run, ref):
     return exact, excused, bad
 
 
+def compare_naive(run, ref):
+    """Naive verification against the oracle: exact, except requests whose
+    oracle trace holds a draw within 1e-6 of a cumulative-mass boundary.
+    Returns (n_exact, n_near_tie_excused, list of unexcused request ids)."""
+    acc, num, bonus, st = (t.cpu().numpy() for t in (run.n_acc, run.n_num, run.n_bonus, run.status))
+    exact = excused = 0
+    bad = []
+    for b in range(len(num)):
+        if (num[b] == ref["num_accepted"][b] and bonus[b] == ref["bonus"][b] and st[b] == ref["status"][b]
+                and np.array_equal(acc[b], ref["accepted"][b])):
+            exact += 1
+        elif ref["traces"][b] and min(m for _, m in ref["traces"][b]) < 1e-6:
+            excused += 1
+        else:
+            bad.append(b)
+    return exact, excused, bad
+
+
 def oracle_masks(w):
     return o_tree.build_mask_batch(w.parent)
 
 
-__all__ = ["GpuRun", "to_dev", "u64", "compare_mss", "bf16_tol_check", "out_to_f64", "oracle_masks",
+__all__ = ["GpuRun", "to_dev", "u64", "compare_mss", "compare_naive", "bf16_tol_check", "out_to_f64", "oracle_masks",
            "o_attn", "o_commit", "o_tree", "o_verify", "DEV"]

@@ -80,6 +80,35 @@ def test_mss_samples_target_distribution():
     assert 0.5 * np.abs(q1 - exact.sum(1)).sum() > 5 * max(ref)
 
 
+def test_naive_is_unbiased_and_mss_accepts_more():
+    """Naive sampling (draw, then look for the token; the drawn token is
+    emitted on a miss) also samples the target, and MSS accepts more tokens
+    per iteration on the same trees (Theorem 4.3, Table 3's comparison)."""
+    print("[case] loop naive vs MSS", flush=True)
+    dl, model, drafter = _setup(8, seed=11, noise=1.0)
+    prompt_row = torch.tensor([1, 5, 2])
+    exact = dl.continuation_probs(model, prompt_row.cuda(), 2)
+    per_iter = {}
+    for mode in ("naive", "mss"):
+        counts = np.zeros((8, 8))
+        n = acc = iters = 0
+        for rep in range(2):
+            B = 8192
+            dec = dl.SpecDecoder(model, drafter, B, mode=mode, tree=("expand", (2, 2)), seed=300 + rep,
+                                 draft_seed=400 + rep)
+            dec.prefill(prompt_row[None, :].repeat(B, 1).cuda())
+            out = np.array(dec.generate(2))
+            np.add.at(counts, (out[:, 0], out[:, 1]), 1)
+            n += B
+            acc += dec.accepted_total
+            iters += dec.iters * B
+        tv_ = 0.5 * np.abs(counts / n - exact).sum()
+        per_iter[mode] = (acc + iters) / iters
+        print(f"{mode}: TV {tv_:.4f}, {per_iter[mode]:.3f} tokens per request per iteration")
+        assert tv_ < 0.025
+    assert per_iter["mss"] > per_iter["naive"]
+
+
 @pytest.mark.parametrize("mode,dtype", [("mss", torch.float32), ("greedy", torch.bfloat16)])
 def test_cache_holds_committed_tokens(mode, dtype):
     print(f"[case] loop cache {mode} {dtype}", flush=True)

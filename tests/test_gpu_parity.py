@@ -17,8 +17,8 @@ from tests.golden.load import read_mask_fixture
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from tests.gpu_util import (GpuRun, compare_mss, o_attn, o_commit, o_tree, o_verify, out_to_f64,
-                                to_dev, u64)
+    from tests.gpu_util import (GpuRun, compare_mss, compare_naive, o_attn, o_commit, o_tree, o_verify,
+                                out_to_f64, to_dev, u64)
 
 TOL = {"bf16": (2e-2, 2e-2), "f32": (1e-5, 1e-5)}
 
@@ -366,6 +366,88 @@ def test_verify_many_requests(V):
     ref = _check_mss(run, "many requests")
     assert int(run.ws_v.count_nonzero()) == 0
     assert (ref["status"] == 0).all()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_naive_small(name):
+    _print_case("naive", name)
+    w = _small(name)
+    run = GpuRun(w).mask().naive()
+    torch.cuda.synchronize()
+    ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [0] * w.B, w.seed, w.offset)
+    ex, excused, bad = compare_naive(run, ref)
+    print(f"{name}: naive exact {ex}, near-tie {excused}")
+    assert not bad
+
+
+@pytest.mark.parametrize("V", [8, 4097, 16384, 16385, 40000, 33001])
+def test_naive_both_kernels(V):
+    # one workgroup per request up to V = 16384, sliced rows above; peaked
+    # target rows make the draws hit tree tokens, so walks go deep
+    for cfg, kw in ((2, dict(B=3, L=20, H=1)), (4, dict(B=2, H=1))):
+        w = synth.make_workload(cfg, V=V, **kw)
+        tl = w.target_logits.copy()
+        for b in range(w.B):
+            for i in range(w.N):         # node i's row favours its first child's token
+                kids = [c for c in range(w.N) if w.parent[b, c] == i]
+                if kids:
+                    tl[b, i + 1, w.token[b, kids[0]]] += 12.0
+            roots = [c for c in range(w.N) if w.parent[b, c] == -1]
+            tl[b, 0, w.token[b, roots[0]]] += 12.0
+        w.target_logits = tl
+        _print_case("naive", cfg, V)
+        run = GpuRun(w).mask().naive(offset=7)
+        torch.cuda.synchronize()
+        ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [0] * w.B, w.seed, 7)
+        ex, excused, bad = compare_naive(run, ref)
+        print(f"naive cfg{cfg} V={V}: exact {ex}, near-tie {excused}, accepted {run.n_num.cpu().numpy().tolist()}")
+        assert not bad
+        assert int(run.n_num.max()) >= 2
+        assert int(run.ws_v.count_nonzero()) == 0
+
+
+def test_naive_status_and_rejection_rate():
+    w = synth.make_workload(2, B=6, L=20, H=1, V=500)
+    tok = w.token.copy()
+    tl = w.target_logits.copy()
+    tok[1, 3] = w.V                 # bad token
+    tl[3, 0, 17] = np.nan
+    tl[4, 0, :] = -np.inf
+    w.token, w.target_logits = tok, tl
+    run = GpuRun(w).mask()
+    run.status[0] = 1
+    run.naive()
+    torch.cuda.synchronize()
+    ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [1, 0, 0, 0, 0, 0], w.seed, w.offset)
+    assert list(run.status.cpu().numpy()) == list(ref["status"])
+    ex, excused, bad = compare_naive(run, ref)
+    assert not bad
+    # Theorem 4.3's naive comparator: root rejection rate 1 - (mass of the
+    # distinct root-child tokens), over many requests with their own streams
+    from tests.test_gpu_distribution import P8, Q8
+    p = np.array([float(x) for x in P8])
+    q = np.array([float(x) for x in Q8])
+    parent, tok, tl, sp, qr = synth.iid_tree_batch(4243, 200_000, p, q, "star3")
+    n = tok.shape[0]
+    par = torch.from_numpy(np.tile(parent, (n, 1))).cuda()
+    anc = torch.zeros((n, 3), dtype=torch.int64, device="cuda:0")
+    child = torch.zeros((n, 4), dtype=torch.int64, device="cuda:0")
+    depth = torch.zeros((n, 3), dtype=torch.int32, device="cuda:0")
+    st = torch.zeros((n,), dtype=torch.int32, device="cuda:0")
+    import tree_speculative_verification_attn_amd as tv
+    tv.tree_build_mask(par, anc, child, depth, st)
+    acc = torch.empty((n, 3), dtype=torch.int32, device="cuda:0")
+    num = torch.empty((n,), dtype=torch.int32, device="cuda:0")
+    bonus = torch.empty((n,), dtype=torch.int32, device="cuda:0")
+    ws = torch.zeros(tv.tree_verify_workspace(n, 3, 8), dtype=torch.uint8, device="cuda:0")
+    tv.tree_verify_naive(torch.from_numpy(tl).cuda(), torch.from_numpy(tok).cuda(), child, st, 3, 0,
+                         acc, num, bonus, ws)
+    torch.cuda.synchronize()
+    num = num.cpu().numpy()
+    want = np.mean([o_verify.naive_reject_prob(p, row) for row in tok])
+    got = np.mean(num == 0)
+    print(f"naive root rejection {got:.4f}, closed form {want:.4f}")
+    assert abs(got - want) < 4 * np.sqrt(want * (1 - want) / n)
 
 
 # ----------------------------------------------------------------------------

@@ -14,7 +14,7 @@ __all__ = [
     "TreeVerifyError", "lib", "lib_path", "TV_F32", "TV_BF16", "EXPORTS",
     "tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
     "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss", "kv_commit_accepted",
-    "tree_logits_transform", "TV_OUT_LOGITS", "TV_OUT_PROBS", "tv_status_string",
+    "tree_verify_naive", "tree_logits_transform", "TV_OUT_LOGITS", "TV_OUT_PROBS", "tv_status_string",
 ]
 
 TV_F32 = 0
@@ -23,7 +23,7 @@ TV_OUT_LOGITS = 0
 TV_OUT_PROBS = 1
 EXPORTS = ("tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
            "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss",
-           "kv_commit_accepted", "tree_logits_transform", "tv_status_string")
+           "kv_commit_accepted", "tree_verify_naive", "tree_logits_transform", "tv_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libtreeverify.so")
@@ -48,6 +48,7 @@ def _load():
         "tree_verify_mss": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ, P], I),
         "kv_commit_accepted": ([I, I, I, I, I, P, P, I, I, P, I, P, P, P, P, P], I),
         "tree_logits_transform": ([I, I, P, P, F, I, F, I, P], I),
+        "tree_verify_naive": ([I, I, I, P, P, P, P, U64, U64, P, P, P, P, SZ, P], I),
         "tv_status_string": ([I], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -145,6 +146,16 @@ def tree_verify_mss(target_logits, ssm_probs, q_row, token, child, status, seed,
                                _ptr(token), _ptr(child), _ptr(status), int(seed), int(offset),
                                _ptr(accepted), _ptr(num_accepted), _ptr(bonus), _ptr(rounds),
                                _ptr(workspace), ws_bytes, _stream(stream)), "tree_verify_mss")
+
+
+def tree_verify_naive(target_logits, token, child, status, seed, offset, accepted, num_accepted, bonus,
+                      workspace, stream=None):
+    B, N1, V = target_logits.shape
+    N = N1 - 1
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().tree_verify_naive(B, N, V, _ptr(target_logits), _ptr(token), _ptr(child), _ptr(status),
+                                   int(seed), int(offset), _ptr(accepted), _ptr(num_accepted), _ptr(bonus),
+                                   _ptr(workspace), ws_bytes, _stream(stream)), "tree_verify_naive")
 
 
 def kv_commit_accepted(k_cache, v_cache, block_table, prefix_len, accepted, num_accepted, status,

@@ -52,8 +52,8 @@ constexpr int kHdr = 4;                            // header words per workgroup
 constexpr unsigned kSpinLimit = 1u << 22;          // polls of one word before giving up
 
 enum : int { FLAG_NAN = 1, FLAG_PINF = 2, FLAG_FINITE = 4 };
-enum : int { MODE_GREEDY = 0, MODE_MSS = 1 };
-enum : int { P_ENTER = 0, P_RESID = 1, P_FINAL = 2, P_DONE = 3 };
+enum : int { MODE_GREEDY = 0, MODE_MSS = 1, MODE_NAIVE = 2 };
+enum : int { P_ENTER = 0, P_RESID = 1, P_NSAMPLE = 2, P_FINAL = 3, P_DONE = 4 };   // passes of the walk
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -200,6 +200,7 @@ __device__ __forceinline__ bool q_bad(float q) { return !(q >= 0.f) || q == INFI
 // walk state lives in registers and a pass needs no barrier beyond those of
 // its workgroup reductions.
 // ---------------------------------------------------------------------------
+template <int MODE>
 __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   constexpr int NW = kCoThreads / 64;
   const int G = a.G;
@@ -207,7 +208,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   const int g = static_cast<int>(blockIdx.x) % G;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int N = a.N, V = a.V;
-  const bool mss = a.mode == MODE_MSS;
+  constexpr bool mss = MODE == MODE_MSS, naive = MODE == MODE_NAIVE;
+  constexpr bool need_z = mss || naive;               // the walk needs the normaliser
   const int xa = g * kSlice + t * kElem;              // first entry of this thread
   const int nx = max(0, min(kElem, V - xa));          // entries it owns
   const float* lbase = a.logits + static_cast<size_t>(b) * (N + 1) * V;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   __shared__ float s_rx2[2][TV_MAX_NODES];
   __shared__ double s_gt[NW][kMaxG];             // slice totals of the current distribution (per wave)
   __shared__ double s_scan[NW];
-  __shared__ int s_status0, s_timeout, s_found, s_last;
+  __shared__ int s_status0, s_timeout, s_found, s_last, s_xs;
   __shared__ float own_s[kElem];
 
   static_assert(kElem % 4 == 0 || kElem < 4, "entries per thread");
@@ -296,9 +298,133 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
 
   int ex_no = 0;                // exchanges done
   int rs_no = 0;                // workgroup sums done (bank parity)
-  int pre = 0;                  // greedy: the entered node's row is in lvn (1), qn (2), or not loaded (0)
+  int pre = 0;                  // greedy/naive: the entered node's row is in lvn (1), qn (2), or not loaded (0)
+  int c1 = -1, c2 = -1;         // greedy/naive: the children whose rows are prefetched
+
+  // The slice holding u2 * total, from the slice totals in index order, and
+  // the threshold inside it (every wave, same values).
+  auto locate = [&](uint32_t word) {
+    double run = 0.0;
+    for (int base = 0; base < G; base += 64) {     // the same sums as the search below
+      const double v = base + lane < G ? s_gt[wave][base + lane] : 0.0;
+      double ex;
+      run = tv::readlane_f64(run + tv::wave_scan_dpp(v, &ex), 63);
+    }
+    const double T = tv::unit_open0(word) * run;
+    double carry = 0.0, ex_owner = 0.0, ex_last = 0.0;
+    int last = -1;
+    owner = -1;
+    for (int base = 0; base < G && owner < 0; base += 64) {
+      const double v = base + lane < G ? s_gt[wave][base + lane] : 0.0;
+      double excl;
+      const double incl = carry + tv::wave_scan_dpp(v, &excl);
+      excl += carry;
+      const uint64_t hit = __ballot(v > 0.0 && excl < T && incl >= T);
+      const uint64_t pos = __ballot(v > 0.0);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        owner = base + l;
+        ex_owner = tv::readlane_f64(excl, l);
+      } else if (pos) {
+        const int l = 63 - __builtin_clzll(pos);
+        last = base + l;
+        ex_last = tv::readlane_f64(excl, l);
+      }
+      carry = tv::readlane_f64(incl, 63);
+    }
+    if (owner < 0) {       // rounding left the total short: last non-empty slice
+      owner = last;
+      ex_owner = ex_last;
+    }
+    Tloc = fmax(T - ex_owner, 1e-300);
+  };
+
+  // The owner slice's workgroup finds the sampled token (all its threads
+  // call this; every thread gets the token).
+  auto slice_search = [&]() -> int {
+    float (&cur)[kElem] = rn;          // the residual array is free during a draw
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < kElem; ++e) {
+      cur[e] = e < nx ? (mode == 0 ? (lv[e] == -INFINITY ? 0.f : tv::exp_acc(lv[e] - m)) : cv[e]) : 0.f;
+      part += static_cast<double>(cur[e]);
+    }
+    double wexcl;
+    const double wincl = tv::wave_scan_dpp(part, &wexcl);
+    if (lane == 63) s_scan[wave] = wincl;
+    if (t == 0) s_found = -1;
+    __syncthreads();
+    double wbase = 0.0, total = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      if (w2 < wave) wbase += s_scan[w2];
+      total += s_scan[w2];
+    }
+    const double incl = wbase + wincl;
+    const double excl = wbase + wexcl;     // the previous thread's incl, bit for bit (wexcl = 0 in lane 0)
+    // threshold in (0, slice total]: exactly one thread has excl < T <= incl
+    const double T = fmin(Tloc, total);
+    if (excl < T && incl >= T) {
+#pragma unroll
+      for (int e = 0; e < kElem; ++e) own_s[e] = cur[e];
+      double accd = excl;
+      int xs = -1, last_pos = -1;
+      for (int e = 0; e < nx; ++e) {
+        const float c = own_s[e];
+        if (c > 0.f) last_pos = xa + e;
+        accd += static_cast<double>(c);
+        if (accd >= T) {
+          xs = xa + e;
+          break;
+        }
+      }
+      s_found = xs >= 0 ? xs : last_pos;   // rounding left the chunk short: last positive entry
+    }
+    __syncthreads();
+    return s_found;
+  };
+
   for (;;) {
     if (status != TV_REQ_OK || pass >= P_FINAL || timed_out) break;
+    if (naive && pass == P_NSAMPLE) {
+      // ---- naive: the owner slice draws the token, every workgroup takes it ----
+      const uint32_t tag = static_cast<uint32_t>(ex_no + 1);
+      const int par = ex_no & 1;
+      if (g == owner) {
+        const int x = slice_search();
+        if (t == 0) put_tagged(kid + par * 64, tag, static_cast<uint32_t>(x));
+      }
+      if (wave == 0) {
+        bool to = false;
+        if (lane == 0) {
+          uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
+          if (!take_tagged<1>(kid + par * 64, tag, v)) to = true;
+          s_xs = static_cast<int>(v[0]);
+        }
+        if (__any(to) && lane == 0) s_timeout = 1;
+      }
+      __syncthreads();
+      ++ex_no;
+      if (s_timeout) {
+        timed_out = true;
+        break;
+      }
+      const int x = s_xs;
+      const uint64_t hit = __ballot(lane < N && ((U >> lane) & 1ull) && s_tok[lane] == x);
+      if (!hit) {
+        bonus = x;
+        pass = P_DONE;
+        continue;
+      }
+      const int nxt = __builtin_ctzll(hit);
+      if (t == 0) s_acc[k] = nxt;
+      ++k;
+      u = nxt;
+      U = s_child[nxt + 1];
+      pre = nxt == c1 ? 1 : (nxt == c2 ? 2 : 0);
+      pass = P_ENTER;
+      continue;
+    }
     if (pass == P_RESID) {
 #pragma unroll
       for (int e = 0; e < kElem; ++e) qv[e] = qn[e];
@@ -315,8 +441,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         load8(lrow, lv);
       }
     }
-    // greedy: the rows of the first two children, in case the walk enters one
-    int c1 = -1, c2 = -1;
+    // greedy/naive: the rows of the first two children, in case the walk enters one
+    if (!mss && pass == P_ENTER) c1 = c2 = -1;
     if (!mss && pass == P_ENTER && U) {
       c1 = __builtin_ctzll(U);
       load8(lbase + static_cast<size_t>(c1 + 1) * V, lvn);
@@ -376,7 +502,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         F |= s_wf[par][w2];
       }
       double S = 0.0;
-      if (mss && M != -INFINITY && M == M && M != INFINITY) {
+      if (need_z && M != -INFINITY && M == M && M != INFINITY) {
         double acc = 0.0;
 #pragma unroll
         for (int e = 0; e < kElem; ++e)
@@ -482,7 +608,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       tv::wave_argmax_dpp(mm, am);
       fl = tv::wave_or_dpp(fl);
       fail = (fl & (FLAG_NAN | FLAG_PINF)) || !(fl & FLAG_FINITE);
-      if (!fail && !mss) {
+      if (!fail && MODE == MODE_GREEDY) {
         // greedy: the child whose token is the argmax, lowest node first
         const uint64_t hit = __ballot(lane < N && ((U >> lane) & 1ull) && s_tok[lane] == am);
         if (hit) {
@@ -529,8 +655,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     }
     if (fail) {
       status = TV_REQ_NONFINITE;
-    } else if (mss) {
-      if (cand >= 0) {
+    } else if (mss && cand >= 0) {   // (cand >= 0 only in MSS)
+      {
         // ratio test: u1 <= p(x) / q(x) with p(x) = e / Z, tested as
         // u1 * q(x) * Z <= e (no division); q(x) = 0 accepts exactly when p(x) > 0
         if (q_bad(qx_c)) {
@@ -553,95 +679,24 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
             pass = P_RESID;
           }
         }
-      } else {
-        // no child left: the slice holding u2 * total, from the slice
-        // totals in index order, and the threshold inside it
-        const tv::u32x4 w0 = tv::mss_words(a.seed, a.offset, b, u + 1, 0);
-        double run = 0.0;
-        for (int base = 0; base < G; base += 64) {     // the same sums as the search below
-          const double v = base + lane < G ? s_gt[wave][base + lane] : 0.0;
-          double ex;
-          run = tv::readlane_f64(run + tv::wave_scan_dpp(v, &ex), 63);
-        }
-        const double T = tv::unit_open0(w0.z) * run;
-        double carry = 0.0, ex_owner = 0.0, ex_last = 0.0;
-        int last = -1;
-        owner = -1;
-        for (int base = 0; base < G && owner < 0; base += 64) {
-          const double v = base + lane < G ? s_gt[wave][base + lane] : 0.0;
-          double excl;
-          const double incl = carry + tv::wave_scan_dpp(v, &excl);
-          excl += carry;
-          const uint64_t hit = __ballot(v > 0.0 && excl < T && incl >= T);
-          const uint64_t pos = __ballot(v > 0.0);
-          if (hit) {
-            const int l = __builtin_ctzll(hit);
-            owner = base + l;
-            ex_owner = tv::readlane_f64(excl, l);
-          } else if (pos) {
-            const int l = 63 - __builtin_clzll(pos);
-            last = base + l;
-            ex_last = tv::readlane_f64(excl, l);
-          }
-          carry = tv::readlane_f64(incl, 63);
-        }
-        if (owner < 0) {       // rounding left the total short: last non-empty slice
-          owner = last;
-          ex_owner = ex_last;
-        }
-        Tloc = fmax(T - ex_owner, 1e-300);
-        pass = P_FINAL;
       }
+    } else if (need_z) {
+      // MSS with no child left, or naive having entered u: locate the slice
+      // of the draw (the next pass makes it)
+      locate(tv::mss_words(a.seed, a.offset, b, u + 1, 0).z);
+      pass = mss ? P_FINAL : P_NSAMPLE;
     }
   }
   __syncthreads();
   const bool ok = status == TV_REQ_OK && !s_timeout;
 
-  // ---- final sample: the owner slice's workgroup finds the token ----
-  if (ok && pass == P_FINAL && g == owner) {
-    float cur[kElem];
-    double part = 0.0;
-#pragma unroll
-    for (int e = 0; e < kElem; ++e) {
-      cur[e] = e < nx ? (mode == 0 ? (lv[e] == -INFINITY ? 0.f : tv::exp_acc(lv[e] - m)) : cv[e]) : 0.f;
-      part += static_cast<double>(cur[e]);
-    }
-    double wexcl;
-    const double wincl = tv::wave_scan_dpp(part, &wexcl);
-    if (lane == 63) s_scan[wave] = wincl;
-    if (t == 0) s_found = -1;
-    __syncthreads();
-    double wbase = 0.0, total = 0.0;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) {
-      if (w2 < wave) wbase += s_scan[w2];
-      total += s_scan[w2];
-    }
-    const double incl = wbase + wincl;
-    const double excl = wbase + wexcl;     // the previous thread's incl, bit for bit (wexcl = 0 in lane 0)
-    // threshold in (0, slice total]: exactly one thread has excl < T <= incl
-    const double T = fmin(Tloc, total);
-    if (excl < T && incl >= T) {
-#pragma unroll
-      for (int e = 0; e < kElem; ++e) own_s[e] = cur[e];
-      double accd = excl;
-      int xs = -1, last_pos = -1;
-      for (int e = 0; e < nx; ++e) {
-        const float c = own_s[e];
-        if (c > 0.f) last_pos = xa + e;
-        accd += static_cast<double>(c);
-        if (accd >= T) {
-          xs = xa + e;
-          break;
-        }
-      }
-      s_found = xs >= 0 ? xs : last_pos;   // rounding left the chunk short: last positive entry
-    }
-    __syncthreads();
-    if (t == 0) a.bonus[b] = s_found;
+  // ---- MSS's final sample: the owner slice's workgroup finds the token ----
+  if (mss && ok && pass == P_FINAL && g == owner) {
+    const int x = slice_search();
+    if (t == 0) a.bonus[b] = x;
   }
 
-  // ---- results: workgroup 0 writes the path (and the greedy bonus) ----
+  // ---- results: workgroup 0 writes the path (and the greedy / naive bonus) ----
   if (g == 0) {
     if (t == 0) {
       int stt = status;
@@ -709,14 +764,14 @@ constexpr int kRowWaves = kRowThreads / 64;
 constexpr int kRowQuad = 4 * kRowThreads;        // entries covered by one register quad
 constexpr int kRowMaxE = 32;                     // registers per row per thread
 
-template <int E, bool VEC>
+template <int E, bool VEC, int MODE>
 __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
   static_assert(E % 4 == 0 && E <= kRowMaxE, "row registers");
   constexpr int C = E / 4;
   const int b = a.b0 + static_cast<int>(blockIdx.x);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int N = a.N, V = a.V;
-  const bool mss = a.mode == MODE_MSS;
+  constexpr bool mss = MODE == MODE_MSS, naive = MODE == MODE_NAIVE;
   const float* lbase = a.logits + static_cast<size_t>(b) * (N + 1) * V;
   const float* sbase = mss ? a.ssm + static_cast<size_t>(b) * a.R * V : nullptr;
 
@@ -925,16 +980,149 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
   double Z = 1.0;
   bool final_sample = false;
 
-  if (status == TV_REQ_OK && !mss) {
-    // ---------------- greedy ----------------
-    int c1 = -1, c2 = -1;
-    auto fetch_children = [&]() {
-      c1 = U ? __builtin_ctzll(U) : -1;
-      const uint64_t rest = U & (U - 1);
-      c2 = rest ? __builtin_ctzll(rest) : -1;
-      if (c1 >= 0) load_row(lbase + static_cast<size_t>(c1 + 1) * V, qa, -INFINITY);
-      if (c2 >= 0) dma_row(lbase + static_cast<size_t>(c2 + 1) * V);
+  // ---- a sample of the current distribution: smallest x with cumsum >= u * total ----
+  // Cumulative sums run in x order: quad by quad, within a quad wave by wave,
+  // within a wave lane by lane (four entries per lane).  Every wave publishes
+  // its scanned total per quad; a scan over those totals (the same in every
+  // wave) finds the (quad, wave) whose range brackets the threshold, and only
+  // that wave repeats its lane scan (the same operations on the same values,
+  // so the same sums) to find the lane and the entry.  Inside one wave each
+  // inclusive sum equals the next lane's exclusive sum bit for bit, so with
+  // the threshold clamped to the wave's top exactly one lane brackets it.
+  auto sample_lv = [&](uint32_t word) -> int {
+    constexpr int K = C * kRowWaves;                 // (quad, wave) ranges
+    constexpr int NB = (K + 63) / 64;
+    auto quad_sum = [&](int i) {
+      double s = 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += static_cast<double>(lv[4 * i + r]);
+      return s;
     };
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      double ex;
+      const double inc = tv::wave_scan_dpp(quad_sum(i), &ex);
+      if (lane == 63) s_scan[i * kRowWaves + wave] = inc;
+    }
+    if (t == 0) s_found = -1;
+    __syncthreads();
+    // prefix sums over the ranges, 64 per batch (every wave alike)
+    double lo[NB], hi[NB], carry = 0.0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int kk = nb * 64 + lane;
+      const double v = kk < K ? s_scan[kk] : 0.0;
+      double ex;
+      const double in = tv::wave_scan_dpp(v, &ex);
+      lo[nb] = carry + ex;
+      hi[nb] = carry + in;
+      carry = tv::readlane_f64(hi[nb], 63);
+    }
+    const double T = tv::unit_open0(word) * carry;   // in (0, total]
+    int kstar = -1;
+    double Astar = 0.0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint64_t hit = __ballot(lo[nb] < T && hi[nb] >= T);
+      if (kstar < 0 && hit) {
+        const int l = __builtin_ctzll(hit);
+        kstar = nb * 64 + l;
+        Astar = tv::readlane_f64(lo[nb], l);
+      }
+    }
+    if (kstar < 0) {            // rounding left the total short: the last non-empty range
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint64_t pos = __ballot(hi[nb] > lo[nb]);
+        if (pos) {
+          const int l = 63 - __builtin_clzll(pos);
+          kstar = nb * 64 + l;
+          Astar = tv::readlane_f64(lo[nb], l);
+        }
+      }
+    }
+    const int qi = kstar / kRowWaves, qw = kstar % kRowWaves;
+    if (kstar >= 0 && wave == qw) {
+      double sq = 0.0;
+#pragma unroll
+      for (int i = 0; i < C; ++i)
+        if (i == qi) sq = quad_sum(i);
+      double exl;
+      const double inl = tv::wave_scan_dpp(sq, &exl);
+      const double Tw = fmin(T, Astar + tv::readlane_f64(inl, 63));
+      const double l0 = Astar + exl, l1 = Astar + inl;
+      if (l0 < Tw && l1 >= Tw) {
+        double accd = l0;
+        int xs = -1, last_pos = -1;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          if (i == qi) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float c = lv[4 * i + r];
+              if (xs < 0) {
+                if (c > 0.f) last_pos = xof(4 * i + r);
+                accd += static_cast<double>(c);
+                if (accd >= Tw) xs = xof(4 * i + r);
+              }
+            }
+          }
+        }
+        s_found = xs >= 0 ? xs : last_pos;   // rounding left the lane short: its last positive entry
+      }
+    }
+    __syncthreads();
+    return s_found;
+  };
+
+
+  // greedy and naive: the rows of the entered node's first two children
+  int c1 = -1, c2 = -1;
+  auto fetch_children = [&]() {
+    c1 = U ? __builtin_ctzll(U) : -1;
+    const uint64_t rest = U & (U - 1);
+    c2 = rest ? __builtin_ctzll(rest) : -1;
+    if (c1 >= 0) load_row(lbase + static_cast<size_t>(c1 + 1) * V, qa, -INFINITY);
+    if (c2 >= 0) dma_row(lbase + static_cast<size_t>(c2 + 1) * V);
+  };
+  auto enter_child = [&](int nxt) {
+    if (t == 0) s_acc[k] = nxt;
+    ++k;
+    u = nxt;
+    U = s_child[nxt + 1];
+    if (nxt == c1) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) lv[e] = qa[e];
+    } else if (nxt == c2) {
+      lds_row(lv, -INFINITY);
+    } else {
+      load_row(lbase + static_cast<size_t>(u + 1) * V, lv, -INFINITY);
+    }
+    fetch_children();
+  };
+
+  if (status == TV_REQ_OK && naive) {
+    // ---------------- naive sampling: draw, then look for the token ----------------
+    fetch_children();
+    for (;;) {
+      float M;
+      const int nan = block_max(lv, &M);
+      if (nan || M == INFINITY || M == -INFINITY) {
+        status = TV_REQ_NONFINITE;
+        break;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) lv[e] = lv[e] != -INFINITY ? tv::exp_acc(lv[e] - M) : 0.f;
+      const int x = sample_lv(tv::mss_words(a.seed, a.offset, b, u + 1, 0).z);
+      const uint64_t hit = __ballot(lane < N && ((U >> lane) & 1ull) && s_tok[lane] == x);
+      if (!hit) {
+        bonus = x;
+        break;
+      }
+      enter_child(__builtin_ctzll(hit));
+    }
+  } else if (status == TV_REQ_OK && !mss) {
+    // ---------------- greedy ----------------
     fetch_children();
     for (;;) {
       float M;
@@ -949,20 +1137,7 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
         bonus = A;
         break;
       }
-      const int nxt = __builtin_ctzll(hit);
-      if (t == 0) s_acc[k] = nxt;
-      ++k;
-      u = nxt;
-      U = s_child[nxt + 1];
-      if (nxt == c1) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) lv[e] = qa[e];
-      } else if (nxt == c2) {
-        lds_row(lv, -INFINITY);
-      } else {
-        load_row(lbase + static_cast<size_t>(u + 1) * V, lv, -INFINITY);
-      }
-      fetch_children();
+      enter_child(__builtin_ctzll(hit));
     }
   } else if (status == TV_REQ_OK) {
     // ---------------- MSS ----------------
@@ -1062,100 +1237,9 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
     }
   }
 
-  // ---------------- final sample: smallest x with cumsum >= u2 * total ----------------
-  // Cumulative sums run in x order: quad by quad, within a quad wave by wave,
-  // within a wave lane by lane (four entries per lane).  Every wave publishes
-  // its scanned total per quad; a scan over those totals (the same in every
-  // wave) finds the (quad, wave) whose range brackets the threshold, and only
-  // that wave repeats its lane scan (the same operations on the same values,
-  // so the same sums) to find the lane and the entry.  Inside one wave each
-  // inclusive sum equals the next lane's exclusive sum bit for bit, so with
-  // the threshold clamped to the wave's top exactly one lane brackets it.
   if (final_sample) {
-    constexpr int K = C * kRowWaves;                 // (quad, wave) ranges
-    constexpr int NB = (K + 63) / 64;
     const tv::u32x4 w0 = tv::mss_words(a.seed, a.offset, b, u + 1, 0);
-    auto quad_sum = [&](int i) {
-      double s = 0.0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s += static_cast<double>(lv[4 * i + r]);
-      return s;
-    };
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      double ex;
-      const double inc = tv::wave_scan_dpp(quad_sum(i), &ex);
-      if (lane == 63) s_scan[i * kRowWaves + wave] = inc;
-    }
-    if (t == 0) s_found = -1;
-    __syncthreads();
-    // prefix sums over the ranges, 64 per batch (every wave alike)
-    double lo[NB], hi[NB], carry = 0.0;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int kk = nb * 64 + lane;
-      const double v = kk < K ? s_scan[kk] : 0.0;
-      double ex;
-      const double in = tv::wave_scan_dpp(v, &ex);
-      lo[nb] = carry + ex;
-      hi[nb] = carry + in;
-      carry = tv::readlane_f64(hi[nb], 63);
-    }
-    const double T = tv::unit_open0(w0.z) * carry;   // in (0, total]
-    int kstar = -1;
-    double Astar = 0.0;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint64_t hit = __ballot(lo[nb] < T && hi[nb] >= T);
-      if (kstar < 0 && hit) {
-        const int l = __builtin_ctzll(hit);
-        kstar = nb * 64 + l;
-        Astar = tv::readlane_f64(lo[nb], l);
-      }
-    }
-    if (kstar < 0) {            // rounding left the total short: the last non-empty range
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const uint64_t pos = __ballot(hi[nb] > lo[nb]);
-        if (pos) {
-          const int l = 63 - __builtin_clzll(pos);
-          kstar = nb * 64 + l;
-          Astar = tv::readlane_f64(lo[nb], l);
-        }
-      }
-    }
-    const int qi = kstar / kRowWaves, qw = kstar % kRowWaves;
-    if (kstar >= 0 && wave == qw) {
-      double sq = 0.0;
-#pragma unroll
-      for (int i = 0; i < C; ++i)
-        if (i == qi) sq = quad_sum(i);
-      double exl;
-      const double inl = tv::wave_scan_dpp(sq, &exl);
-      const double Tw = fmin(T, Astar + tv::readlane_f64(inl, 63));
-      const double l0 = Astar + exl, l1 = Astar + inl;
-      if (l0 < Tw && l1 >= Tw) {
-        double accd = l0;
-        int xs = -1, last_pos = -1;
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-          if (i == qi) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float c = lv[4 * i + r];
-              if (xs < 0) {
-                if (c > 0.f) last_pos = xof(4 * i + r);
-                accd += static_cast<double>(c);
-                if (accd >= Tw) xs = xof(4 * i + r);
-              }
-            }
-          }
-        }
-        s_found = xs >= 0 ? xs : last_pos;   // rounding left the lane short: its last positive entry
-      }
-    }
-    __syncthreads();
-    bonus = s_found;
+    bonus = sample_lv(w0.z);
   }
 
   // ---------------- results ----------------
@@ -1186,26 +1270,47 @@ tv_status check_verify_args(int B, int N, int V) {
 }
 
 // Workgroups of the walk kernel that fit on the device at once (cached per
-// device: it depends only on the kernel and the device).
-int walk_capacity(int dev) {
-  static int cache[64];
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+// device and mode: it depends only on the kernel and the device).
+const void* walk_kernel_of(int mode) {
+  if (mode == MODE_MSS) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS>);
+  if (mode == MODE_NAIVE) return reinterpret_cast<const void*>(walk_kernel<MODE_NAIVE>);
+  return reinterpret_cast<const void*>(walk_kernel<MODE_GREEDY>);
+}
+
+int walk_capacity(int dev, int mode) {
+  static int cache[3][64];
+  const bool cached = dev >= 0 && dev < 64 && mode >= 0 && mode < 3;
+  if (cached && cache[mode][dev] > 0) return cache[mode][dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(walk_kernel),
-                                                   kCoThreads, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, walk_kernel_of(mode), kCoThreads, 0) != hipSuccess)
     return 0;
   const int cap = cus * std::max(1, per_cu);
-  if (dev >= 0 && dev < 64) cache[dev] = cap;
+  if (cached) cache[mode][dev] = cap;
   return cap;
 }
 
+void launch_sliced(const WalkArgs& a, int grid, hipStream_t stream) {
+  if (a.mode == MODE_MSS)
+    hipLaunchKernelGGL((walk_kernel<MODE_MSS>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+  else if (a.mode == MODE_NAIVE)
+    hipLaunchKernelGGL((walk_kernel<MODE_NAIVE>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((walk_kernel<MODE_GREEDY>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+}
+
+template <int E, int MODE>
+void launch_row_mode(const WalkArgs& a, int B, bool vec, hipStream_t stream) {
+  if (vec)
+    hipLaunchKernelGGL((walk_row_kernel<E, true, MODE>), dim3(B), dim3(kRowThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((walk_row_kernel<E, false, MODE>), dim3(B), dim3(kRowThreads), 0, stream, a);
+}
 template <int E>
 void launch_row(const WalkArgs& a, int B, bool vec, hipStream_t stream) {
-  if (vec)
-    hipLaunchKernelGGL((walk_row_kernel<E, true>), dim3(B), dim3(kRowThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((walk_row_kernel<E, false>), dim3(B), dim3(kRowThreads), 0, stream, a);
+  if (a.mode == MODE_MSS) launch_row_mode<E, MODE_MSS>(a, B, vec, stream);
+  else if (a.mode == MODE_NAIVE) launch_row_mode<E, MODE_NAIVE>(a, B, vec, stream);
+  else launch_row_mode<E, MODE_GREEDY>(a, B, vec, stream);
 }
 
 // Launch the walk in request batches whose workgroups all fit on the device
@@ -1222,21 +1327,16 @@ tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
     return tv::launch_status();
   }
   const int G = a.G;
-  if (G == 1) {          // a request's only workgroup waits on nobody else
-    a.b0 = 0;
-    hipLaunchKernelGGL(walk_kernel, dim3(B), dim3(kCoThreads), 0, stream, a);
-    return tv::launch_status();
-  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TV_EHIP;
-  const int capacity = walk_capacity(dev);
+  const int capacity = walk_capacity(dev, a.mode);
   if (capacity <= 0) return TV_EHIP;
   if (G > capacity) return TV_EINVAL;
   const int per_launch = capacity / G;
   for (int b0 = 0; b0 < B; b0 += per_launch) {
     const int nb = std::min(per_launch, B - b0);
     a.b0 = b0;
-    hipLaunchKernelGGL(walk_kernel, dim3(nb * G), dim3(kCoThreads), 0, stream, a);
+    launch_sliced(a, nb * G, stream);
     if (hipGetLastError() != hipSuccess) return TV_EHIP;
   }
   return TV_OK;
@@ -1313,5 +1413,30 @@ extern "C" tv_status tree_verify_mss(int B, int N, int V, int R, const float* ta
   a.num_accepted = num_accepted;
   a.bonus = bonus;
   a.rounds = rounds;
+  return launch_walk(a, B, stream);
+}
+
+extern "C" tv_status tree_verify_naive(int B, int N, int V, const float* target_logits,
+                                       const int32_t* token, const uint64_t* child, int32_t* status,
+                                       uint64_t seed, uint64_t offset, int32_t* accepted,
+                                       int32_t* num_accepted, int32_t* bonus, void* workspace,
+                                       size_t ws_bytes, hipStream_t stream) {
+  const tv_status c = check_verify_args(B, N, V);
+  if (c != TV_OK) return c;
+  if (B == 0) return TV_OK;
+  if (!target_logits || !child || !status || !num_accepted || !bonus ||
+      (N > 0 && (!token || !accepted)))
+    return TV_EINVAL;
+  if (!workspace || ws_bytes < ws_layout(B, V).total) return TV_EWORKSPACE;
+  WalkArgs a = make_args(MODE_NAIVE, N, V, 1, workspace, B);
+  a.logits = target_logits;
+  a.token = token;
+  a.child = child;
+  a.status = status;
+  a.seed = seed;
+  a.offset = offset;
+  a.accepted = accepted;
+  a.num_accepted = num_accepted;
+  a.bonus = bonus;
   return launch_walk(a, B, stream);
 }

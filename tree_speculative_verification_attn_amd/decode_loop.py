@@ -25,7 +25,8 @@ each single token) plus noise.  Their dense layers use torch; masks,
 attention, verification and KV compaction run in the library's kernels.  The
 loop exists to check the path end to end: greedy speculative decoding must
 emit exactly what plain greedy decoding of the target emits, and stochastic
-speculative decoding must sample the target's own distribution.
+speculative decoding (MSS, or the naive draw-then-check rule that Theorem 4.3
+compares it with) must sample the target's own distribution.
 """
 import numpy as np
 import torch
@@ -241,7 +242,7 @@ class SpecDecoder:
 
     def __init__(self, model, drafter, B, mode="mss", tree=("expand", (2, 2)), capacity=512,
                  seed=0, draft_seed=0):
-        assert mode in ("greedy", "mss")
+        assert mode in ("greedy", "mss", "naive")
         self.model, self.drafter, self.B, self.mode, self.tree = model, drafter, B, mode, tree
         self.state = PagedState(model, B, capacity, seed=seed)
         self.seed, self.it = seed + 12345, 0
@@ -262,7 +263,7 @@ class SpecDecoder:
         st, dev, B = self.state, self.model.device, self.B
         root = st.pending_pass(self.pending)                     # row 0 of the new tree
         kind, arg = self.tree
-        sample = self.mode == "mss"
+        sample = self.mode != "greedy"
         if kind == "expand":
             parent, token, q_row, ssm = expand_tree(self.drafter, self.pending, arg, sample, self.gen)
         else:
@@ -277,6 +278,8 @@ class SpecDecoder:
         tok32 = token.int().contiguous()
         if self.mode == "greedy":
             tv.tree_verify_greedy(tl, tok32, child, status, acc, num, bonus, ws)
+        elif self.mode == "naive":
+            tv.tree_verify_naive(tl, tok32, child, status, self.seed, self.it, acc, num, bonus, ws)
         else:
             rounds = torch.empty((B,), dtype=torch.int32, device=dev)
             tv.tree_verify_mss(tl, ssm, q_row, tok32, child, status, self.seed, self.it, acc, num, bonus,
