@@ -44,6 +44,9 @@ __global__ __launch_bounds__(kThreads) void kv_commit_kernel(
   const size_t block_stride = static_cast<size_t>(H) * head_stride;
   const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks;
 
+  // first round trip: the request's header and its accepted ids together
+  // (a node id is only used once k is known to cover it)
+  const int a_t = t < N ? accepted[static_cast<size_t>(b) * N + t] : 0;
   if (t == 0) {
     const int st = status[b];
     const int k = num_accepted[b];
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void kv_commit_kernel(
   if (k > N) {
     if (t == 0) atomicOr(&s_bad, 2);
   } else if (t < k) {
-    const int a = accepted[static_cast<size_t>(b) * N + t];
+    const int a = a_t;
     if (a < 0 || a >= N) {
       atomicOr(&s_bad, 2);
     } else {
