@@ -12,15 +12,17 @@
 // key K/V row is read from HBM exactly once and reused by all N tree queries
 // of that (b, h), which is what makes the tree pass cheaper than per-path
 // decoding.  The pass is bound by HBM bandwidth, so the bf16 kernel runs one
-// workgroup per CU with a deep ring of K/V stages in LDS (128 KB of loads in
-// flight per CU).  The number of chunks per (b, h) comes from a small cost
+// workgroup per CU that streams its chunk through LDS.  The number of chunks
+// per (b, h) comes from a small cost
 // model: as few as keep every CU busy, because each extra chunk leaves an
 // unnormalised partial (O, max, sum) that a second kernel reads back and
 // merges with log-sum-exp weights.
 //
-// bf16 path (matrix cores): K/V stages of 64 keys go HBM -> LDS with
-// direct-to-LDS loads; wave w < ceil(N/16) owns query tile w for the whole
-// chunk and keeps its running max, sum and O in registers.  Per 32 keys:
+// bf16 path (matrix cores): K/V stages of 32 keys go HBM -> LDS with
+// direct-to-LDS loads; three independent 4-wave groups per workgroup each
+// run a two-buffer ring (48 KB of loads in flight per CU) and claim stages
+// of the chunk at run time.  Within a group, wave w < ceil(N/16) owns query
+// tile w and keeps its running max, sum and O in registers.  Per 32 keys:
 //   S^T[key][query] = K . Q^T     on v_mfma_f32_16x16x32_bf16
 //     (A = 16 keys x 32 dims of K from LDS, B = 32 dims x 16 queries of Q)
 //   O^T[dim][query] += V^T . P^T  on the same instruction
@@ -149,8 +151,8 @@ __device__ __forceinline__ int tile_off(int r, int c16) {   // byte offset
 }
 
 // One workgroup per (request b, head h, key chunk s), made of kGroups groups of 4
-// waves.  The chunk is cut into stages of 32 keys; group g takes stages
-// g, g + kGroups, g + 2 kGroups, ... and runs as if it were a workgroup of its own: a
+// waves.  The chunk is cut into stages of 32 keys, which the groups claim
+// as they go (see the loop below); each group runs as if it were a workgroup of its own: a
 // two-buffer ring of K/V stages filled HBM -> LDS with direct-to-LDS loads
 // (no registers), one stage in flight while the other is read, and its own
 // barrier (an LDS counter), so the groups drift independently and one
@@ -192,6 +194,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   __shared__ __attribute__((aligned(16))) uint8_t ring[kGroups * kRing * 2 * TILE];
   __shared__ int s_hung;
   __shared__ int s_gbar[kGroups];
+  __shared__ int s_next;                    // next stage of the chunk not yet claimed
+  __shared__ int s_sel[kGroups][2];         // stage a group's wave 0 claimed for the group
   __shared__ int s_blk[kMaxChunkBlocks];
 
   // Every load that depends on nothing goes out first, in every thread:
@@ -200,9 +204,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   // prefix length is not written during the launch, so every thread sees
   // the same value; the status can be (another workgroup of the request may
   // flag a bad block), so the workgroup agrees on it at a barrier below.
+  // Status and prefix length are read with vector loads (the request index
+  // is moved to a vector register first): as scalar loads of a uniform
+  // address the compiler issues them where they are first used, after the
+  // wait below, and every workgroup would start with two more dependent
+  // trips to memory.
+  // The kernel arguments the start reads are fetched in one batch of scalar
+  // loads (otherwise a second batch waits on the first).
+  asm volatile("" :: "s"(a.q), "s"(a.kc), "s"(a.vc), "s"(a.block_table), "s"(a.prefix_len), "s"(a.anc),
+               "s"(a.status), "s"(a.N), "s"(a.H), "s"(a.num_blocks), "s"(a.max_blocks), "s"(a.chunk));
   const int N = a.N;
-  const int st = a.status[b];
-  const int L = a.prefix_len[b];
+  int b_v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(b_v) : "s"(b));
+  const int st_v = a.status[b_v];
+  const int L_v = a.prefix_len[b_v];
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
   // Query tile of this wave.  Wave gw of a group runs on SIMD gw, so the
   // tile index is rotated by the group: with fewer tiles than waves, the
@@ -241,6 +256,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   // so it adds no wait of its own inside the stage loop, where a wait would
   // also drain the stage loads in flight, which it does not know about.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
+  const int st = __builtin_amdgcn_readfirstlane(st_v);
+  const int L = __builtin_amdgcn_readfirstlane(L_v);
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int i = threadIdx.x + r * kAttnThreads;
@@ -256,7 +273,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   if (k_begin >= T) return;                 // empty chunk (never chunk 0): not counted by the merge
   const int k_end = min(T, k_begin + a.chunk);
   const int nst = (k_end - k_begin + SK - 1) / SK;                // stages of the chunk
-  const int nloc = nst > grp ? (nst - grp + kGroups - 1) / kGroups : 0;   // this group's
   const int nblk = (k_end - 1) / TV_BLOCK - blk_first + 1;        // blocks covering the chunk's keys
 
   const uint8_t* __restrict__ kg = static_cast<const uint8_t*>(a.kc);
@@ -272,7 +288,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     if (i < nblk && (raw[r] < 0 || raw[r] >= a.num_blocks)) bad = 1;
   }
   if (threadIdx.x < kGroups) s_gbar[threadIdx.x] = 0;
-  if (threadIdx.x == 0) s_hung = 0;
+  if (threadIdx.x < 2 * kGroups) s_sel[threadIdx.x >> 1][threadIdx.x & 1] = INT_MAX;
+  if (threadIdx.x == 0) {
+    s_hung = 0;
+    s_next = kGroups * kRing;               // the ones before are handed out statically below
+  }
   // (__syncthreads_or is a logical OR: one call per flag)
   if (__syncthreads_or(st != TV_REQ_OK)) {  // a skipped request: zero output
     if (s == 0) zero_out<uint16_t>(a, b, h);
@@ -454,21 +474,49 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
-  // The ring's buffers all start filling now.  In the loop, one barrier
-  // per stage: after it, the stage's loads have landed for every wave, and
-  // every wave has finished reading the buffer of the stage before, which is
-  // then refilled with the stage kRing - 1 further on, so that stage is in
-  // flight during this stage's compute.
-  for (int r = 0; r < kRing && r < nloc; ++r) issue(grp + kGroups * r, gring + r * 2 * TILE);
-  for (int it = 0; it < nloc; ++it) {
-    uint8_t* cur = gring + (it % kRing) * 2 * TILE;
-    // stages issued so far: 0 .. min(nloc, it + kRing - 1) - 1 (it = 0: 0 .. kRing - 1)
-    const int issued = it == 0 ? min(kRing, nloc) : min(nloc, it + kRing - 1);
-    wait_stage(issued - 1 - it);
+  // Stages are handed to the groups at run time.  Group g starts with
+  // stages g, g + kGroups, ... (one per ring buffer, all loading now); after
+  // that, whenever a buffer frees up, the group claims the next unclaimed
+  // stage of the chunk from an LDS counter.  A group whose loads land late
+  // thus takes fewer stages, and the groups finish close together (with a
+  // fixed share, the group that started last decides when the workgroup
+  // ends).  Wave 0 of the group claims just before it arrives at the
+  // barrier and leaves the index in s_sel; the other waves read it after
+  // the barrier.  held[0] is the stage being computed, held[1..] the ones in
+  // flight; claims only grow, so once held[0] is past the chunk every later
+  // one is too.
+  //
+  // In the loop, one barrier per stage: after it, the stage's loads have
+  // landed for every wave, and every wave has finished reading the buffer
+  // of the stage before, which is then refilled with the newly claimed
+  // stage, in flight during this stage's compute.
+  int held[kRing];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) {
+    held[r] = grp + kGroups * r;
+    if (held[r] < nst) issue(held[r], gring + r * 2 * TILE);
+  }
+  for (int it = 0;; ++it) {
+    if (held[0] >= nst) break;
+    // in flight: held[1 .. kRing - 1] at it = 0, held[1 .. kRing - 2] after
+    // (the last buffer is refilled after this iteration's barrier)
+    int later = 0;
+#pragma unroll
+    for (int r = 1; r < kRing; ++r)
+      if ((it == 0 || r < kRing - 1) && held[r] < nst) ++later;
+    wait_stage(later);
+    if (it >= 1 && gw == 0 && lane == 0)
+      s_sel[grp][it & 1] = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     group_barrier();
-    if (it >= 1 && it + kRing - 1 < nloc)
-      issue(grp + kGroups * (it + kRing - 1), gring + ((it + kRing - 1) % kRing) * 2 * TILE);
-    if (computes) compute(grp + kGroups * it, cur);
+    if (it >= 1) {
+      const int nx = s_sel[grp][it & 1];
+      held[kRing - 1] = nx;
+      if (nx >= 0 && nx < nst) issue(nx, gring + ((it + kRing - 1) % kRing) * 2 * TILE);
+    }
+    if (computes) compute(held[0], gring + (it % kRing) * 2 * TILE);
+#pragma unroll
+    for (int r = 0; r + 1 < kRing; ++r) held[r] = held[r + 1];
+    held[kRing - 1] = INT_MAX;                // claimed at the next iteration
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lrun += __shfl_xor(lrun, 16, 64);
