@@ -44,9 +44,11 @@
 
 namespace {
 
-constexpr int kCoThreads = 256;                    // threads per workgroup
-constexpr int kElem = 8;                           // vocabulary entries per thread
-constexpr int kSlice = kCoThreads * kElem;         // entries per workgroup
+constexpr int kOwnThreads = 256;                   // threads that own vocabulary entries
+constexpr int kCoThreads = kOwnThreads + 64;       // threads per workgroup: the owners and the poll wave
+constexpr int kPollWave = kOwnThreads / 64;        // stages the request and polls the exchanges
+constexpr int kElem = 8;                           // vocabulary entries per owner thread
+constexpr int kSlice = kOwnThreads * kElem;        // entries per workgroup
 constexpr int kMaxG = (1 << 20) / kSlice;          // workgroups per request at V = 2^20
 constexpr int kHdr = 4;                            // header words per workgroup per exchange
 constexpr unsigned kSpinLimit = 1u << 22;          // polls of one word before giving up
@@ -200,7 +202,7 @@ __device__ __forceinline__ bool q_bad(float q) { return !(q >= 0.f) || q == INFI
 // walk state lives in registers and a pass needs no barrier beyond those of
 // its workgroup reductions.
 // ---------------------------------------------------------------------------
-template <int MODE>
+template <int MODE, bool VEC>
 __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   constexpr int NW = kCoThreads / 64;
   const int G = a.G;
@@ -211,14 +213,12 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   constexpr bool mss = MODE == MODE_MSS, naive = MODE == MODE_NAIVE;
   constexpr bool need_z = mss || naive;               // the walk needs the normaliser
   const int xa = g * kSlice + t * kElem;              // first entry of this thread
-  const int nx = max(0, min(kElem, V - xa));          // entries it owns
+  const int nx = t < kOwnThreads ? max(0, min(kElem, V - xa)) : 0;   // entries it owns
   const float* lbase = a.logits + static_cast<size_t>(b) * (N + 1) * V;
   const float* sbase = mss ? a.ssm + static_cast<size_t>(b) * a.R * V : nullptr;
   uint32_t* done = a.done + static_cast<size_t>(b) * 64;
   uint64_t* hdr = a.hdr + static_cast<size_t>(b) * 2 * G * kHdr;
   uint64_t* kid = a.kid + static_cast<size_t>(b) * 2 * 64;
-  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 &&
-                   (!mss || (reinterpret_cast<uintptr_t>(a.ssm) & 15) == 0);
 
   __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES];
   __shared__ uint64_t s_child[TV_MAX_NODES + 1];
@@ -231,29 +231,38 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   __shared__ double s_gs[2][kMaxG];
   __shared__ int s_ga[2][kMaxG];
   __shared__ float s_rx2[2][TV_MAX_NODES];
+  __shared__ float s_lxq[2][2];                  // MSS: p and q at the candidate's token, from wave 0
   __shared__ double s_gt[NW][kMaxG];             // slice totals of the current distribution (per wave)
   __shared__ double s_scan[NW];
   __shared__ int s_status0, s_timeout, s_found, s_last, s_xs;
   __shared__ float own_s[kElem];
 
-  static_assert(kElem % 4 == 0 || kElem < 4, "entries per thread");
-  auto load8 = [&](const float* row, float (&dst)[kElem]) {
-    if (vec && nx == kElem && kElem % 4 == 0) {
+  static_assert(kElem % 4 == 0, "entries per thread");
+  // VEC (V a multiple of 4, rows 16-byte aligned): a thread owns 0, 4 or 8
+  // entries and loads them as float4s.  The choice is made at compile time: a
+  // run-time choice leaves both paths writing the same registers, and the
+  // compiler then drains every load in flight before the float4 ones.
+  // Entries past the vocabulary (and all of the poll wave's) get a neutral
+  // value, so the passes over a row need no bounds tests: -inf for logits
+  // (never a max, no mass) and 0 for draft rows (a zero residual).
+  auto load8 = [&](const float* row, float (&dst)[kElem], float pad) {
+    if constexpr (VEC) {
 #pragma unroll
       for (int e = 0; e < kElem; e += 4) {
-        const float4 f = *reinterpret_cast<const float4*>(row + xa + e);
+        float4 f = make_float4(pad, pad, pad, pad);
+        if (e < nx) f = *reinterpret_cast<const float4*>(row + xa + e);
         dst[e] = f.x; dst[e + 1] = f.y; dst[e + 2] = f.z; dst[e + 3] = f.w;
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < kElem; ++k) dst[k] = k < nx ? row[xa + k] : 0.f;
+      for (int k = 0; k < kElem; ++k) dst[k] = k < nx ? row[xa + k] : pad;
     }
   };
 
   // ---------------- issue the first loads, stage the request ----------------
   float lv[kElem];         // logits of the current node's row, this thread's entries
-  load8(lbase, lv);        // the root row is always visited
-  if (wave == 0) {
+  load8(lbase, lv, -INFINITY);   // the root row is always visited
+  if (wave == kPollWave) {
     const size_t rb = static_cast<size_t>(b);
     const int st0 = lane == 0 ? a.status[b] : 0;
     // child[N] (children of the last node) is empty after masking
@@ -346,7 +355,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     double part = 0.0;
 #pragma unroll
     for (int e = 0; e < kElem; ++e) {
-      cur[e] = e < nx ? (mode == 0 ? (lv[e] == -INFINITY ? 0.f : tv::exp_acc(lv[e] - m)) : cv[e]) : 0.f;
+      cur[e] = mode == 0 ? (lv[e] == -INFINITY ? 0.f : tv::exp_acc(lv[e] - m)) : cv[e];   // padding: 0
       part += static_cast<double>(cur[e]);
     }
     double wexcl;
@@ -394,7 +403,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         const int x = slice_search();
         if (t == 0) put_tagged(kid + par * 64, tag, static_cast<uint32_t>(x));
       }
-      if (wave == 0) {
+      if (wave == kPollWave) {
         bool to = false;
         if (lane == 0) {
           uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
@@ -438,18 +447,26 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
 #pragma unroll
         for (int e = 0; e < kElem; ++e) lv[e] = qn[e];
       } else {
-        load8(lrow, lv);
+        load8(lrow, lv, -INFINITY);
       }
     }
+    // Every load issued so far is complete here: the rows just moved were
+    // requested a pass ago, and the root row or a row loaded just above is
+    // needed now anyway.  Waiting before the next candidates' rows are
+    // requested matters: otherwise the compiler makes this pass's arithmetic
+    // wait for those loads too (it cannot tell them apart across the loop),
+    // and each pass pays a whole memory round trip the prefetch was meant
+    // to hide.
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
     // greedy/naive: the rows of the first two children, in case the walk enters one
     if (!mss && pass == P_ENTER) c1 = c2 = -1;
     if (!mss && pass == P_ENTER && U) {
       c1 = __builtin_ctzll(U);
-      load8(lbase + static_cast<size_t>(c1 + 1) * V, lvn);
+      load8(lbase + static_cast<size_t>(c1 + 1) * V, lvn, -INFINITY);
       const uint64_t rest = U & (U - 1);
       if (rest) {
         c2 = __builtin_ctzll(rest);
-        load8(lbase + static_cast<size_t>(c2 + 1) * V, qn);
+        load8(lbase + static_cast<size_t>(c2 + 1) * V, qn, -INFINITY);
       }
     }
     // the child tested after this pass, and its rows (loads in flight during the pass)
@@ -460,10 +477,15 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       w = tv::mss_words(a.seed, a.offset, b, u + 1, j);
       cand = nth_bit(U, tv::pick_index(w.x, __builtin_popcountll(U)));
       const float* qrow_c = sbase + static_cast<size_t>(s_qrow[cand]) * V;
-      load8(qrow_c, qn);
-      load8(lbase + static_cast<size_t>(cand + 1) * V, lvn);
-      lx_c = lrow[s_tok[cand]];
-      qx_c = qrow_c[s_tok[cand]];
+      // p and q at the candidate's token go out before the rows, so that
+      // waiting for them does not wait for the rows; the poll wave loads
+      // nothing here and takes them from wave 0 after the exchange
+      if (wave != kPollWave) {
+        lx_c = lrow[s_tok[cand]];
+        qx_c = qrow_c[s_tok[cand]];
+      }
+      load8(qrow_c, qn, 0.f);
+      load8(lbase + static_cast<size_t>(cand + 1) * V, lvn, -INFINITY);
     }
     const uint32_t tag = static_cast<uint32_t>(ex_no + 1);
     const int par = ex_no & 1;
@@ -471,21 +493,25 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
 
     if (pass == P_ENTER) {
       // ---- statistics of u's row over this slice ----
+      // Branch-free: a strict > keeps the first index of the max; a thread
+      // whose entries are all -inf keeps no index, which only matters for a
+      // row that fails anyway.  The flags only decide "any NaN, or no finite
+      // maximum", so they follow from a NaN bit and the thread's maximum:
+      // +inf present <=> max = +inf; some finite entry <=> max finite (NaN
+      // never wins a >).
       float mx = -INFINITY;
-      int arg = 0x7FFFFFFF, flags = 0;
+      int arg = 0x7FFFFFFF;
+      bool nan = false;
 #pragma unroll
       for (int e = 0; e < kElem; ++e) {
-        if (e < nx) {
-          const float f = lv[e];
-          if (f != f) flags |= FLAG_NAN;
-          else if (f == INFINITY) flags |= FLAG_PINF;
-          else if (f != -INFINITY) flags |= FLAG_FINITE;
-          if (f > mx || (f == mx && arg == 0x7FFFFFFF)) {   // first index of the max
-            mx = f;
-            arg = xa + e;
-          }
-        }
+        const float f = lv[e];
+        nan |= f != f;
+        const bool take = f > mx;
+        mx = take ? f : mx;
+        arg = take ? xa + e : arg;
       }
+      int flags = (nan ? FLAG_NAN : 0) | (mx == INFINITY ? FLAG_PINF : 0) |
+                  ((mx != INFINITY && mx != -INFINITY) ? FLAG_FINITE : 0);
       tv::wave_argmax_dpp(mx, arg);
       flags = tv::wave_or_dpp(flags);
       if (lane == 0) {
@@ -506,7 +532,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         double acc = 0.0;
 #pragma unroll
         for (int e = 0; e < kElem; ++e)
-          if (e < nx && lv[e] != -INFINITY) acc += static_cast<double>(tv::exp_acc(lv[e] - M));
+          acc += lv[e] != -INFINITY ? static_cast<double>(tv::exp_acc(lv[e] - M)) : 0.0;
         int unused;
         S = block_sum_or(acc, 0, s_red, s_redf, rs_no & 1, &unused);
         ++rs_no;
@@ -524,15 +550,11 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       double acc = 0.0;
       int bad = 0;
 #pragma unroll
-      for (int e = 0; e < kElem; ++e) {
-        if (e < nx) {
-          const float c = mode == 0 ? (lv[e] == -INFINITY ? 0.f : tv::exp_acc(lv[e] - m)) : cv[e];
-          if (q_bad(qv[e])) bad = 1;
-          rn[e] = static_cast<float>(fmax(0.0, static_cast<double>(c) - Z * static_cast<double>(qv[e])));
-          acc += static_cast<double>(rn[e]);
-        } else {
-          rn[e] = 0.f;
-        }
+      for (int e = 0; e < kElem; ++e) {      // padding: c = 0 and q = 0, so rn = 0
+        const float c = mode == 0 ? (lv[e] == -INFINITY ? 0.f : tv::exp_acc(lv[e] - m)) : cv[e];
+        bad |= q_bad(qv[e]) ? 1 : 0;
+        rn[e] = static_cast<float>(fmax(0.0, static_cast<double>(c) - Z * static_cast<double>(qv[e])));
+        acc += static_cast<double>(rn[e]);
       }
       int anyb;
       const double Zg = block_sum_or(acc, bad, s_red, s_redf, rs_no & 1, &anyb);
@@ -561,11 +583,11 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       }
     }
 
-    // ---- wave 0 gathers every workgroup's words into LDS ----
+    // ---- the poll wave gathers every workgroup's words into LDS ----
     // (A wave reads a bank only between this exchange's barrier and the next
-    // pass's first barrier, and wave 0 refills the bank two exchanges later,
-    // after that barrier.)
-    if (wave == 0) {
+    // pass's first barrier, and the poll wave refills the bank two exchanges
+    // later, after that barrier.)
+    if (wave == kPollWave) {
       bool to = false;
       if (pass == P_RESID && lane < N && ((U >> lane) & 1ull)) {
         uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
@@ -588,7 +610,15 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       }
       if (__any(to) && lane == 0) s_timeout = 1;
     }
+    if (mss && cand >= 0 && t == 0) {
+      s_lxq[par][0] = lx_c;
+      s_lxq[par][1] = qx_c;
+    }
     __syncthreads();
+    if (mss && cand >= 0 && wave == kPollWave) {
+      lx_c = s_lxq[par][0];
+      qx_c = s_lxq[par][1];
+    }
     ++ex_no;
     if (s_timeout) {
       timed_out = true;
@@ -1271,32 +1301,39 @@ tv_status check_verify_args(int B, int N, int V) {
 
 // Workgroups of the walk kernel that fit on the device at once (cached per
 // device and mode: it depends only on the kernel and the device).
+template <bool VEC>
 const void* walk_kernel_of(int mode) {
-  if (mode == MODE_MSS) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS>);
-  if (mode == MODE_NAIVE) return reinterpret_cast<const void*>(walk_kernel<MODE_NAIVE>);
-  return reinterpret_cast<const void*>(walk_kernel<MODE_GREEDY>);
+  if (mode == MODE_MSS) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC>);
+  if (mode == MODE_NAIVE) return reinterpret_cast<const void*>(walk_kernel<MODE_NAIVE, VEC>);
+  return reinterpret_cast<const void*>(walk_kernel<MODE_GREEDY, VEC>);
 }
 
-int walk_capacity(int dev, int mode) {
-  static int cache[3][64];
+int walk_capacity(int dev, int mode, bool vec) {
+  static int cache[2][3][64];
   const bool cached = dev >= 0 && dev < 64 && mode >= 0 && mode < 3;
-  if (cached && cache[mode][dev] > 0) return cache[mode][dev];
+  if (cached && cache[vec][mode][dev] > 0) return cache[vec][mode][dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, walk_kernel_of(mode), kCoThreads, 0) != hipSuccess)
-    return 0;
+  const void* fn = vec ? walk_kernel_of<true>(mode) : walk_kernel_of<false>(mode);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kCoThreads, 0) != hipSuccess) return 0;
   const int cap = cus * std::max(1, per_cu);
-  if (cached) cache[mode][dev] = cap;
+  if (cached) cache[vec][mode][dev] = cap;
   return cap;
 }
 
-void launch_sliced(const WalkArgs& a, int grid, hipStream_t stream) {
+template <bool VEC>
+void launch_sliced_vec(const WalkArgs& a, int grid, hipStream_t stream) {
   if (a.mode == MODE_MSS)
-    hipLaunchKernelGGL((walk_kernel<MODE_MSS>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else if (a.mode == MODE_NAIVE)
-    hipLaunchKernelGGL((walk_kernel<MODE_NAIVE>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_NAIVE, VEC>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((walk_kernel<MODE_GREEDY>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_GREEDY, VEC>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+}
+
+void launch_sliced(const WalkArgs& a, int grid, bool vec, hipStream_t stream) {
+  if (vec) launch_sliced_vec<true>(a, grid, stream);
+  else launch_sliced_vec<false>(a, grid, stream);
 }
 
 template <int E, int MODE>
@@ -1317,10 +1354,10 @@ void launch_row(const WalkArgs& a, int B, bool vec, hipStream_t stream) {
 // at once, so the workgroups of a request never wait for one another's
 // residency (the waits are bounded regardless).
 tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
+  const bool vec = (a.V & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 &&
+                   (a.mode != MODE_MSS || (reinterpret_cast<uintptr_t>(a.ssm) & 15) == 0);
   if (a.V <= kRowThreads * kRowMaxE) {     // one workgroup per request
     a.b0 = 0;
-    const bool vec = (a.V & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 &&
-                     (a.mode != MODE_MSS || (reinterpret_cast<uintptr_t>(a.ssm) & 15) == 0);
     if (a.V <= kRowThreads * 8) launch_row<8>(a, B, vec, stream);
     else if (a.V <= kRowThreads * 16) launch_row<16>(a, B, vec, stream);
     else launch_row<32>(a, B, vec, stream);
@@ -1329,14 +1366,14 @@ tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
   const int G = a.G;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TV_EHIP;
-  const int capacity = walk_capacity(dev, a.mode);
+  const int capacity = walk_capacity(dev, a.mode, vec);
   if (capacity <= 0) return TV_EHIP;
   if (G > capacity) return TV_EINVAL;
   const int per_launch = capacity / G;
   for (int b0 = 0; b0 < B; b0 += per_launch) {
     const int nb = std::min(per_launch, B - b0);
     a.b0 = b0;
-    launch_sliced(a, nb * G, stream);
+    launch_sliced(a, nb * G, vec, stream);
     if (hipGetLastError() != hipSuccess) return TV_EHIP;
   }
   return TV_OK;
