@@ -2,7 +2,8 @@
 
 A step is the whole verification path over one batch of synthetic input:
 tree_build_mask -> tree_attn_verify -> tree_verify_greedy -> tree_verify_mss
--> kv_commit_accepted.  The default workload is the LLaMA-7B-shaped layer
+-> kv_commit_accepted, the last two as one tree_verify_mss_commit launch
+(which gives exactly their results).  The default workload is the LLaMA-7B-shaped layer
 (bf16, 8 requests x 32 heads x 128 dims, 1024-token prefixes, a 46-node
 expansion tree <2,2,2,1,1,1,1>, fp32 logits over a 32000-token vocabulary).
 
@@ -130,11 +131,10 @@ def main():
         if ev: ev[2].record(cur)
         tv.tree_verify_greedy(c["tl"], token, child, status, g_acc, g_num, g_bonus, ws_v)
         if ev: ev[3].record(cur)
-        tv.tree_verify_mss(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset + i, m_acc,
-                           m_num, m_bonus, m_rounds, ws_v)
+        # MSS and the compaction of its path, in one launch
+        tv.tree_verify_mss_commit(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset + i, m_acc,
+                                  m_num, m_bonus, m_rounds, ws_v, c["k"], c["v"], bt, pl)
         if ev: ev[4].record(cur)
-        tv.kv_commit_accepted(c["k"], c["v"], bt, pl, m_acc, m_num, status)
-        if ev: ev[5].record(cur)
 
     for i in range(args.warmup):
         step(i)
@@ -148,14 +148,14 @@ def main():
 
     # Eager pass with HIP events between the calls: per-call times on the
     # launch stream (the attention figure feeds the roofline).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    names = ["mask", "attn", "greedy", "mss", "commit"]
+    names = ["mask", "attn", "greedy", "mss_commit"]
     comp = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
             for k, n in enumerate(names)}
     assert int((status != 0).sum()) == 0, "a request failed during the benchmark"

@@ -232,6 +232,35 @@ tv_status kv_commit_accepted(tv_dtype dt, int B, int N, int H, int D, void* k_ca
                              const int32_t* accepted, const int32_t* num_accepted,
                              int32_t* status, hipStream_t stream);
 
+/*
+ * tree_verify_mss_commit - tree_verify_mss, then kv_commit_accepted of the
+ * path it accepted, in one launch.
+ * Defines: the two operations above (SpecInfer summary, "Token Verification:
+ * Stochastic Decoding and Multi-Step Speculative Sampling
+ * (VerifyStochastic)" and "KV-cache for verified tokens"): verification
+ * decides the accepted path, and only that path keeps its cache entries.
+ *
+ * The results are exactly those of
+ *   tree_verify_mss(B, N, V, R, target_logits, ..., workspace, ws_bytes, stream);
+ *   kv_commit_accepted(kv_dtype, B, N, H, D, k_cache, v_cache, num_blocks,
+ *                      block_size, block_table, max_blocks, prefix_len,
+ *                      accepted, num_accepted, status, stream);
+ * on the same arguments (outputs, status codes, cache contents, prefix
+ * lengths).  The workgroup of a request that writes the accepted path also
+ * moves its rows, which saves the second launch and its start-up round trips.
+ * The first 18 arguments are tree_verify_mss's, the rest kv_commit_accepted's
+ * (N, B and accepted / num_accepted / status are shared); ownership,
+ * workspace rules and errors are the union of theirs.
+ */
+tv_status tree_verify_mss_commit(int B, int N, int V, int R, const float* target_logits,
+                                 const float* ssm_probs, const int32_t* q_row, const int32_t* token,
+                                 const uint64_t* child, int32_t* status, uint64_t seed,
+                                 uint64_t offset, int32_t* accepted, int32_t* num_accepted,
+                                 int32_t* bonus, int32_t* rounds, void* workspace, size_t ws_bytes,
+                                 tv_dtype kv_dtype, int H, int D, void* k_cache, void* v_cache,
+                                 int num_blocks, int block_size, const int32_t* block_table,
+                                 int max_blocks, int32_t* prefix_len, hipStream_t stream);
+
 /* Human-readable name of a tv_status value (static storage). */
 /*
  * tree_verify_naive - naive sampling verification (the comparator of

@@ -88,6 +88,19 @@ class GpuRun:
                            self.m_acc, self.m_num, self.m_bonus, self.m_rounds, self._ws_verify())
         return self
 
+    def mss_commit(self, seed=None, offset=None):
+        """tree_verify_mss and the commit of its path in one call."""
+        w = self.w
+        self.m_acc = torch.empty((w.B, w.N), dtype=torch.int32, device=DEV)
+        self.m_num = torch.empty((w.B,), dtype=torch.int32, device=DEV)
+        self.m_bonus = torch.empty((w.B,), dtype=torch.int32, device=DEV)
+        self.m_rounds = torch.empty((w.B,), dtype=torch.int32, device=DEV)
+        tv.tree_verify_mss_commit(self.tl, self.sp, self.qr, self.token, self.child, self.status,
+                                  w.seed if seed is None else seed, w.offset if offset is None else offset,
+                                  self.m_acc, self.m_num, self.m_bonus, self.m_rounds, self._ws_verify(),
+                                  self.k, self.v, self.bt, self.pl)
+        return self
+
     def naive(self, seed=None, offset=None):
         w = self.w
         self.n_acc = torch.empty((w.B, w.N), dtype=torch.int32, device=DEV)

@@ -90,6 +90,19 @@ def test_host_argument_checks(L):
     assert L.kv_commit_accepted(1, 2, 5, 2, 128, None, _p(), 10, 16, _p(), 4, _p(), _p(), _p(), _p(),
                                 None) == TV_EINVAL
 
+    def mss_commit(N=5, R=3, dt=1, H=2, D=128, bs=16, kc=True, ws_bytes=None):
+        return L.tree_verify_mss_commit(2, N, 1000, R, _p(), _p(), _p(), _p(), _p(), _p(), 1, 0, _p(), _p(),
+                                        _p(), None, _p(), wsv if ws_bytes is None else ws_bytes, dt, H, D,
+                                        _p() if kc else None, _p(), 10, bs, _p(), 4, _p(), None)
+    assert mss_commit(dt=5) == TV_EDTYPE
+    assert mss_commit(N=65) == TV_ETOOBIG
+    assert mss_commit(R=0) == TV_EINVAL
+    assert mss_commit(D=96) == TV_EINVAL
+    assert mss_commit(H=0) == TV_EINVAL
+    assert mss_commit(bs=8) == TV_EINVAL
+    assert mss_commit(kc=False) == TV_EINVAL
+    assert mss_commit(ws_bytes=wsv - 1) == TV_EWORKSPACE
+
 
 def test_binding_names_match_exports():
     for n in tv_pkg.EXPORTS:

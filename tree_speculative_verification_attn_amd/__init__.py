@@ -15,6 +15,7 @@ __all__ = [
     "tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
     "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss", "kv_commit_accepted",
     "tree_verify_naive", "tree_logits_transform", "TV_OUT_LOGITS", "TV_OUT_PROBS", "tv_status_string",
+    "tree_verify_mss_commit",
 ]
 
 TV_F32 = 0
@@ -23,7 +24,8 @@ TV_OUT_LOGITS = 0
 TV_OUT_PROBS = 1
 EXPORTS = ("tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
            "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss",
-           "kv_commit_accepted", "tree_verify_naive", "tree_logits_transform", "tv_status_string")
+           "kv_commit_accepted", "tree_verify_naive", "tree_logits_transform", "tv_status_string",
+           "tree_verify_mss_commit")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libtreeverify.so")
@@ -47,6 +49,8 @@ def _load():
         "tree_verify_greedy": ([I, I, I, P, P, P, P, P, P, P, P, SZ, P], I),
         "tree_verify_mss": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ, P], I),
         "kv_commit_accepted": ([I, I, I, I, I, P, P, I, I, P, I, P, P, P, P, P], I),
+        "tree_verify_mss_commit": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ,
+                                    I, I, I, P, P, I, I, P, I, P, P], I),
         "tree_logits_transform": ([I, I, P, P, F, I, F, I, P], I),
         "tree_verify_naive": ([I, I, I, P, P, P, P, U64, U64, P, P, P, P, SZ, P], I),
         "tv_status_string": ([I], ctypes.c_char_p),
@@ -146,6 +150,22 @@ def tree_verify_mss(target_logits, ssm_probs, q_row, token, child, status, seed,
                                _ptr(token), _ptr(child), _ptr(status), int(seed), int(offset),
                                _ptr(accepted), _ptr(num_accepted), _ptr(bonus), _ptr(rounds),
                                _ptr(workspace), ws_bytes, _stream(stream)), "tree_verify_mss")
+
+
+def tree_verify_mss_commit(target_logits, ssm_probs, q_row, token, child, status, seed, offset,
+                           accepted, num_accepted, bonus, rounds, workspace,
+                           k_cache, v_cache, block_table, prefix_len, stream=None):
+    """tree_verify_mss followed by kv_commit_accepted of its path, in one launch."""
+    B, N1, V = target_logits.shape
+    R = ssm_probs.shape[1]
+    nb, H, bs, D = k_cache.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().tree_verify_mss_commit(B, N1 - 1, V, R, _ptr(target_logits), _ptr(ssm_probs), _ptr(q_row),
+                                      _ptr(token), _ptr(child), _ptr(status), int(seed), int(offset),
+                                      _ptr(accepted), _ptr(num_accepted), _ptr(bonus), _ptr(rounds),
+                                      _ptr(workspace), ws_bytes, _dtype_code(k_cache), H, D, _ptr(k_cache),
+                                      _ptr(v_cache), nb, bs, _ptr(block_table), block_table.shape[1],
+                                      _ptr(prefix_len), _stream(stream)), "tree_verify_mss_commit")
 
 
 def tree_verify_naive(target_logits, token, child, status, seed, offset, accepted, num_accepted, bonus,

@@ -38,7 +38,7 @@
 // after it has finished reading exchange n, so bank reuse never overwrites a
 // word that is still to be read.  The last workgroup to leave zeroes the
 // words, so every call starts from a zeroed workspace.
-#include "tv_common.h"
+#include "kv_move.h"
 
 #include <algorithm>
 
@@ -97,7 +97,10 @@ struct WalkArgs {
   uint32_t* done;
   uint64_t* hdr;
   uint64_t* kid;
+  bool commit;              // MSS: also compact the accepted path in the KV cache
+  tv::KvRef kv;             //   the cache, block table and prefix lengths
 };
+constexpr int kMoveChunks = 8;                     // 16-byte chunks per thread per batch of the move
 
 // device-scope relaxed atomics: coherent across XCDs without L2 flushes
 __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
@@ -202,7 +205,7 @@ __device__ __forceinline__ bool q_bad(float q) { return !(q >= 0.f) || q == INFI
 // walk state lives in registers and a pass needs no barrier beyond those of
 // its workgroup reductions.
 // ---------------------------------------------------------------------------
-template <int MODE, bool VEC>
+template <int MODE, bool VEC, bool COMMIT>
 __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   constexpr int NW = kCoThreads / 64;
   const int G = a.G;
@@ -235,6 +238,9 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   __shared__ double s_gt[NW][kMaxG];             // slice totals of the current distribution (per wave)
   __shared__ double s_scan[NW];
   __shared__ int s_status0, s_timeout, s_found, s_last, s_xs;
+  __shared__ int s_L;                            // COMMIT: the request's prefix length
+  __shared__ tv::CommitLds s_mv;                 // COMMIT: the move's block offsets
+  __shared__ int s_tblk[tv::kMaxTreeBlocks];     // COMMIT: block ids covering the tree's slots
   __shared__ float own_s[kElem];
 
   static_assert(kElem % 4 == 0, "entries per thread");
@@ -284,9 +290,18 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       }
       s_status0 = st;
       s_timeout = 0;
+      // nothing writes the prefix length before the move at the end
+      if constexpr (COMMIT) s_L = g == 0 ? a.kv.prefix_len[b] : 0;
     }
   }
   __syncthreads();
+
+  // COMMIT: the poll wave of workgroup 0 fetches the block ids of the tree's
+  // slots now; the loads land long before its first poll waits (in issue
+  // order) for anything
+  int tblk = 0;
+  if constexpr (COMMIT)
+    if (g == 0 && wave == kPollWave && lane < tv::kMaxTreeBlocks) tblk = tv::tree_block_id(a.kv, b, N, s_L, lane);
 
   // ---- walk state: registers, identical in every thread of the request ----
   int status = s_status0;
@@ -717,6 +732,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       pass = mss ? P_FINAL : P_NSAMPLE;
     }
   }
+  if constexpr (COMMIT)
+    if (g == 0 && wave == kPollWave && lane < tv::kMaxTreeBlocks) s_tblk[lane] = tblk;
   __syncthreads();
   const bool ok = status == TV_REQ_OK && !s_timeout;
 
@@ -726,11 +743,27 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     if (t == 0) a.bonus[b] = x;
   }
 
+  int stt = status;
+  if (stt == TV_REQ_OK && s_timeout) stt = TV_REQ_TIMEOUT;
+
+  // ---- verify + commit: workgroup 0 also compacts the accepted path,
+  // exactly as kv_commit_accepted would after this call.  Its checks and the
+  // first batch of row loads go out now, so the loads are in flight while
+  // the results are written and the workgroups sign off below. ----
+  tv::MovePlan plan;
+  int mres = -1;                   // TV_REQ_OK: move; -1: nothing to do; else the status to store
+  uint4 mbuf[kMoveChunks];
+  if constexpr (COMMIT) {
+    if (g == 0) {
+      mres = tv::move_prepare<kCoThreads, kMoveChunks, true>(a.kv, b, N, stt, s_L, ok ? k : -1, s_acc, false, s_mv,
+                                                              s_tblk, plan);
+      if (mres == TV_REQ_OK) tv::move_load<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, 0, mbuf);
+    }
+  }
+
   // ---- results: workgroup 0 writes the path (and the greedy / naive bonus) ----
   if (g == 0) {
     if (t == 0) {
-      int stt = status;
-      if (stt == TV_REQ_OK && s_timeout) stt = TV_REQ_TIMEOUT;
       if (stt != TV_REQ_OK) {
         a.status[b] = stt;
         a.num_accepted[b] = -1;
@@ -747,12 +780,24 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   }
 
   // ---- leave the workspace zeroed: the last workgroup out clears it ----
-  __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have completed
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's stores (and the move's first loads) have completed
   __syncthreads();
-  if (t == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == static_cast<uint32_t>(G - 1);
+  uint32_t prev = 0;
+  if (t == 0) prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (COMMIT) {
+    if (g == 0) {
+      if (mres == TV_REQ_OK) {
+        // every load of the first batch, in every thread, completed before
+        // the barrier above
+        tv::move_store<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, 0, mbuf);
+        tv::move_rest<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, plan.step);
+        if (t == 0) a.kv.prefix_len[b] = s_L + k;
+      } else if (mres >= 0 && mres != stt && t == 0) {
+        a.status[b] = mres;
+      }
+    }
   }
+  if (t == 0) s_last = prev == static_cast<uint32_t>(G - 1);
   __syncthreads();
   if (s_last) {          // every workgroup has finished reading
     for (int i = t; i < 2 * G * kHdr; i += kCoThreads) st_u64(hdr + i, 0ull);
@@ -794,7 +839,7 @@ constexpr int kRowWaves = kRowThreads / 64;
 constexpr int kRowQuad = 4 * kRowThreads;        // entries covered by one register quad
 constexpr int kRowMaxE = 32;                     // registers per row per thread
 
-template <int E, bool VEC, int MODE>
+template <int E, bool VEC, int MODE, bool COMMIT>
 __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
   static_assert(E % 4 == 0 && E <= kRowMaxE, "row registers");
   constexpr int C = E / 4;
@@ -814,6 +859,8 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
   __shared__ float s_ex[2][2];                   // the next child's token: old / new residual
   __shared__ double s_scan[C * kRowWaves];       // final sample: wave totals, quad-major
   __shared__ int s_status0, s_found;
+  __shared__ int s_L;                            // COMMIT: the request's prefix length
+  __shared__ tv::CommitLds s_mv;                 // COMMIT: the move's block offsets
   // the prefetched row (a draft row in MSS, the second child's logits in
   // greedy), in x order, written by direct-to-LDS loads; each wave reads
   // back only what its own loads wrote
@@ -1000,6 +1047,7 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
         else if (bad_q & real) st = TV_REQ_BAD_QROW;
       }
       s_status0 = st;
+      if constexpr (COMMIT) s_L = a.kv.prefix_len[b];   // nothing writes it before the move
     }
   }
   __syncthreads();
@@ -1291,6 +1339,12 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
   }
   const int kk = status == TV_REQ_OK ? k : 0;
   for (int i = t; i < N; i += kRowThreads) a.accepted[static_cast<size_t>(b) * N + i] = i < kk ? s_acc[i] : -1;
+  // verify + commit: compact the accepted path, as kv_commit_accepted would
+  if constexpr (COMMIT) {
+    const int res = tv::commit_request<kRowThreads, kMoveChunks, true>(a.kv, b, N, status, s_L,
+                                                                        status == TV_REQ_OK ? k : -1, s_acc, false, s_mv);
+    if (t == 0 && res != status) a.status[b] = res;
+  }
 }
 
 tv_status check_verify_args(int B, int N, int V) {
@@ -1301,34 +1355,38 @@ tv_status check_verify_args(int B, int N, int V) {
 
 // Workgroups of the walk kernel that fit on the device at once (cached per
 // device and mode: it depends only on the kernel and the device).
+// kernel variant: 0 greedy, 1 MSS, 2 naive, 3 MSS + commit
 template <bool VEC>
-const void* walk_kernel_of(int mode) {
-  if (mode == MODE_MSS) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC>);
-  if (mode == MODE_NAIVE) return reinterpret_cast<const void*>(walk_kernel<MODE_NAIVE, VEC>);
-  return reinterpret_cast<const void*>(walk_kernel<MODE_GREEDY, VEC>);
+const void* walk_kernel_of(int variant) {
+  if (variant == 3) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, true>);
+  if (variant == MODE_MSS) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, false>);
+  if (variant == MODE_NAIVE) return reinterpret_cast<const void*>(walk_kernel<MODE_NAIVE, VEC, false>);
+  return reinterpret_cast<const void*>(walk_kernel<MODE_GREEDY, VEC, false>);
 }
 
-int walk_capacity(int dev, int mode, bool vec) {
-  static int cache[2][3][64];
-  const bool cached = dev >= 0 && dev < 64 && mode >= 0 && mode < 3;
-  if (cached && cache[vec][mode][dev] > 0) return cache[vec][mode][dev];
+int walk_capacity(int dev, int variant, bool vec) {
+  static int cache[2][4][64];
+  const bool cached = dev >= 0 && dev < 64 && variant >= 0 && variant < 4;
+  if (cached && cache[vec][variant][dev] > 0) return cache[vec][variant][dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const void* fn = vec ? walk_kernel_of<true>(mode) : walk_kernel_of<false>(mode);
+  const void* fn = vec ? walk_kernel_of<true>(variant) : walk_kernel_of<false>(variant);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kCoThreads, 0) != hipSuccess) return 0;
   const int cap = cus * std::max(1, per_cu);
-  if (cached) cache[vec][mode][dev] = cap;
+  if (cached) cache[vec][variant][dev] = cap;
   return cap;
 }
 
 template <bool VEC>
 void launch_sliced_vec(const WalkArgs& a, int grid, hipStream_t stream) {
-  if (a.mode == MODE_MSS)
-    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+  if (a.mode == MODE_MSS && a.commit)
+    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, true>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+  else if (a.mode == MODE_MSS)
+    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, false>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else if (a.mode == MODE_NAIVE)
-    hipLaunchKernelGGL((walk_kernel<MODE_NAIVE, VEC>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_NAIVE, VEC, false>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((walk_kernel<MODE_GREEDY, VEC>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_GREEDY, VEC, false>), dim3(grid), dim3(kCoThreads), 0, stream, a);
 }
 
 void launch_sliced(const WalkArgs& a, int grid, bool vec, hipStream_t stream) {
@@ -1336,16 +1394,17 @@ void launch_sliced(const WalkArgs& a, int grid, bool vec, hipStream_t stream) {
   else launch_sliced_vec<false>(a, grid, stream);
 }
 
-template <int E, int MODE>
+template <int E, int MODE, bool COMMIT = false>
 void launch_row_mode(const WalkArgs& a, int B, bool vec, hipStream_t stream) {
   if (vec)
-    hipLaunchKernelGGL((walk_row_kernel<E, true, MODE>), dim3(B), dim3(kRowThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_row_kernel<E, true, MODE, COMMIT>), dim3(B), dim3(kRowThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((walk_row_kernel<E, false, MODE>), dim3(B), dim3(kRowThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_row_kernel<E, false, MODE, COMMIT>), dim3(B), dim3(kRowThreads), 0, stream, a);
 }
 template <int E>
 void launch_row(const WalkArgs& a, int B, bool vec, hipStream_t stream) {
-  if (a.mode == MODE_MSS) launch_row_mode<E, MODE_MSS>(a, B, vec, stream);
+  if (a.mode == MODE_MSS && a.commit) launch_row_mode<E, MODE_MSS, true>(a, B, vec, stream);
+  else if (a.mode == MODE_MSS) launch_row_mode<E, MODE_MSS>(a, B, vec, stream);
   else if (a.mode == MODE_NAIVE) launch_row_mode<E, MODE_NAIVE>(a, B, vec, stream);
   else launch_row_mode<E, MODE_GREEDY>(a, B, vec, stream);
 }
@@ -1366,7 +1425,7 @@ tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
   const int G = a.G;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TV_EHIP;
-  const int capacity = walk_capacity(dev, a.mode, vec);
+  const int capacity = walk_capacity(dev, a.mode == MODE_MSS && a.commit ? 3 : a.mode, vec);
   if (capacity <= 0) return TV_EHIP;
   if (G > capacity) return TV_EINVAL;
   const int per_launch = capacity / G;
@@ -1450,6 +1509,51 @@ extern "C" tv_status tree_verify_mss(int B, int N, int V, int R, const float* ta
   a.num_accepted = num_accepted;
   a.bonus = bonus;
   a.rounds = rounds;
+  return launch_walk(a, B, stream);
+}
+
+extern "C" tv_status tree_verify_mss_commit(int B, int N, int V, int R, const float* target_logits,
+                                            const float* ssm_probs, const int32_t* q_row, const int32_t* token,
+                                            const uint64_t* child, int32_t* status, uint64_t seed,
+                                            uint64_t offset, int32_t* accepted, int32_t* num_accepted,
+                                            int32_t* bonus, int32_t* rounds, void* workspace, size_t ws_bytes,
+                                            tv_dtype kv_dtype, int H, int D, void* k_cache, void* v_cache,
+                                            int num_blocks, int block_size, const int32_t* block_table,
+                                            int max_blocks, int32_t* prefix_len, hipStream_t stream) {
+  const tv_status c = check_verify_args(B, N, V);
+  if (c != TV_OK) return c;
+  if (kv_dtype != TV_F32 && kv_dtype != TV_BF16) return TV_EDTYPE;
+  if (R < 1 || H < 1 || (D != 64 && D != 128) || block_size != TV_BLOCK || max_blocks < 1 || num_blocks < 1)
+    return TV_EINVAL;
+  if (B == 0) return TV_OK;
+  if (!target_logits || !ssm_probs || !child || !status || !num_accepted || !bonus ||
+      (N > 0 && (!token || !accepted || !q_row)))
+    return TV_EINVAL;
+  if (!k_cache || !v_cache || !block_table || !prefix_len) return TV_EINVAL;
+  if (!workspace || ws_bytes < ws_layout(B, V).total) return TV_EWORKSPACE;
+  WalkArgs a = make_args(MODE_MSS, N, V, R, workspace, B);
+  a.logits = target_logits;
+  a.ssm = ssm_probs;
+  a.q_row = q_row;
+  a.token = token;
+  a.child = child;
+  a.status = status;
+  a.seed = seed;
+  a.offset = offset;
+  a.accepted = accepted;
+  a.num_accepted = num_accepted;
+  a.bonus = bonus;
+  a.rounds = rounds;
+  a.commit = true;
+  a.kv.H = H;
+  a.kv.D = D;
+  a.kv.elem = kv_dtype == TV_BF16 ? 2 : 4;
+  a.kv.kc = static_cast<uint8_t*>(k_cache);
+  a.kv.vc = static_cast<uint8_t*>(v_cache);
+  a.kv.num_blocks = num_blocks;
+  a.kv.block_table = block_table;
+  a.kv.max_blocks = max_blocks;
+  a.kv.prefix_len = prefix_len;
   return launch_walk(a, B, stream);
 }
 
