@@ -14,6 +14,9 @@ are used to check two statements from the same page:
     separate nodes (iid_marginal); it does not hold for a fixed child set.
   * Theorem 4.3: the probability that every child is rejected is at most the
     naive verifier's rejection probability, 1 - P_LLM(child tokens).
+  * merged trees (several SSMs proposing one token): Theorem 4.2 holds when
+    every proposal keeps its own round (multi_marginal), not when the merged
+    node is tested once.
 The single-child case is classic speculative sampling (wiki concept page
 "Speculative decoding", "Shared invariant"; the single-draft proof in "How
 Speculative Decoding in LLM Serving Actually Works", "Exact Proof of
@@ -110,6 +113,35 @@ def accept_prob_first_level(p, q, k):
             continue
         tot += w * (1 - all_reject_prob(p, [(x, q) for x in draw]))
     return tot
+
+
+def multi_marginal(p, qs, dedup=False):
+    """Distribution of the emitted token when SSM i proposes one token drawn
+    from its own distribution qs[i] (independent draws), averaged over the
+    draws.  Equal tokens are merged into one node:
+      * dedup=False: every proposal takes part as its own round with its
+        proposer's q (the multiplicity variant);
+      * dedup=True: the merged node is tested once, with the q of its
+        lowest-numbered proposer."""
+    V = len(p)
+    out = [0] * V
+    for draw in product(range(V), repeat=len(qs)):
+        w = 1
+        for i, x in enumerate(draw):
+            w = w * qs[i][x]
+        if w == 0:
+            continue
+        if dedup:
+            first = {}
+            for i, x in enumerate(draw):
+                first.setdefault(x, i)
+            props = [(x, qs[i]) for x, i in sorted(first.items(), key=lambda t: t[1])]
+        else:
+            props = [(x, qs[i]) for i, x in enumerate(draw)]
+        d = node_output_dist(p, props)
+        for x in range(V):
+            out[x] += w * d[x]
+    return out
 
 
 def tv(a, b):

@@ -266,6 +266,132 @@ def verify_mss(parent, token, target_logits, ssm_probs, q_row, status, seed, off
 
 
 # ----------------------------------------------------------------------------
+# VerifyStochastic with several proposers per node (merged token trees)
+# ----------------------------------------------------------------------------
+# When several SSMs propose the same token at the same place, a merged token
+# tree holds one node for it (SpecInfer summary, "Token Tree Merge" and the
+# multi-SSM remark of VerifyStochastic).  VerifyStochastic tests a child with
+# the distribution of the SSM that proposed it; the variant here keeps every
+# proposal: a node proposed by m SSMs takes part in m rounds, each with its
+# proposer's draft row, exactly as if the m proposals were separate children
+# carrying the same token.  Accepting any of them enters the node; rejecting
+# one drops only that proposal.  With one proposal per node this is
+# VerifyStochastic itself, and for independent draws (one per SSM, each from
+# its own distribution) the emitted token follows P_LLM (Theorem 4.2), which
+# testing a merged node once does not give.
+#
+# A request's proposals are slots s = 0..S-1: prop_node[s] is the node
+# (-1: unused slot) and prop_row[s] its proposer's row of ssm_probs.  The
+# random proposal is the idx-th untested one in ascending slot order, idx as
+# for a child; the Philox counter still counts rounds at the node.
+def proposals_of(parent, prop_node, u):
+    """Slots whose node is a child of u (u = -1: the root), ascending slot order."""
+    return [s for s, c in enumerate(prop_node) if int(c) >= 0 and int(parent[int(c)]) == u]
+
+
+def _proposal_checks(parent_b, token_b, V, prop_node_b, prop_row_b, R):
+    """Status after the up-front checks: tokens of the tree's nodes in [0, V),
+    then every used slot names a node of the tree (not a padding slot) and a
+    draft row in [0, R)."""
+    st = _request_checks(parent_b, token_b, V)
+    if st != ST_OK:
+        return st
+    N = len(parent_b)
+    for c, r in zip(prop_node_b, prop_row_b):
+        c, r = int(c), int(r)
+        if c == -1:
+            continue
+        if not (0 <= c < N) or int(parent_b[c]) == -2 or not (0 <= r < R):
+            return ST_BAD_QROW
+    return ST_OK
+
+
+def mss_multi_one(b, parent, token, logits, ssm, prop_node, prop_row, seed, offset):
+    """VerifyStochastic over proposals for request b (assumes the checks
+    passed).  Returns (accepted nodes, bonus, rounds, status, trace) as
+    mss_one."""
+    accepted = []
+    trace = []
+    rounds = 0
+    u = -1
+    if not row_ok(logits[0]):
+        return accepted, -1, rounds, ST_NONFINITE, trace
+    p_cur = softmax_row(logits[0])
+    while True:
+        untested = proposals_of(parent, prop_node, u)
+        slot = u + 1
+        j = 0
+        moved = False
+        while untested:
+            w = philox.words(seed, offset, b, slot, j)
+            s = select_child(untested, w[0])
+            c = int(prop_node[s])
+            x = int(token[c])
+            qrow = np.asarray(ssm[prop_row[s]], dtype=np.float32).astype(np.float64)
+            q_x = qrow[x]
+            if not math.isfinite(q_x) or q_x < 0.0:
+                return accepted, -1, rounds, ST_NONFINITE, trace
+            ratio = ratio_of(p_cur[x], q_x)
+            u1 = philox.unit_open0(w[1])
+            rounds += 1
+            trace.append(("ratio", abs(u1 - ratio) if math.isfinite(ratio) else math.inf))
+            if u1 <= ratio:
+                accepted.append(c)
+                u = c
+                if not row_ok(logits[c + 1]):
+                    return accepted, -1, rounds, ST_NONFINITE, trace
+                p_cur = softmax_row(logits[c + 1])
+                moved = True
+                break
+            if not q_row_ok(qrow):
+                return accepted, -1, rounds, ST_NONFINITE, trace
+            p_new, z = residual(p_cur, qrow)
+            if z == 0.0:
+                trace.append(("zero_residual", 0.0))
+            p_cur = p_new
+            untested = [t for t in untested if t != s]
+            j += 1
+        if moved:
+            continue
+        w = philox.words(seed, offset, b, slot, 0)
+        x, margin = sample_from(p_cur, philox.unit_open0(w[2]))
+        trace.append(("sample", margin))
+        return accepted, x, rounds, ST_OK, trace
+
+
+def verify_mss_multi(parent, token, target_logits, ssm_probs, prop_node, prop_row, status, seed,
+                     offset=0):
+    """Batched VerifyStochastic over proposals; outputs as verify_mss.
+    prop_node, prop_row: [B][S] int arrays (S <= 64)."""
+    B, N = token.shape
+    V = target_logits.shape[2]
+    R = ssm_probs.shape[1]
+    acc = np.full((B, N), -1, dtype=np.int64)
+    num = np.full(B, -1, dtype=np.int64)
+    bonus = np.full(B, -1, dtype=np.int64)
+    rounds = np.full(B, -1, dtype=np.int64)
+    st = [int(x) for x in status]
+    traces = [[] for _ in range(B)]
+    for b in range(B):
+        if st[b] == ST_OK:
+            st[b] = _proposal_checks(parent[b], token[b], V, prop_node[b], prop_row[b], R)
+        if st[b] != ST_OK:
+            continue
+        path, bn, rd, s_b, tr = mss_multi_one(b, parent[b], token[b], target_logits[b], ssm_probs[b],
+                                              prop_node[b], prop_row[b], seed, offset)
+        traces[b] = tr
+        st[b] = s_b
+        if s_b != ST_OK:
+            continue
+        acc[b, : len(path)] = path
+        num[b] = len(path)
+        bonus[b] = bn
+        rounds[b] = rd
+    return dict(accepted=acc, num_accepted=num, bonus=bonus, rounds=rounds,
+                status=np.array(st), traces=traces)
+
+
+# ----------------------------------------------------------------------------
 # Naive sampling verification (Theorem 4.3's comparator)
 # ----------------------------------------------------------------------------
 def naive_reject_prob(p, child_tokens):

@@ -473,3 +473,45 @@ def iid_tree_batch(seed: int, n_req: int, p: np.ndarray, q: np.ndarray, shape: s
     sp = np.broadcast_to(q.astype(np.float32), (n_req, 1, V)).copy()
     q_row = np.zeros((n_req, N), dtype=np.int32)
     return np.array(parent, dtype=np.int32), draws, tl, sp, q_row
+
+
+def merged_tree_batch(seed: int, n_req: int, p: np.ndarray, qs: list):
+    """Many requests sharing one target distribution p; SSM i proposes one
+    root child drawn from its own distribution qs[i] (independent draws), and
+    proposals of the same token share one node (first appearance order).
+
+    Returns parent[N] with N = len(qs) (nodes past the request's distinct
+    tokens are padding, parent -2: the tree shape differs per request, so
+    parent is [n_req][N]), token[n_req][N], target_logits[n_req][N+1][V] =
+    log p, ssm_probs[n_req][R][V] with row i = qs[i], prop_node[n_req][S] and
+    prop_row[n_req][S] (S = len(qs): slot i is SSM i's proposal), and q_row
+    [n_req][N] = the row of each node's first proposer."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = len(qs)
+    V = len(p)
+    draws = np.zeros((n_req, k), dtype=np.int64)
+    for i, q in enumerate(qs):
+        cq = np.cumsum(np.asarray(q, dtype=np.float64))
+        cq[-1] = 1.0
+        draws[:, i] = np.minimum(np.searchsorted(cq, rng.random(n_req), side="right"), V - 1)
+    parent = np.full((n_req, k), -2, dtype=np.int32)
+    token = np.zeros((n_req, k), dtype=np.int32)
+    prop_node = np.zeros((n_req, k), dtype=np.int32)
+    prop_row = np.tile(np.arange(k, dtype=np.int32), (n_req, 1))
+    q_row = np.zeros((n_req, k), dtype=np.int32)
+    for b in range(n_req):
+        node_of = {}
+        for i in range(k):
+            x = int(draws[b, i])
+            if x not in node_of:
+                c = len(node_of)
+                node_of[x] = c
+                parent[b, c] = -1
+                token[b, c] = x
+                q_row[b, c] = i
+            prop_node[b, i] = node_of[x]
+    with np.errstate(divide="ignore"):
+        lp = np.log(np.asarray(p, dtype=np.float64)).astype(np.float32)
+    tl = np.broadcast_to(lp, (n_req, k + 1, V)).copy()
+    sp = np.broadcast_to(np.asarray(qs, dtype=np.float32), (n_req, k, V)).copy()
+    return parent, token, tl, sp, prop_node, prop_row, q_row
