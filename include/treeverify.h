@@ -233,6 +233,39 @@ tv_status kv_commit_accepted(tv_dtype dt, int B, int N, int H, int D, void* k_ca
                              int32_t* status, hipStream_t stream);
 
 /*
+ * tree_verify_mss_multi - VerifyStochastic on a merged token tree, every
+ * proposal its own round.
+ * Defines: SpecInfer summary, "Token Verification: Stochastic Decoding and
+ * Multi-Step Speculative Sampling (VerifyStochastic)" (a child is tested
+ * with the distribution of the SSM that proposed it) and "Token Tree Merge"
+ * (proposals of the same token share one node).  A node proposed by m SSMs
+ * takes part in m rounds, each with its proposer's draft row; accepting any
+ * of them enters the node, rejecting one drops only that proposal.  With
+ * independent draws, one per SSM, the emitted token then follows P_LLM
+ * (Theorem 4.2), which testing a merged node once does not give.
+ *
+ *   prop_node [B][S] int32  node of proposal slot s, -1 = unused slot
+ *   prop_row  [B][S] int32  its proposer's row of ssm_probs
+ *   S <= 64 slots per request.  At node u the untested proposals of u's
+ *   children are taken in ascending slot order; the random proposal, the
+ *   Philox counter, the ratio test, the residual and the final sample are
+ *   tree_verify_mss's with "child" read as "proposal" (j counts rounds at u).
+ *   With slot s = node s and prop_row = q_row the results equal
+ *   tree_verify_mss's.
+ * Other arguments, outputs and workspace as tree_verify_mss (q_row is
+ * replaced by the proposal lists).  status may also become TV_REQ_BAD_QROW
+ * when a used slot names a row outside [0, R) or no node of the tree.
+ * Errors: those of tree_verify_mss; TV_ETOOBIG for S > 64; TV_EINVAL for
+ * S < 0 or missing proposal arrays.
+ */
+tv_status tree_verify_mss_multi(int B, int N, int S, int V, int R, const float* target_logits,
+                                const float* ssm_probs, const int32_t* prop_node, const int32_t* prop_row,
+                                const int32_t* token, const uint64_t* child, int32_t* status,
+                                uint64_t seed, uint64_t offset, int32_t* accepted,
+                                int32_t* num_accepted, int32_t* bonus, int32_t* rounds,
+                                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * tree_verify_mss_commit - tree_verify_mss, then kv_commit_accepted of the
  * path it accepted, in one launch.
  * Defines: the two operations above (SpecInfer summary, "Token Verification:

@@ -101,6 +101,19 @@ class GpuRun:
                                   self.k, self.v, self.bt, self.pl)
         return self
 
+    def mss_multi(self, prop_node, prop_row, seed=None, offset=None):
+        """MSS over proposal lists (numpy [B][S] int arrays)."""
+        w = self.w
+        self.m_acc = torch.empty((w.B, w.N), dtype=torch.int32, device=DEV)
+        self.m_num = torch.empty((w.B,), dtype=torch.int32, device=DEV)
+        self.m_bonus = torch.empty((w.B,), dtype=torch.int32, device=DEV)
+        self.m_rounds = torch.empty((w.B,), dtype=torch.int32, device=DEV)
+        tv.tree_verify_mss_multi(self.tl, self.sp, to_dev(np.asarray(prop_node, dtype=np.int32)),
+                                 to_dev(np.asarray(prop_row, dtype=np.int32)), self.token, self.child, self.status,
+                                 w.seed if seed is None else seed, w.offset if offset is None else offset,
+                                 self.m_acc, self.m_num, self.m_bonus, self.m_rounds, self._ws_verify())
+        return self
+
     def naive(self, seed=None, offset=None):
         w = self.w
         self.n_acc = torch.empty((w.B, w.N), dtype=torch.int32, device=DEV)

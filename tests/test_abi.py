@@ -103,6 +103,16 @@ def test_host_argument_checks(L):
     assert mss_commit(kc=False) == TV_EINVAL
     assert mss_commit(ws_bytes=wsv - 1) == TV_EWORKSPACE
 
+    def multi(S=3, R=2, pn=True):
+        return L.tree_verify_mss_multi(2, 5, S, 1000, R, _p(), _p(), _p() if pn else None, _p(), _p(), _p(), _p(),
+                                       1, 0, _p(), _p(), _p(), None, _p(), wsv, None)
+    assert multi(S=65) == TV_ETOOBIG
+    assert multi(S=-1) == TV_EINVAL
+    assert multi(R=0) == TV_EINVAL
+    assert multi(pn=False) == TV_EINVAL
+    assert L.tree_verify_mss_multi(2, 5, 3, 1000, 2, _p(), _p(), _p(), _p(), _p(), _p(), _p(), 1, 0, _p(), _p(),
+                                   _p(), None, _p(), wsv - 1, None) == TV_EWORKSPACE
+
 
 def test_binding_names_match_exports():
     for n in tv_pkg.EXPORTS:

@@ -15,7 +15,7 @@ __all__ = [
     "tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
     "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss", "kv_commit_accepted",
     "tree_verify_naive", "tree_logits_transform", "TV_OUT_LOGITS", "TV_OUT_PROBS", "tv_status_string",
-    "tree_verify_mss_commit",
+    "tree_verify_mss_commit", "tree_verify_mss_multi",
 ]
 
 TV_F32 = 0
@@ -25,7 +25,7 @@ TV_OUT_PROBS = 1
 EXPORTS = ("tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
            "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss",
            "kv_commit_accepted", "tree_verify_naive", "tree_logits_transform", "tv_status_string",
-           "tree_verify_mss_commit")
+           "tree_verify_mss_commit", "tree_verify_mss_multi")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libtreeverify.so")
@@ -51,6 +51,7 @@ def _load():
         "kv_commit_accepted": ([I, I, I, I, I, P, P, I, I, P, I, P, P, P, P, P], I),
         "tree_verify_mss_commit": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ,
                                     I, I, I, P, P, I, I, P, I, P, P], I),
+        "tree_verify_mss_multi": ([I, I, I, I, I, P, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ, P], I),
         "tree_logits_transform": ([I, I, P, P, F, I, F, I, P], I),
         "tree_verify_naive": ([I, I, I, P, P, P, P, U64, U64, P, P, P, P, SZ, P], I),
         "tv_status_string": ([I], ctypes.c_char_p),
@@ -166,6 +167,19 @@ def tree_verify_mss_commit(target_logits, ssm_probs, q_row, token, child, status
                                       _ptr(workspace), ws_bytes, _dtype_code(k_cache), H, D, _ptr(k_cache),
                                       _ptr(v_cache), nb, bs, _ptr(block_table), block_table.shape[1],
                                       _ptr(prefix_len), _stream(stream)), "tree_verify_mss_commit")
+
+
+def tree_verify_mss_multi(target_logits, ssm_probs, prop_node, prop_row, token, child, status, seed, offset,
+                          accepted, num_accepted, bonus, rounds, workspace, stream=None):
+    """MSS over proposals: prop_node / prop_row [B][S] int32 (node -1 = unused slot)."""
+    B, N1, V = target_logits.shape
+    R = ssm_probs.shape[1]
+    S = prop_node.shape[1]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().tree_verify_mss_multi(B, N1 - 1, S, V, R, _ptr(target_logits), _ptr(ssm_probs), _ptr(prop_node),
+                                     _ptr(prop_row), _ptr(token), _ptr(child), _ptr(status), int(seed), int(offset),
+                                     _ptr(accepted), _ptr(num_accepted), _ptr(bonus), _ptr(rounds),
+                                     _ptr(workspace), ws_bytes, _stream(stream)), "tree_verify_mss_multi")
 
 
 def tree_verify_naive(target_logits, token, child, status, seed, offset, accepted, num_accepted, bonus,

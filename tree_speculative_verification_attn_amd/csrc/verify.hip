@@ -99,6 +99,10 @@ struct WalkArgs {
   uint64_t* kid;
   bool commit;              // MSS: also compact the accepted path in the KV cache
   tv::KvRef kv;             //   the cache, block table and prefix lengths
+  bool multi;               // MSS over proposals (several per node):
+  int S;                    //   slots per request
+  const int32_t* prop_node; //   [B][S] node of each proposal, -1 = unused slot
+  const int32_t* prop_row;  //   [B][S] its proposer's row of ssm
 };
 constexpr int kMoveChunks = 8;                     // 16-byte chunks per thread per batch of the move
 
@@ -198,6 +202,42 @@ __device__ __forceinline__ double block_sum_or(double v, int f, double (*red)[kC
 __device__ __forceinline__ bool q_bad(float q) { return !(q >= 0.f) || q == INFINITY; }
 
 // ---------------------------------------------------------------------------
+// Staging of a walk over proposals (MSS on merged trees), one wave: lane s is
+// proposal slot s and, as in the one-proposal staging, lane i is node i with
+// child mask cm and token tok.  A slot's node must be a node of the tree
+// (some node's child: `real`) and its row in [0, R); *bad is the ballot of
+// the used slots that are not.  child_slots of lane u + 1 is the mask of the
+// slots whose node is a child of u, so the walk picks among proposals
+// exactly as it picks among children when every node has one proposal.
+struct SlotStage {
+  uint64_t child_slots;
+  int node, tok, row;       // this lane's slot (node -1: unused or invalid)
+};
+__device__ SlotStage stage_slots(const WalkArgs& a, int b, int N, uint64_t cm, int tok, uint64_t real,
+                                 uint64_t* bad) {
+  const int lane = threadIdx.x & 63;
+  const size_t rb = static_cast<size_t>(b);
+  const int pn = lane < a.S ? a.prop_node[rb * a.S + lane] : -1;
+  const int pr = lane < a.S ? a.prop_row[rb * a.S + lane] : 0;
+  const bool node_ok = pn >= 0 && pn < N && ((real >> (pn & 63)) & 1ull);
+  *bad = __ballot(lane < a.S && pn != -1 && (!node_ok || pr < 0 || pr >= a.R));
+  SlotStage r;
+  r.node = node_ok ? pn : -1;
+  r.tok = __shfl(tok, node_ok ? pn : 0, 64);
+  r.row = node_ok ? pr : 0;
+  r.child_slots = 0ull;
+  const int last = min(N, 63);          // node 63 has no children
+  for (int uu = 0; uu <= last; ++uu) {
+    const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(static_cast<uint32_t>(cm)), uu, 64));
+    const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(static_cast<uint32_t>(cm >> 32)), uu, 64));
+    const uint64_t cmu = (static_cast<uint64_t>(hi) << 32) | lo;
+    const uint64_t m = __ballot(node_ok && ((cmu >> (pn & 63)) & 1ull));
+    if (lane == uu) r.child_slots = m;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // The walk kernel.  grid = (requests in this launch) * G, block = 256.
 //
 // Every wave of every workgroup of a request reads the same exchanged words
@@ -205,7 +245,7 @@ __device__ __forceinline__ bool q_bad(float q) { return !(q >= 0.f) || q == INFI
 // walk state lives in registers and a pass needs no barrier beyond those of
 // its workgroup reductions.
 // ---------------------------------------------------------------------------
-template <int MODE, bool VEC, bool COMMIT>
+template <int MODE, bool VEC, bool COMMIT, bool MULTI = false>
 __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   constexpr int NW = kCoThreads / 64;
   const int G = a.G;
@@ -223,7 +263,9 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   uint64_t* hdr = a.hdr + static_cast<size_t>(b) * 2 * G * kHdr;
   uint64_t* kid = a.kid + static_cast<size_t>(b) * 2 * 64;
 
-  __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES];
+  // per child (per proposal slot when MULTI): token and draft row; s_child[u + 1]
+  // the children (proposals) of u; s_node the slot's node (MULTI)
+  __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES], s_node[TV_MAX_NODES];
   __shared__ uint64_t s_child[TV_MAX_NODES + 1];
   __shared__ double s_red[2][NW];
   __shared__ int s_redf[2][NW];
@@ -274,19 +316,27 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     // child[N] (children of the last node) is empty after masking
     const uint64_t cm = lane < N ? a.child[rb * (N + 1) + lane] & later_nodes(lane - 1, N) : 0ull;
     const int tok = lane < N ? a.token[rb * N + lane] : 0;
-    const int qr = (mss && lane < N) ? a.q_row[rb * N + lane] : 0;
+    const int qr = (mss && !MULTI && lane < N) ? a.q_row[rb * N + lane] : 0;
     const uint64_t real = wave_or64(cm);     // padding slots are nobody's child: unchecked
     const uint64_t bad_tok = __ballot(lane < N && (tok < 0 || tok >= V));
-    const uint64_t bad_q = __ballot(mss && lane < N && (qr < 0 || qr >= a.R));
-    s_child[lane] = cm;
-    s_tok[lane] = tok;
-    s_qrow[lane] = qr;
+    uint64_t bad_q = __ballot(mss && !MULTI && lane < N && (qr < 0 || qr >= a.R)) & real;
+    if constexpr (MULTI) {
+      const SlotStage ss = stage_slots(a, b, N, cm, tok, real, &bad_q);
+      s_child[lane] = ss.child_slots;
+      s_tok[lane] = ss.tok;
+      s_qrow[lane] = ss.row;
+      s_node[lane] = ss.node;
+    } else {
+      s_child[lane] = cm;
+      s_tok[lane] = tok;
+      s_qrow[lane] = qr;
+    }
     if (lane == 0) {
       s_child[TV_MAX_NODES] = 0ull;
       int st = st0;
       if (st == TV_REQ_OK) {
         if (bad_tok & real) st = TV_REQ_BAD_TOKEN;
-        else if (bad_q & real) st = TV_REQ_BAD_QROW;
+        else if (bad_q) st = TV_REQ_BAD_QROW;
       }
       s_status0 = st;
       s_timeout = 0;
@@ -500,7 +550,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         qx_c = qrow_c[s_tok[cand]];
       }
       load8(qrow_c, qn, 0.f);
-      load8(lbase + static_cast<size_t>(cand + 1) * V, lvn, -INFINITY);
+      load8(lbase + static_cast<size_t>((MULTI ? s_node[cand] : cand) + 1) * V, lvn, -INFINITY);
     }
     const uint32_t tag = static_cast<uint32_t>(ex_no + 1);
     const int par = ex_no & 1;
@@ -604,7 +654,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     // later, after that barrier.)
     if (wave == kPollWave) {
       bool to = false;
-      if (pass == P_RESID && lane < N && ((U >> lane) & 1ull)) {
+      if (pass == P_RESID && (MULTI || lane < N) && ((U >> lane) & 1ull)) {
         uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
         if (!take_tagged<1>(kid + par * 64 + lane, tag, v)) to = true;
         s_rx2[par][lane] = __uint_as_float(v[0]);
@@ -691,7 +741,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       fail = tv::wave_or_dpp(ab) != 0;
       if (!fail && Znew > 0.0) {       // else the distribution stays (zero-normaliser guard)
         for (int gg = lane; gg < G; gg += 64) s_gt[wave][gg] = s_gs[par][gg];
-        if (lane < N && ((U >> lane) & 1ull)) rx = s_rx2[par][lane];
+        if ((MULTI || lane < N) && ((U >> lane) & 1ull)) rx = s_rx2[par][lane];
 #pragma unroll
         for (int e = 0; e < kElem; ++e) cv[e] = rn[e];
         Z = Znew;
@@ -712,10 +762,11 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
           const bool accept = qx_c > 0.f ? tv::unit_open0(w.y) * static_cast<double>(qx_c) * Z <= e : e > 0.0;
           ++rounds;
           if (accept) {
-            if (t == 0) s_acc[k] = cand;
+            const int node = MULTI ? s_node[cand] : cand;   // the proposal's node
+            if (t == 0) s_acc[k] = node;
             ++k;
-            u = cand;
-            U = s_child[cand + 1];
+            u = node;
+            U = s_child[node + 1];
             j = 0;
             pass = P_ENTER;
           } else {
@@ -839,7 +890,7 @@ constexpr int kRowWaves = kRowThreads / 64;
 constexpr int kRowQuad = 4 * kRowThreads;        // entries covered by one register quad
 constexpr int kRowMaxE = 32;                     // registers per row per thread
 
-template <int E, bool VEC, int MODE, bool COMMIT>
+template <int E, bool VEC, int MODE, bool COMMIT, bool MULTI = false>
 __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
   static_assert(E % 4 == 0 && E <= kRowMaxE, "row registers");
   constexpr int C = E / 4;
@@ -850,8 +901,10 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
   const float* lbase = a.logits + static_cast<size_t>(b) * (N + 1) * V;
   const float* sbase = mss ? a.ssm + static_cast<size_t>(b) * a.R * V : nullptr;
 
-  __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES];
-  __shared__ float s_qx[TV_MAX_NODES];           // MSS: each node's draft probability of its token
+  // per child (per proposal slot when MULTI): token, draft row, draft
+  // probability of the token; s_node the slot's node (MULTI)
+  __shared__ int s_tok[TV_MAX_NODES], s_qrow[TV_MAX_NODES], s_acc[TV_MAX_NODES], s_node[TV_MAX_NODES];
+  __shared__ float s_qx[TV_MAX_NODES];
   __shared__ uint64_t s_child[TV_MAX_NODES + 1];
   __shared__ float s_wm[2][kRowWaves];           // per-wave max, two banks
   __shared__ int s_wa[2][kRowWaves], s_wf[2][kRowWaves];
@@ -1029,22 +1082,32 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
     const int st0 = lane == 0 ? a.status[b] : 0;
     const uint64_t cm = lane < N ? a.child[rb * (N + 1) + lane] & later_nodes(lane - 1, N) : 0ull;
     const int tok = lane < N ? a.token[rb * N + lane] : 0;
-    const int qr = (mss && lane < N) ? a.q_row[rb * N + lane] : 0;
+    const int qr = (mss && !MULTI && lane < N) ? a.q_row[rb * N + lane] : 0;
     const uint64_t real = wave_or64(cm);
     const uint64_t bad_tok = __ballot(lane < N && (tok < 0 || tok >= V));
-    const uint64_t bad_q = __ballot(mss && lane < N && (qr < 0 || qr >= a.R));
-    s_child[lane] = cm;
-    s_tok[lane] = tok;
-    s_qrow[lane] = qr;
+    uint64_t bad_q = __ballot(mss && !MULTI && lane < N && (qr < 0 || qr >= a.R)) & real;
     // every tested child's ratio needs q(token): load them all now, in parallel
-    const bool ok_q = mss && lane < N && tok >= 0 && tok < V && qr >= 0 && qr < a.R;
-    s_qx[lane] = ok_q ? sbase[static_cast<size_t>(qr) * V + tok] : 0.f;
+    if constexpr (MULTI) {
+      const SlotStage ss = stage_slots(a, b, N, cm, tok, real, &bad_q);
+      s_child[lane] = ss.child_slots;
+      s_tok[lane] = ss.tok;
+      s_qrow[lane] = ss.row;
+      s_node[lane] = ss.node;
+      const bool ok_q = ss.node >= 0 && ss.tok >= 0 && ss.tok < V;
+      s_qx[lane] = ok_q ? sbase[static_cast<size_t>(ss.row) * V + ss.tok] : 0.f;
+    } else {
+      s_child[lane] = cm;
+      s_tok[lane] = tok;
+      s_qrow[lane] = qr;
+      const bool ok_q = mss && lane < N && tok >= 0 && tok < V && qr >= 0 && qr < a.R;
+      s_qx[lane] = ok_q ? sbase[static_cast<size_t>(qr) * V + tok] : 0.f;
+    }
     if (lane == 0) {
       s_child[TV_MAX_NODES] = 0ull;
       int st = st0;
       if (st == TV_REQ_OK) {
         if (bad_tok & real) st = TV_REQ_BAD_TOKEN;
-        else if (bad_q & real) st = TV_REQ_BAD_QROW;
+        else if (bad_q) st = TV_REQ_BAD_QROW;
       }
       s_status0 = st;
       if constexpr (COMMIT) s_L = a.kv.prefix_len[b];   // nothing writes it before the move
@@ -1270,10 +1333,11 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(WalkArgs a) {
       const bool accept = qx > 0.f ? tv::unit_open0(w.y) * static_cast<double>(qx) * Z <= e : e > 0.0;
       ++rounds;
       if (accept) {
-        if (t == 0) s_acc[k] = cand;
+        const int node = MULTI ? s_node[cand] : cand;   // the proposal's node
+        if (t == 0) s_acc[k] = node;
         ++k;
-        u = cand;
-        U = s_child[cand + 1];
+        u = node;
+        U = s_child[node + 1];
         j = 0;
         load_row(lbase + static_cast<size_t>(u + 1) * V, lv, -INFINITY);
         choose();
@@ -1355,9 +1419,10 @@ tv_status check_verify_args(int B, int N, int V) {
 
 // Workgroups of the walk kernel that fit on the device at once (cached per
 // device and mode: it depends only on the kernel and the device).
-// kernel variant: 0 greedy, 1 MSS, 2 naive, 3 MSS + commit
+// kernel variant: 0 greedy, 1 MSS, 2 naive, 3 MSS + commit, 4 MSS over proposals
 template <bool VEC>
 const void* walk_kernel_of(int variant) {
+  if (variant == 4) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, false, true>);
   if (variant == 3) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, true>);
   if (variant == MODE_MSS) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, false>);
   if (variant == MODE_NAIVE) return reinterpret_cast<const void*>(walk_kernel<MODE_NAIVE, VEC, false>);
@@ -1365,8 +1430,8 @@ const void* walk_kernel_of(int variant) {
 }
 
 int walk_capacity(int dev, int variant, bool vec) {
-  static int cache[2][4][64];
-  const bool cached = dev >= 0 && dev < 64 && variant >= 0 && variant < 4;
+  static int cache[2][5][64];
+  const bool cached = dev >= 0 && dev < 64 && variant >= 0 && variant < 5;
   if (cached && cache[vec][variant][dev] > 0) return cache[vec][variant][dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
@@ -1379,7 +1444,9 @@ int walk_capacity(int dev, int variant, bool vec) {
 
 template <bool VEC>
 void launch_sliced_vec(const WalkArgs& a, int grid, hipStream_t stream) {
-  if (a.mode == MODE_MSS && a.commit)
+  if (a.mode == MODE_MSS && a.multi)
+    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, false, true>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+  else if (a.mode == MODE_MSS && a.commit)
     hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, true>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else if (a.mode == MODE_MSS)
     hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, false>), dim3(grid), dim3(kCoThreads), 0, stream, a);
@@ -1394,16 +1461,17 @@ void launch_sliced(const WalkArgs& a, int grid, bool vec, hipStream_t stream) {
   else launch_sliced_vec<false>(a, grid, stream);
 }
 
-template <int E, int MODE, bool COMMIT = false>
+template <int E, int MODE, bool COMMIT = false, bool MULTI = false>
 void launch_row_mode(const WalkArgs& a, int B, bool vec, hipStream_t stream) {
   if (vec)
-    hipLaunchKernelGGL((walk_row_kernel<E, true, MODE, COMMIT>), dim3(B), dim3(kRowThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_row_kernel<E, true, MODE, COMMIT, MULTI>), dim3(B), dim3(kRowThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((walk_row_kernel<E, false, MODE, COMMIT>), dim3(B), dim3(kRowThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_row_kernel<E, false, MODE, COMMIT, MULTI>), dim3(B), dim3(kRowThreads), 0, stream, a);
 }
 template <int E>
 void launch_row(const WalkArgs& a, int B, bool vec, hipStream_t stream) {
-  if (a.mode == MODE_MSS && a.commit) launch_row_mode<E, MODE_MSS, true>(a, B, vec, stream);
+  if (a.mode == MODE_MSS && a.multi) launch_row_mode<E, MODE_MSS, false, true>(a, B, vec, stream);
+  else if (a.mode == MODE_MSS && a.commit) launch_row_mode<E, MODE_MSS, true>(a, B, vec, stream);
   else if (a.mode == MODE_MSS) launch_row_mode<E, MODE_MSS>(a, B, vec, stream);
   else if (a.mode == MODE_NAIVE) launch_row_mode<E, MODE_NAIVE>(a, B, vec, stream);
   else launch_row_mode<E, MODE_GREEDY>(a, B, vec, stream);
@@ -1425,7 +1493,8 @@ tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
   const int G = a.G;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TV_EHIP;
-  const int capacity = walk_capacity(dev, a.mode == MODE_MSS && a.commit ? 3 : a.mode, vec);
+  const int variant = a.mode != MODE_MSS ? a.mode : (a.multi ? 4 : (a.commit ? 3 : MODE_MSS));
+  const int capacity = walk_capacity(dev, variant, vec);
   if (capacity <= 0) return TV_EHIP;
   if (G > capacity) return TV_EINVAL;
   const int per_launch = capacity / G;
@@ -1554,6 +1623,40 @@ extern "C" tv_status tree_verify_mss_commit(int B, int N, int V, int R, const fl
   a.kv.block_table = block_table;
   a.kv.max_blocks = max_blocks;
   a.kv.prefix_len = prefix_len;
+  return launch_walk(a, B, stream);
+}
+
+extern "C" tv_status tree_verify_mss_multi(int B, int N, int S, int V, int R, const float* target_logits,
+                                           const float* ssm_probs, const int32_t* prop_node,
+                                           const int32_t* prop_row, const int32_t* token, const uint64_t* child,
+                                           int32_t* status, uint64_t seed, uint64_t offset, int32_t* accepted,
+                                           int32_t* num_accepted, int32_t* bonus, int32_t* rounds, void* workspace,
+                                           size_t ws_bytes, hipStream_t stream) {
+  const tv_status c = check_verify_args(B, N, V);
+  if (c != TV_OK) return c;
+  if (S < 0 || S > TV_MAX_NODES) return S < 0 ? TV_EINVAL : TV_ETOOBIG;
+  if (R < 1) return TV_EINVAL;
+  if (B == 0) return TV_OK;
+  if (!target_logits || !ssm_probs || !child || !status || !num_accepted || !bonus ||
+      (N > 0 && (!token || !accepted)) || (S > 0 && (!prop_node || !prop_row)))
+    return TV_EINVAL;
+  if (!workspace || ws_bytes < ws_layout(B, V).total) return TV_EWORKSPACE;
+  WalkArgs a = make_args(MODE_MSS, N, V, R, workspace, B);
+  a.logits = target_logits;
+  a.ssm = ssm_probs;
+  a.token = token;
+  a.child = child;
+  a.status = status;
+  a.seed = seed;
+  a.offset = offset;
+  a.accepted = accepted;
+  a.num_accepted = num_accepted;
+  a.bonus = bonus;
+  a.rounds = rounds;
+  a.multi = true;
+  a.S = S;
+  a.prop_node = prop_node;
+  a.prop_row = prop_row;
   return launch_walk(a, B, stream);
 }
 
