@@ -192,7 +192,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
 
   // per group: kRing stage buffers, each [K tile | V tile]
   __shared__ __attribute__((aligned(16))) uint8_t ring[kGroups * kRing * 2 * TILE];
+  // per group: a copy of the (request, head)'s Q rows, in the K tiles' layout
+  constexpr int QROWS = 16 * NQT;
+  constexpr int QBYTES = QROWS * D * 2;
+  static_assert(QBYTES % 1024 == 0, "Q copy in whole wave loads");
+  __shared__ __attribute__((aligned(16))) uint8_t sq[kGroups * QBYTES];
   __shared__ int s_hung;
+  __shared__ int s_wflag[kAttnThreads / 64];      // per wave: 1 = request skipped, 2 = bad block id
   __shared__ int s_gbar[kGroups];
   __shared__ int s_next;                    // next stage of the chunk not yet claimed
   __shared__ int s_sel[kGroups][2];         // stage a group's wave 0 claimed for the group
@@ -226,17 +232,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   const int qt = (gw - grp) & 3;
   const bool computes = qt < NQT;
   const int n_q = 16 * qt + lr;
-  bf16x8 qv[KC];
+  bf16x8 qv[KC];            // this wave's Q tile: read from the group's copy at its first stage
   uint64_t ancq = 0;
-#pragma unroll
-  for (int c = 0; c < KC; ++c) qv[c] = as_bf16x8(make_uint4(0, 0, 0, 0));
-  if (computes && n_q < N) {
-    ancq = a.anc[static_cast<size_t>(b) * N + n_q];
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-      qv[c] = as_bf16x8(*reinterpret_cast<const uint4*>(
-          qg + ((static_cast<size_t>(b) * N + n_q) * a.H + h) * D + 32 * c + 8 * lg));
-  }
+  if (computes && n_q < N) ancq = a.anc[static_cast<size_t>(b) * N + n_q];
   // Block ids of every block the chunk can cover, before the prefix length
   // is known (the table index is clamped to the table).  Ids outside
   // [0, num_blocks) are stored as 0, so every K/V load stays in bounds; the
@@ -293,14 +291,40 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     s_hung = 0;
     s_next = kGroups * kRing;               // the ones before are handed out statically below
   }
-  // (__syncthreads_or is a logical OR: one call per flag)
-  if (__syncthreads_or(st != TV_REQ_OK)) {  // a skipped request: zero output
+  // The workgroup agrees on the status (another workgroup of the request
+  // may flag a bad block meanwhile) and on the bad-block flag with one
+  // barrier: each wave leaves its flags in a slot of its own.
+  const bool wave_bad = __any(bad);          // (voted by the whole wave)
+  if (lane == 0) s_wflag[wave] = (st != TV_REQ_OK ? 1 : 0) | (wave_bad ? 2 : 0);
+  __syncthreads();
+  int wflags = 0;
+#pragma unroll
+  for (int w = 0; w < kAttnThreads / 64; ++w) wflags |= s_wflag[w];
+  if (wflags & 1) {                          // a skipped request: zero output
     if (s == 0) zero_out<uint16_t>(a, b, h);
     return;
   }
-  const int badblk = __syncthreads_or(bad);
+  const int badblk = wflags & 2;
 
   uint8_t* gring = ring + grp * kRing * 2 * TILE;   // this group's stage buffers
+  uint8_t* gq = sq + grp * QBYTES;                   // this group's Q copy
+
+  // The group's Q copy goes HBM -> LDS by direct-to-LDS loads issued just
+  // before the group's first stages, so Q is not waited for at the start: a
+  // stage's wait (loads complete in issue order) covers the copy, and each
+  // wave reads its tile from it at its first stage.  Rows past N repeat row
+  // N - 1 (the tile reads zero them).
+  auto issue_q = [&]() {
+    constexpr int RPL = 1024 / (2 * D);            // rows per 1 KB wave load
+    for (int li = gw; li < QBYTES / 1024; li += 4) {
+      const int row = li * RPL + lane / CPR, phys = lane % CPR;
+      const int n = min(row, N - 1);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(qg + ((static_cast<size_t>(b) * N + n) * a.H + h) * D) +
+                           swz<D>(row, phys) * 16;
+      const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(gq + li * 1024));
+      asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds_addr) : "memory");
+    }
+  };
 
   // Issue this wave's share of chunk stage `st` into `dst` (K tile then V
   // tile).  Each 1 KB load covers 64/CPR consecutive keys of one cache
@@ -491,6 +515,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   // of the stage before, which is then refilled with the newly claimed
   // stage, in flight during this stage's compute.
   int held[kRing];
+  issue_q();
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
     held[r] = grp + kGroups * r;
@@ -512,6 +537,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       const int nx = s_sel[grp][it & 1];
       held[kRing - 1] = nx;
       if (nx >= 0 && nx < nst) issue(nx, gring + ((it + kRing - 1) % kRing) * 2 * TILE);
+    }
+    if (it == 0 && computes) {
+      // the group's Q copy has landed (its loads precede this stage's)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        qv[c] = n_q < N ? as_bf16x8(*reinterpret_cast<const uint4*>(gq + tile_off<D>(n_q, 4 * c + lg)))
+                        : as_bf16x8(make_uint4(0, 0, 0, 0));
     }
     if (computes) compute(held[0], gring + (it % kRing) * 2 * TILE);
 #pragma unroll
