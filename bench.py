@@ -2,14 +2,18 @@
 
 A step is the whole verification path over one batch of synthetic input:
 tree_build_mask -> tree_attn_verify -> tree_verify_greedy -> tree_verify_mss
--> kv_commit_accepted, the last two as one tree_verify_mss_commit launch
-(which gives exactly their results).  The default workload is the LLaMA-7B-shaped layer
+-> kv_commit_accepted, in three launches: tree_mask_attn_verify (the masks
+and the attention, with the results of the first two calls) and
+tree_verify_mss_commit (the results of the last two).  The default workload is the LLaMA-7B-shaped layer
 (bf16, 8 requests x 32 heads x 128 dims, 1024-token prefixes, a 46-node
 expansion tree <2,2,2,1,1,1,1>, fp32 logits over a 32000-token vocabulary).
 
 Inputs stay resident in HBM.  Because one step's data (~250 MB) would fit in
 the 256 MB Infinity Cache, the timed loop rotates over several copies of the
 inputs whose total exceeds twice that cache, so each step reads from HBM.
+The commit grows each copy's prefix lengths; the timed graphs hold one step
+per copy and then one copy that restores every copy's prefix lengths, so each
+step sees the same workload.
 
 Prints ONE JSON line (rank 0, N = 1): throughput in verified tree tokens/s
 (B * N tree nodes per step), the roofline of the dominant kernel (attention,
@@ -59,6 +63,12 @@ def attn_bytes(w):
     return kv + qo
 
 
+def mask_bytes(w):
+    """Algorithmic bytes of the mask part of tree_mask_attn_verify: parents
+    read, ancestor and child masks, depths and status written, once each."""
+    return w.B * w.N * 4 + w.B * w.N * 8 + w.B * (w.N + 1) * 8 + w.B * w.N * 4 + w.B * 4
+
+
 def logit_bytes(w):
     """Algorithmic bytes of one verify call: every target row read once."""
     return w.B * (w.N + 1) * w.V * 4
@@ -98,7 +108,10 @@ def main():
                            tl=to_dev(w.target_logits), sp=to_dev(w.ssm_probs)))
     bt = to_dev(w.block_table)
     pl0 = to_dev(w.prefix_len)
-    pl = pl0.clone()
+    pl0_all = pl0.repeat(n_copies, 1)
+    pl_all = pl0_all.clone()                  # row c: prefix lengths of input copy c
+    for c, cp in enumerate(copies):
+        cp["pl"] = pl_all[c]
     parent = to_dev(w.parent)
     token = to_dev(w.token)
     qr = to_dev(w.q_row)
@@ -120,21 +133,22 @@ def main():
     m_rounds = torch.empty((B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, ev=None, restore=True):
         c = copies[i % n_copies]
         cur = torch.cuda.current_stream()              # the capture stream inside a graph
-        pl.copy_(pl0)                                  # the commit of the last step grew it
+        if restore:
+            c["pl"].copy_(pl0)                         # the last commit on this copy grew it
         if ev: ev[0].record(cur)
-        tv.tree_build_mask(parent, anc, child, depth, status)
+        # the masks and the attention, in one launch
+        tv.tree_mask_attn_verify(c["q"], c["k"], c["v"], bt, c["pl"], parent, anc, child, depth, status, out,
+                                 ws_attn, scale=w.scale)
         if ev: ev[1].record(cur)
-        tv.tree_attn_verify(c["q"], c["k"], c["v"], bt, pl, anc, status, out, ws_attn, scale=w.scale)
-        if ev: ev[2].record(cur)
         tv.tree_verify_greedy(c["tl"], token, child, status, g_acc, g_num, g_bonus, ws_v)
-        if ev: ev[3].record(cur)
+        if ev: ev[2].record(cur)
         # MSS and the compaction of its path, in one launch
         tv.tree_verify_mss_commit(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset + i, m_acc,
-                                  m_num, m_bonus, m_rounds, ws_v, c["k"], c["v"], bt, pl)
-        if ev: ev[4].record(cur)
+                                  m_num, m_bonus, m_rounds, ws_v, c["k"], c["v"], bt, c["pl"])
+        if ev: ev[3].record(cur)
 
     for i in range(args.warmup):
         step(i)
@@ -148,36 +162,49 @@ def main():
 
     # Eager pass with HIP events between the calls: per-call times on the
     # launch stream (the attention figure feeds the roofline).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    names = ["mask", "attn", "greedy", "mss_commit"]
+    names = ["mask_attn", "greedy", "mss_commit"]
     comp = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
             for k, n in enumerate(names)}
     assert int((status != 0).sum()) == 0, "a request failed during the benchmark"
 
-    # The timed loop: one HIP graph per input copy holds the whole step, so
-    # the host issues one launch per step.
-    graphs = []
+    # The timed loop: a HIP graph holds one step per input copy and then one
+    # copy restoring every copy's prefix lengths; steps left over run from
+    # one-step graphs that restore their own copy first.
+    cycle, singles = None, []
     if not args.eager:
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle):
+            for c in range(n_copies):
+                step(c, restore=False)
+            pl_all.copy_(pl0_all)
         for c in range(n_copies):
             gph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gph):
                 step(c)
-            graphs.append(gph)
-        for gph in graphs:
+            singles.append(gph)
+        cycle.replay()
+        for gph in singles:
             gph.replay()
+        pl_all.copy_(pl0_all)
         torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % n_copies].replay()
-        else:
+    if cycle is not None:
+        i = 0
+        while i + n_copies <= args.steps:
+            cycle.replay()
+            i += n_copies
+        for j in range(i, args.steps):
+            singles[j % n_copies].replay()
+    else:
+        for i in range(args.steps):
             step(args.warmup + args.steps + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -203,13 +230,18 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * 2 * n_copies)
 
-    t_attn = per_call_ms(lambda c: tv.tree_attn_verify(c["q"], c["k"], c["v"], bt, pl0, anc, status, out, ws_attn,
-                                                       scale=w.scale))
+    pl_all.copy_(pl0_all)
+    # the step's attention launch (masks built in the kernel), and the
+    # attention alone for the comparison with per-path attention
+    t_attn = per_call_ms(lambda c: tv.tree_mask_attn_verify(c["q"], c["k"], c["v"], bt, pl0, parent, anc, child,
+                                                            depth, status, out, ws_attn, scale=w.scale))
+    t_attn_only = per_call_ms(lambda c: tv.tree_attn_verify(c["q"], c["k"], c["v"], bt, pl0, anc, status, out,
+                                                            ws_attn, scale=w.scale))
     t_mss = per_call_ms(lambda c: tv.tree_verify_mss(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset,
                                                      m_acc, m_num, m_bonus, m_rounds, ws_v))
     assert int((status != 0).sum()) == 0, "a request failed during the benchmark"
     variants = verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status, ws_v, t_mss)
-    a_bytes = attn_bytes(w)
+    a_bytes = attn_bytes(w) + mask_bytes(w)
     l_bytes = logit_bytes(w)
     attn_gbs = a_bytes / (t_attn * 1e-3) / 1e9
     mss_gbs = l_bytes / (t_mss * 1e-3) / 1e9
@@ -232,12 +264,13 @@ def main():
                    "tree": str(w.meta.get("tree")), "batch": B, "tree_nodes": N,
                    "prefix_len": int(w.prefix_len.max()), "vocab": V,
                    "input_copies_rotated": n_copies},
-        "roofline": {"bound": "hbm", "kernel": "tree_attn_verify", "achieved": round(attn_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "tree_mask_attn_verify", "achieved": round(attn_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name), "algorithmic_bytes": a_bytes,
-                     "ms_per_launch": round(t_attn, 5)},
+                     "ms_per_launch": round(t_attn, 5),
+                     "tree_attn_verify_ms_per_launch": round(t_attn_only, 5)},
         "eager_components_ms": {k: round(v, 5) for k, v in comp.items()},
-        "launch": "eager" if args.eager else "hip_graph_per_step",
+        "launch": "eager" if args.eager else f"hip_graph_per_{n_copies}_steps",
         "eager_ms_per_step": round(eager_ms, 5),
         "mss": {"ms_per_launch": round(t_mss, 5), "achieved_GBps_on_logit_bytes": round(mss_gbs, 1),
                 "frac": round(mss_gbs / HBM_PEAK_GBS, 4), "logit_bytes": l_bytes,
@@ -245,7 +278,7 @@ def main():
                 "mean_tokens_emitted_per_request": round(acc_tokens, 3)},
     }
     res["verify_variants"] = variants
-    res["tree_vs_sequence"] = tree_vs_sequence(torch, tv, w, copies, bt, t_attn, stream)
+    res["tree_vs_sequence"] = tree_vs_sequence(torch, tv, w, copies, bt, t_attn_only, stream)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, value)
     print(json.dumps(res))
@@ -402,7 +435,8 @@ def copy_calibration(torch, mib):
 
 
 ATTN_SOURCES = ("tree_speculative_verification_attn_amd/csrc/attn.hip",
-                "tree_speculative_verification_attn_amd/csrc/tv_common.h")
+                "tree_speculative_verification_attn_amd/csrc/tv_common.h",
+                "tree_speculative_verification_attn_amd/csrc/tree_mask.h")
 
 
 def attn_source_hash():
@@ -415,7 +449,7 @@ def attn_source_hash():
 
 
 def measured_traffic(workload):
-    """HBM bytes per tree_attn_verify launch from the committed counter
+    """HBM bytes per attention launch of the step from the committed counter
     summary of this workload, or None when there is none or the attention
     sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"tree_attn_verify_{workload}_traffic.md")

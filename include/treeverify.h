@@ -120,7 +120,10 @@ tv_status tree_build_mask(int B, int N, const int32_t* parent, uint64_t* anc,
  *   status        [B] int32 in/out: requests with status != 0 get zero output;
  *                 the call may set TV_REQ_KV_CAPACITY or TV_REQ_BAD_BLOCK
  *                 (then that request's output is unspecified)
- *   out           [B][N][H][D]
+ *   out           [B][N][H][D]; for bf16, a (request, head) whose keys span
+ *                 more than 6 stages of 32 keys per chunk sums them in an order
+ *                 set at run time, so repeated calls agree to rounding, not bit
+ *                 for bit
  *   workspace     ws_bytes >= tree_attn_verify_workspace(...) bytes of device
  *                 memory for per-chunk partial results (may be null when that
  *                 size is 0); contents on entry do not matter.  Calls that
@@ -136,6 +139,36 @@ tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
                            int max_blocks, const int32_t* prefix_len, const uint64_t* anc,
                            int32_t* status, void* out, void* workspace, size_t ws_bytes,
                            hipStream_t stream);
+
+/*
+ * tree_mask_attn_verify - tree_build_mask followed by tree_attn_verify, in one
+ * launch where it can.
+ * Defines: the TreeMask equation and Definition 4.1 with Equations 1-4 of the
+ * SpecInfer summary, as for the two calls it stands for.
+ *
+ * Results (anc, child, depth, status, out) are those of
+ *   tree_build_mask(B, N, parent, anc, child, depth, status);
+ *   tree_attn_verify(..., prefix_len, anc, status, out, workspace, ...);
+ * so status is written, not read: TV_REQ_BAD_PARENT, TV_REQ_KV_CAPACITY,
+ * TV_REQ_BAD_BLOCK or TV_REQ_OK (a request that fails a check gets the later
+ * call's treatment: zero output for a malformed tree or a prefix past the
+ * table, unspecified output for a bad block id).  With bf16 and a chunk plan of
+ * one chunk per (request, head) (tree_attn_verify_workspace gives 0) it is one
+ * kernel: every workgroup derives its request's masks from parent; otherwise
+ * the two kernels run one after the other.  N = 0 only builds the (empty) masks.
+ *
+ *   parent        [B][N] int32 in; anc [B][N], child [B][N+1] uint64, depth
+ *                 [B][N] int32 out, as tree_build_mask
+ *   others        as tree_attn_verify (anc is not read)
+ * Errors: those of the two calls; every argument is checked before anything
+ * is launched, so an error return leaves every buffer unchanged.
+ */
+tv_status tree_mask_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                int num_blocks, int block_size, const int32_t* block_table,
+                                int max_blocks, const int32_t* prefix_len, const int32_t* parent,
+                                uint64_t* anc, uint64_t* child, int32_t* depth, int32_t* status,
+                                void* out, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * tree_verify_greedy - VerifyGreedy.

@@ -59,6 +59,17 @@ class GpuRun:
                             self.ws_attn if ws else None, scale=w.scale)
         return self
 
+    def mask_attn(self):
+        """tree_mask_attn_verify: the masks and the attention in one call."""
+        w = self.w
+        code = tv.TV_BF16 if w.dtype == "bf16" else tv.TV_F32
+        ws = tv.tree_attn_verify_workspace(code, w.B, w.N, w.H, w.D, w.max_blocks)
+        self.ws_attn = torch.zeros(max(ws, 1), dtype=torch.uint8, device=DEV)
+        self.out = torch.empty_like(self.q)
+        tv.tree_mask_attn_verify(self.q, self.k, self.v, self.bt, self.pl, self.parent, self.anc, self.child,
+                                 self.depth, self.status, self.out, self.ws_attn if ws else None, scale=w.scale)
+        return self
+
     def _ws_verify(self):
         """One verify workspace for every verify call of this run: zeroed once
         at allocation, and each completed call leaves it zeroed again."""

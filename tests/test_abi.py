@@ -73,6 +73,23 @@ def test_host_argument_checks(L):
     assert L.tree_attn_verify_workspace(1, 2, 5, 2, 128, 4) == 0     # one chunk: no workspace
     del args
 
+    def fused(dt=1, B=2, D=128, N=5, bs=16, ws=None, ws_bytes=0, mb=4, par=True, anc=True, ch=True, st=True):
+        return L.tree_mask_attn_verify(dt, B, N, 2, D, 0.1, _p(), _p(), _p(), 10, bs, _p(), mb, _p(),
+                                       _p() if par else None, _p() if anc else None, _p() if ch else None,
+                                       _p(), _p() if st else None, _p(), ws, ws_bytes, None)
+    assert fused(dt=7) == TV_EDTYPE
+    assert fused(D=96) == TV_EINVAL
+    assert fused(bs=8) == TV_EINVAL
+    assert fused(N=70) == TV_ETOOBIG
+    assert fused(par=False) == TV_EINVAL
+    assert fused(anc=False) == TV_EINVAL
+    assert fused(ch=False) == TV_EINVAL
+    assert fused(st=False) == TV_EINVAL
+    assert fused(N=0, ch=False) == TV_EINVAL
+    assert fused(B=0, par=False, ch=False) == TV_OK
+    assert fused(mb=400) == TV_EWORKSPACE
+    assert fused(mb=400, ws=_p(), ws_bytes=need - 1) == TV_EWORKSPACE
+
     wsv = L.tree_verify_workspace(2, 5, 1000)
     assert wsv > 0
     assert L.tree_verify_workspace(2, 65, 1000) == 0

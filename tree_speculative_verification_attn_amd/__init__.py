@@ -15,7 +15,7 @@ __all__ = [
     "tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
     "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss", "kv_commit_accepted",
     "tree_verify_naive", "tree_logits_transform", "TV_OUT_LOGITS", "TV_OUT_PROBS", "tv_status_string",
-    "tree_verify_mss_commit", "tree_verify_mss_multi",
+    "tree_verify_mss_commit", "tree_verify_mss_multi", "tree_mask_attn_verify",
 ]
 
 TV_F32 = 0
@@ -25,7 +25,7 @@ TV_OUT_PROBS = 1
 EXPORTS = ("tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
            "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss",
            "kv_commit_accepted", "tree_verify_naive", "tree_logits_transform", "tv_status_string",
-           "tree_verify_mss_commit", "tree_verify_mss_multi")
+           "tree_verify_mss_commit", "tree_verify_mss_multi", "tree_mask_attn_verify")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libtreeverify.so")
@@ -45,6 +45,7 @@ def _load():
         "tree_build_mask": ([I, I, P, P, P, P, P, P], I),
         "tree_attn_verify_workspace": ([I, I, I, I, I, I], SZ),
         "tree_attn_verify": ([I, I, I, I, I, F, P, P, P, I, I, P, I, P, P, P, P, P, SZ, P], I),
+        "tree_mask_attn_verify": ([I, I, I, I, I, F, P, P, P, I, I, P, I, P, P, P, P, P, P, P, P, SZ, P], I),
         "tree_verify_workspace": ([I, I, I], SZ),
         "tree_verify_greedy": ([I, I, I, P, P, P, P, P, P, P, P, SZ, P], I),
         "tree_verify_mss": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ, P], I),
@@ -127,6 +128,20 @@ def tree_attn_verify(q, k_cache, v_cache, block_table, prefix_len, anc, status, 
                                 block_table.shape[1], _ptr(prefix_len), _ptr(anc), _ptr(status),
                                 _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "tree_attn_verify")
+
+
+def tree_mask_attn_verify(q, k_cache, v_cache, block_table, prefix_len, parent, anc, child, depth,
+                          status, out, workspace, scale=None, stream=None):
+    """tree_build_mask then tree_attn_verify, one launch where the plan allows."""
+    B, N, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().tree_mask_attn_verify(_dtype_code(q), B, N, H, D, float(scale), _ptr(q), _ptr(k_cache),
+                                     _ptr(v_cache), k_cache.shape[0], k_cache.shape[2], _ptr(block_table),
+                                     block_table.shape[1], _ptr(prefix_len), _ptr(parent), _ptr(anc),
+                                     _ptr(child), _ptr(depth), _ptr(status), _ptr(out), _ptr(workspace),
+                                     ws_bytes, _stream(stream)), "tree_mask_attn_verify")
 
 
 def tree_verify_workspace(B, N, V):

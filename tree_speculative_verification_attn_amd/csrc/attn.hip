@@ -31,7 +31,7 @@
 //
 // fp32 path (vector ALU): same chunking, K/V tiles staged in LDS, all
 // queries of the (b, h) per workgroup.
-#include "tv_common.h"
+#include "tree_mask.h"
 
 #include <algorithm>
 
@@ -60,6 +60,12 @@ struct AttnArgs {
   const int32_t* prefix_len;
   const uint64_t* anc;
   int32_t* status;
+  // masks built in the kernel (attn_mfma_kernel<..., true>): parent [B][N]
+  // in, and the tree_build_mask outputs
+  const int32_t* parent;
+  uint64_t* anc_out;
+  uint64_t* child_out;
+  int32_t* depth_out;
   void* out;
   float* part_o;             // [B][H][S][Npad][D] unnormalised partial outputs
   float* part_ml;            // [B][H][S][Npad][2] (max in log2 domain, sum)
@@ -77,6 +83,13 @@ __device__ __forceinline__ int request_gate(const AttnArgs& a, int b) {
   if (L < 0 || static_cast<int64_t>(L) + a.N > static_cast<int64_t>(a.max_blocks) * TV_BLOCK)
     return TV_REQ_KV_CAPACITY;
   return TV_REQ_OK;
+}
+
+// A status written while other workgroups of the request run (in-kernel
+// masks): a device-scope store, so it reaches memory in the order it is made
+// rather than with its XCD's cache at the end of the kernel.
+__device__ __forceinline__ void store_status(const AttnArgs& a, int b, int v) {
+  __hip_atomic_store(a.status + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T>
@@ -172,7 +185,14 @@ constexpr int kGroupThreads = 256;
 constexpr int kAttnThreads = kGroups * kGroupThreads;
 constexpr unsigned kGroupSpinLimit = 1u << 26;
 
-template <int D, int NQT>
+// MASK: the kernel also builds the request's tree masks (one chunk per
+// (request, head) only).  Every workgroup of request b reads the parents and
+// derives the ancestor masks of its query rows, the tree's validity and the
+// request's status from its own loads; workgroup (b, 0, 0) alone writes the
+// status (device-scope stores) and the mask outputs of tree_build_mask, so no
+// two workgroups write the same word, except a timeout (which comes only after
+// a workgroup's spin limit, long after the first workgroup's setup).
+template <int D, int NQT, bool MASK>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KC = D / 32;               // contraction steps over D
   constexpr int DT = D / 16;               // output dim tiles
@@ -217,12 +237,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   // trips to memory.
   // The kernel arguments the start reads are fetched in one batch of scalar
   // loads (otherwise a second batch waits on the first).
-  asm volatile("" :: "s"(a.q), "s"(a.kc), "s"(a.vc), "s"(a.block_table), "s"(a.prefix_len), "s"(a.anc),
-               "s"(a.status), "s"(a.N), "s"(a.H), "s"(a.num_blocks), "s"(a.max_blocks), "s"(a.chunk));
+  if constexpr (MASK)
+    asm volatile("" :: "s"(a.q), "s"(a.kc), "s"(a.vc), "s"(a.block_table), "s"(a.prefix_len), "s"(a.parent),
+                 "s"(a.N), "s"(a.H), "s"(a.num_blocks), "s"(a.max_blocks), "s"(a.chunk));
+  else
+    asm volatile("" :: "s"(a.q), "s"(a.kc), "s"(a.vc), "s"(a.block_table), "s"(a.prefix_len), "s"(a.anc),
+                 "s"(a.status), "s"(a.N), "s"(a.H), "s"(a.num_blocks), "s"(a.max_blocks), "s"(a.chunk));
   const int N = a.N;
   int b_v;
   asm volatile("v_mov_b32 %0, %1" : "=v"(b_v) : "s"(b));
-  const int st_v = a.status[b_v];
+  const int st_v = MASK ? TV_REQ_OK : a.status[b_v];
   const int L_v = a.prefix_len[b_v];
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
   // Query tile of this wave.  Wave gw of a group runs on SIMD gw, so the
@@ -234,7 +258,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   const int n_q = 16 * qt + lr;
   bf16x8 qv[KC];            // this wave's Q tile: read from the group's copy at its first stage
   uint64_t ancq = 0;
-  if (computes && n_q < N) ancq = a.anc[static_cast<size_t>(b) * N + n_q];
+  int par = -2;             // MASK: parent of node `lane` (every wave builds the masks)
+  if constexpr (MASK) {
+    if (lane < N) par = a.parent[static_cast<size_t>(b) * N + lane];
+  } else {
+    if (computes && n_q < N) ancq = a.anc[static_cast<size_t>(b) * N + n_q];
+  }
   // Block ids of every block the chunk can cover, before the prefix length
   // is known (the table index is clamped to the table).  Ids outside
   // [0, num_blocks) are stored as 0, so every K/V load stays in bounds; the
@@ -254,8 +283,30 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   // so it adds no wait of its own inside the stage loop, where a wait would
   // also drain the stage loads in flight, which it does not know about.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
-  const int st = __builtin_amdgcn_readfirstlane(st_v);
   const int L = __builtin_amdgcn_readfirstlane(L_v);
+  const bool first_wg = h == 0 && s == 0;
+  int st;
+  if constexpr (MASK) {
+    uint64_t anc_l;
+    int dep_l;
+    const bool bad_tree = tv::wave_tree_masks(N, par, anc_l, dep_l);
+    st = bad_tree ? TV_REQ_BAD_PARENT : TV_REQ_OK;
+    const int src = n_q & 63;
+    const uint32_t lo = __shfl(static_cast<uint32_t>(anc_l), src, 64);
+    const uint32_t hi = __shfl(static_cast<uint32_t>(anc_l >> 32), src, 64);
+    ancq = (computes && n_q < N) ? (static_cast<uint64_t>(hi) << 32 | lo) : 0ull;
+    if (first_wg && wave == 0) {
+      if (lane < N) {
+        a.anc_out[static_cast<size_t>(b) * N + lane] = anc_l;
+        a.depth_out[static_cast<size_t>(b) * N + lane] = dep_l;
+      }
+      // (the ring is not written before the barrier below)
+      tv::wave_child_masks(N, par, bad_tree, reinterpret_cast<unsigned long long*>(ring),
+                           a.child_out + static_cast<size_t>(b) * (N + 1));
+    }
+  } else {
+    st = __builtin_amdgcn_readfirstlane(st_v);
+  }
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int i = threadIdx.x + r * kAttnThreads;
@@ -263,7 +314,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   }
   if (L < 0 || static_cast<int64_t>(L) + N > static_cast<int64_t>(a.max_blocks) * TV_BLOCK) {
     // no workgroup of this request gets further, so no bad-block flag can race this
-    if (threadIdx.x == 0 && st == TV_REQ_OK) a.status[b] = TV_REQ_KV_CAPACITY;
+    if constexpr (MASK) {
+      if (first_wg && threadIdx.x == 0) store_status(a, b, st != TV_REQ_OK ? st : TV_REQ_KV_CAPACITY);
+    } else {
+      if (threadIdx.x == 0 && st == TV_REQ_OK) a.status[b] = TV_REQ_KV_CAPACITY;
+    }
     if (s == 0) zero_out<uint16_t>(a, b, h);
     return;
   }
@@ -301,10 +356,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
 #pragma unroll
   for (int w = 0; w < kAttnThreads / 64; ++w) wflags |= s_wflag[w];
   if (wflags & 1) {                          // a skipped request: zero output
+    if (MASK && first_wg && threadIdx.x == 0) store_status(a, b, st);
     if (s == 0) zero_out<uint16_t>(a, b, h);
     return;
   }
   const int badblk = wflags & 2;
+  // (MASK: one chunk, so this chunk's blocks are all the request's blocks)
+  if (MASK && first_wg && threadIdx.x == 0) store_status(a, b, badblk ? TV_REQ_BAD_BLOCK : TV_REQ_OK);
 
   uint8_t* gring = ring + grp * kRing * 2 * TILE;   // this group's stage buffers
   uint8_t* gq = sq + grp * QBYTES;                   // this group's Q copy
@@ -569,8 +627,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     dst[(DT * 4 + 1) * 64] = lrun;
   }
   __syncthreads();
-  if (badblk && threadIdx.x == 0) a.status[b] = TV_REQ_BAD_BLOCK;
-  if (s_hung && threadIdx.x == 0) a.status[b] = TV_REQ_TIMEOUT;
+  if (!MASK && badblk && threadIdx.x == 0) a.status[b] = TV_REQ_BAD_BLOCK;
+  if (s_hung && threadIdx.x == 0) {
+    if (MASK) store_status(a, b, TV_REQ_TIMEOUT);
+    else a.status[b] = TV_REQ_TIMEOUT;
+  }
   if (grp != 0 || !computes) return;
   float mo[kGroups], lo_[kGroups];
   mo[0] = mrun;
@@ -829,8 +890,8 @@ int attn_slots(int D) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
-  const void* fn = D == 128 ? reinterpret_cast<const void*>(attn_mfma_kernel<128, 4>)
-                            : reinterpret_cast<const void*>(attn_mfma_kernel<64, 4>);
+  const void* fn = D == 128 ? reinterpret_cast<const void*>(attn_mfma_kernel<128, 4, false>)
+                            : reinterpret_cast<const void*>(attn_mfma_kernel<64, 4, false>);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kAttnThreads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const int slots = cus * per_cu;
@@ -895,9 +956,41 @@ extern "C" size_t tree_attn_verify_workspace(tv_dtype dt, int B, int N, int H, i
   return make_plan(dt, B, N, H, D, max_blocks).ws_bytes;
 }
 
-template <int D, int NQT>
+template <int D, int NQT, bool MASK = false>
 static void launch_mfma(dim3 grid, hipStream_t st, const AttnArgs& a) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NQT>), grid, dim3(kAttnThreads), 0, st, a);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NQT, MASK>), grid, dim3(kAttnThreads), 0, st, a);
+}
+
+// Argument checks shared by both entry points and the kernel arguments;
+// ptrs_ok: the caller's own pointers (anc, or the mask's) are non-null.
+static tv_status attn_setup(tv_dtype dt, int B, int N, int H, int D, float scale, const void* q,
+                            const void* k_cache, const void* v_cache, int num_blocks, int block_size,
+                            const int32_t* block_table, int max_blocks, const int32_t* prefix_len,
+                            int32_t* status, void* out, void* workspace, size_t ws_bytes, bool ptrs_ok,
+                            AttnArgs& a, Plan& p) {
+  if (dt != TV_F32 && dt != TV_BF16) return TV_EDTYPE;
+  if (B < 0 || N < 0 || H < 1 || (D != 64 && D != 128) || block_size != TV_BLOCK ||
+      max_blocks < 1 || num_blocks < 1)
+    return TV_EINVAL;
+  if (N > TV_MAX_NODES) return TV_ETOOBIG;
+  if (B > 65535 || H > 65535) return TV_EINVAL;      // grid y/z limits
+  if (B == 0 || N == 0) return TV_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !prefix_len || !status || !out || !ptrs_ok)
+    return TV_EINVAL;
+  p = make_plan(dt, B, N, H, D, max_blocks);
+  if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes)) return TV_EWORKSPACE;
+
+  a = AttnArgs{};
+  a.B = B; a.N = N; a.H = H; a.D = D;
+  a.scale_log2 = scale * kLog2e;
+  a.q = q; a.kc = k_cache; a.vc = v_cache;
+  a.num_blocks = num_blocks; a.block_table = block_table; a.max_blocks = max_blocks;
+  a.prefix_len = prefix_len; a.status = status; a.out = out;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.part_o = p.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_ml = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
+  a.chunk = p.chunk; a.splits = p.splits; a.npad = p.npad;
+  return TV_OK;
 }
 
 extern "C" tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
@@ -906,28 +999,13 @@ extern "C" tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, f
                                       int max_blocks, const int32_t* prefix_len, const uint64_t* anc,
                                       int32_t* status, void* out, void* workspace, size_t ws_bytes,
                                       hipStream_t stream) {
-  if (dt != TV_F32 && dt != TV_BF16) return TV_EDTYPE;
-  if (B < 0 || N < 0 || H < 1 || (D != 64 && D != 128) || block_size != TV_BLOCK ||
-      max_blocks < 1 || num_blocks < 1)
-    return TV_EINVAL;
-  if (N > TV_MAX_NODES) return TV_ETOOBIG;
-  if (B > 65535 || H > 65535) return TV_EINVAL;      // grid y/z limits
-  if (B == 0 || N == 0) return TV_OK;
-  if (!q || !k_cache || !v_cache || !block_table || !prefix_len || !anc || !status || !out)
-    return TV_EINVAL;
-  const Plan p = make_plan(dt, B, N, H, D, max_blocks);
-  if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes)) return TV_EWORKSPACE;
-
   AttnArgs a;
-  a.B = B; a.N = N; a.H = H; a.D = D;
-  a.scale_log2 = scale * kLog2e;
-  a.q = q; a.kc = k_cache; a.vc = v_cache;
-  a.num_blocks = num_blocks; a.block_table = block_table; a.max_blocks = max_blocks;
-  a.prefix_len = prefix_len; a.anc = anc; a.status = status; a.out = out;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.part_o = p.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
-  a.part_ml = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
-  a.chunk = p.chunk; a.splits = p.splits; a.npad = p.npad;
+  Plan p;
+  const tv_status e = attn_setup(dt, B, N, H, D, scale, q, k_cache, v_cache, num_blocks, block_size,
+                                 block_table, max_blocks, prefix_len, status, out, workspace, ws_bytes,
+                                 anc != nullptr, a, p);
+  if (e != TV_OK || B == 0 || N == 0) return e;
+  a.anc = anc;
 
   const dim3 grid(p.splits, H, B);
   if (dt == TV_BF16) {
@@ -960,6 +1038,52 @@ extern "C" tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, f
       hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, mgrid, dim3(kThreads), 0, stream, a);
     else
       hipLaunchKernelGGL(attn_merge_kernel<float>, mgrid, dim3(kThreads), 0, stream, a);
+  }
+  return tv::launch_status();
+}
+
+extern "C" tv_status tree_mask_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
+                                           const void* q, const void* k_cache, const void* v_cache,
+                                           int num_blocks, int block_size, const int32_t* block_table,
+                                           int max_blocks, const int32_t* prefix_len,
+                                           const int32_t* parent, uint64_t* anc, uint64_t* child,
+                                           int32_t* depth, int32_t* status, void* out, void* workspace,
+                                           size_t ws_bytes, hipStream_t stream) {
+  AttnArgs a;
+  Plan p;
+  const tv_status e = attn_setup(dt, B, N, H, D, scale, q, k_cache, v_cache, num_blocks, block_size,
+                                 block_table, max_blocks, prefix_len, status, out, workspace, ws_bytes,
+                                 parent && anc && child && depth, a, p);
+  if (e != TV_OK || B == 0) return e;
+  if (!child || !status) return TV_EINVAL;          // (N = 0: only the mask's outputs)
+  if (N == 0) return tree_build_mask(B, N, parent, anc, child, depth, status, stream);
+  if (dt != TV_BF16 || p.splits > 1) {
+    // the two calls this one stands for
+    const tv_status r = tree_build_mask(B, N, parent, anc, child, depth, status, stream);
+    if (r != TV_OK) return r;
+    return tree_attn_verify(dt, B, N, H, D, scale, q, k_cache, v_cache, num_blocks, block_size, block_table,
+                            max_blocks, prefix_len, anc, status, out, workspace, ws_bytes, stream);
+  }
+  a.parent = parent;
+  a.anc_out = anc;
+  a.child_out = child;
+  a.depth_out = depth;
+  const dim3 grid(1, H, B);
+  const int nqt = (N + 15) / 16;
+  if (D == 128) {
+    switch (nqt) {
+      case 1: launch_mfma<128, 1, true>(grid, stream, a); break;
+      case 2: launch_mfma<128, 2, true>(grid, stream, a); break;
+      case 3: launch_mfma<128, 3, true>(grid, stream, a); break;
+      default: launch_mfma<128, 4, true>(grid, stream, a); break;
+    }
+  } else {
+    switch (nqt) {
+      case 1: launch_mfma<64, 1, true>(grid, stream, a); break;
+      case 2: launch_mfma<64, 2, true>(grid, stream, a); break;
+      case 3: launch_mfma<64, 3, true>(grid, stream, a); break;
+      default: launch_mfma<64, 4, true>(grid, stream, a); break;
+    }
   }
   return tv::launch_status();
 }

@@ -6,7 +6,7 @@
 // slot: no ancestors, nobody's child, never a parent.  Each lane climbs its parent
 // chain through cross-lane reads (depth <= 64 steps), so no mask is ever
 // materialised on the host.
-#include "tv_common.h"
+#include "tree_mask.h"
 
 namespace {
 
@@ -17,48 +17,18 @@ __global__ __launch_bounds__(64) void build_mask_kernel(int N, const int32_t* __
                                                         int32_t* __restrict__ status) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
-  const bool live = i < N;
   // parent -2 marks a padding slot (trees of different sizes in one batch);
   // lanes past N behave like padding
-  const int p = live ? parent[static_cast<size_t>(b) * N + i] : -2;
-  const int pp = __shfl(p, p >= 0 ? p : 0, 64);      // parent of my parent
-  const int bad = __any(live && (p < -2 || p >= i || (p >= 0 && pp == -2)));
-  const bool node = live && p != -2;
-
-  uint64_t a = 0;
-  int d = 0;
-  if (!bad && node) {
-    a = 1ull << i;
-    d = 1;
-  }
-  // climb: cur = current ancestor of node i (-1 = reached the root)
-  int cur = (bad || !node) ? -1 : p;
-  for (int step = 0; step < N; ++step) {
-    const int any_left = __any(cur >= 0);
-    if (!any_left) break;
-    const int src = cur >= 0 ? cur : 0;
-    const int up = __shfl(p, src, 64);   // parent of my current ancestor
-    if (cur >= 0) {
-      a |= 1ull << cur;
-      ++d;
-      cur = up;
-    }
-  }
-  if (live) {
+  const int p = i < N ? parent[static_cast<size_t>(b) * N + i] : -2;
+  uint64_t a;
+  int d;
+  const bool bad = tv::wave_tree_masks(N, p, a, d);
+  if (i < N) {
     anc[static_cast<size_t>(b) * N + i] = a;
     depth[static_cast<size_t>(b) * N + i] = d;
   }
-  // child[u + 1] = set of nodes whose parent is u, u = -1 .. N-1: each node
-  // ORs its bit into its parent's word (LDS), then lane u + 1 stores word u + 1
   __shared__ unsigned long long s_child[TV_MAX_NODES + 1];
-  s_child[i] = 0ull;
-  if (i == 0) s_child[TV_MAX_NODES] = 0ull;
-  __syncthreads();
-  if (!bad && node) atomicOr(&s_child[p + 1], 1ull << i);
-  __syncthreads();
-  uint64_t* crow = child + static_cast<size_t>(b) * (N + 1);
-  if (i <= N) crow[i] = s_child[i];
-  if (i == 0 && N == TV_MAX_NODES) crow[N] = s_child[N];
+  tv::wave_child_masks(N, p, bad, s_child, child + static_cast<size_t>(b) * (N + 1));
   if (i == 0) status[b] = bad ? TV_REQ_BAD_PARENT : TV_REQ_OK;
 }
 
