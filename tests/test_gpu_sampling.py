@@ -78,6 +78,26 @@ def test_transform_matches_oracle(V):
     print(f"V={V}: {near} rows with a top-p cut within 1e-6 of a cumulative mass")
 
 
+def test_transform_fallback_paths():
+    # Rows that defeat the short paths of the row-resident kernel: every entry
+    # tied (the list above the top-k bound overflows), a few distinct values
+    # (thousands tied at the top), and 600 entries tied at the maximum (a list
+    # too long for the ranking search but short enough to list).
+    rng = np.random.default_rng(11)
+    V = 32000
+    rows = np.empty((4, V), dtype=np.float32)
+    rows[0] = 0.5
+    rows[1] = rng.integers(0, 3, V).astype(np.float32)
+    rows[2] = rng.normal(0, 1.0, V).astype(np.float32)
+    rows[2, rng.choice(V, 600, replace=False)] = 9.0
+    rows[3] = rng.normal(0, 1.0, V).astype(np.float32)
+    rows[3, rng.choice(V, 3000, replace=False)] = -np.inf
+    for T, k, p in ((0.8, 50, 0.9), (1.0, 200, 1.0), (1.0, 0, 0.5), (1.1, 250, 0.7), (1.0, 7, 1.0)):
+        print(f"[case] transform fallbacks T={T} k={k} p={p}", flush=True)
+        _check_rows(rows, T, k, p, f"fallback {T} {k} {p}")
+        _check_rows(rows[:, :6000].copy(), T, k, p, f"fallback V=6000 {T} {k} {p}")
+
+
 def test_transform_special_rows_in_place_and_errors():
     import tree_speculative_verification_attn_amd as tv
     rows = np.zeros((6, 9), dtype=np.float32)
