@@ -1,8 +1,12 @@
 """The whole verification step captured in a HIP graph: every replay must
-match the eager step bit for bit.
+match the eager step bit for bit (the attention output to rounding where a
+chunk has more than 6 stages of 32 keys, whose summation order is set at run
+time).
 
 The step is tree_build_mask -> tree_attn_verify -> tree_verify_greedy ->
-tree_verify_mss -> kv_commit_accepted on one seeded workload.  Between
+tree_verify_mss -> kv_commit_accepted on one seeded workload, either as five
+calls or as the benchmark's three (tree_mask_attn_verify, tree_verify_greedy,
+tree_verify_mss_commit).  Between
 replays the test restores the KV cache and prefix lengths (which the commit
 changes) with eager copies, runs unrelated eager work, and synchronizes, so a
 graph node that depends on state left by an earlier replay would show up as
@@ -50,7 +54,16 @@ def _state(w):
     return s
 
 
-def _step(s, w):
+def _step(s, w, fused):
+    if fused:
+        tv.tree_mask_attn_verify(s["q"], s["k"], s["v"], s["bt"], s["pl"], s["parent"], s["anc"], s["child"],
+                                 s["depth"], s["status"], s["out"], s["ws_a"], scale=w.scale)
+        tv.tree_verify_greedy(s["tl"], s["token"], s["child"], s["status"], s["g_acc"], s["g_num"], s["g_bonus"],
+                              s["ws_v"])
+        tv.tree_verify_mss_commit(s["tl"], s["sp"], s["qr"], s["token"], s["child"], s["status"], w.seed, w.offset,
+                                  s["m_acc"], s["m_num"], s["m_bonus"], s["m_rounds"], s["ws_v"], s["k"], s["v"],
+                                  s["bt"], s["pl"])
+        return
     tv.tree_build_mask(s["parent"], s["anc"], s["child"], s["depth"], s["status"])
     tv.tree_attn_verify(s["q"], s["k"], s["v"], s["bt"], s["pl"], s["anc"], s["status"], s["out"], s["ws_a"],
                         scale=w.scale)
@@ -65,12 +78,20 @@ OUTS = ("anc", "child", "depth", "status", "out", "g_acc", "g_num", "g_bonus", "
         "m_rounds", "pl", "k", "v")
 
 
+def _same(name, got, ref, w):
+    if name == "out" and int(w.prefix_len.max()) + w.N > 6 * 32:
+        g, r = got.float(), ref.float()
+        return bool(torch.all((g - r).abs() <= 2e-3 + 8e-3 * r.abs()))
+    return torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("cfg,kw", [(2, dict(B=4, L=300, H=8, V=32000)),
                                     (3, dict(B=3, L=77, H=3, V=50272)),
                                     (4, dict(B=6, H=2, V=20000))])
-def test_graph_replay_matches_eager(cfg, kw):
+def test_graph_replay_matches_eager(cfg, kw, fused):
     w = synth.make_workload(cfg, **kw)
-    print("[case] graph replay", cfg, kw, flush=True)
+    print("[case] graph replay", cfg, kw, "three launches" if fused else "five calls", flush=True)
     s = _state(w)
     k0, v0, pl0 = s["k"].clone(), s["v"].clone(), s["pl"].clone()
 
@@ -80,7 +101,7 @@ def test_graph_replay_matches_eager(cfg, kw):
         s["pl"].copy_(pl0)
         s["status"].zero_()
 
-    _step(s, w)                              # eager reference
+    _step(s, w, fused)                       # eager reference
     torch.cuda.synchronize()
     ref = {n: s[n].clone() for n in OUTS}
     assert int((ref["status"] != 0).sum()) == 0
@@ -89,7 +110,7 @@ def test_graph_replay_matches_eager(cfg, kw):
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        _step(s, w)
+        _step(s, w, fused)
     for rep in range(4):
         restore()
         for n in OUTS[4:12]:
@@ -100,5 +121,5 @@ def test_graph_replay_matches_eager(cfg, kw):
         torch.cuda.synchronize()
         assert float(junk) == float(junk)
         for n in OUTS:
-            assert torch.equal(s[n], ref[n]), (rep, n)
+            assert _same(n, s[n], ref[n], w), (rep, n)
         assert int(s["ws_v"].count_nonzero()) == 0
