@@ -696,18 +696,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
 // fp32 vector-ALU kernel
 // ===========================================================================
 // Thread (n = tid / 4, g = tid % 4) owns query n and output dims
-// [g*D/4, (g+1)*D/4).  K/V tiles of 16 keys are staged in LDS.
+// [g*D/4, (g+1)*D/4).  K/V tiles of 16 keys (one cache block) are staged in
+// LDS; the next tile's loads are in flight while the current one is used,
+// rows are padded to D + 4 floats so every product reads LDS 16 bytes at a
+// time (in the same order of summation), and waves whose queries are all past
+// N skip the arithmetic.
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_valu_kernel(AttnArgs a) {
-  constexpr int KT = 16;          // keys per tile
+  constexpr int KT = 16;          // keys per tile (one cache block)
   constexpr int DQ = D / 4;       // dims per thread
-  constexpr int QS = D + 1;       // padded LDS row stride (floats)
+  constexpr int QS = D + 4;       // padded LDS row stride (floats), 16-byte aligned
+  constexpr int PER = KT * D / kThreads;      // tile elements each thread moves
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n = threadIdx.x >> 2, g = threadIdx.x & 3;
 
-  __shared__ float q_s[64 * QS];
-  __shared__ float k_s[KT * QS];
-  __shared__ float v_s[KT * D];
+  __shared__ __attribute__((aligned(16))) float q_s[64 * QS];
+  __shared__ __attribute__((aligned(16))) float k_s[KT * QS];
+  __shared__ __attribute__((aligned(16))) float v_s[KT * D];
   __shared__ float sc_s[64 * (KT + 1)];
   __shared__ int s_gate, s_badblk;
   if (threadIdx.x == 0) {
@@ -745,37 +750,63 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(AttnArgs a) {
   const size_t head_off = static_cast<size_t>(h) * TV_BLOCK * D;
   const size_t blk_stride = static_cast<size_t>(a.H) * TV_BLOCK * D;
 
-  for (int t0 = k_begin; t0 < k_end; t0 += KT) {
-    __syncthreads();   // previous tile fully consumed
+  // this thread's share of a tile, fetched into registers one tile ahead
+  float kn[PER], vn[PER];
+  auto fetch = [&](int t0) {
     int blk = bt[t0 / TV_BLOCK];
     if (blk < 0 || blk >= a.num_blocks) {
       if (threadIdx.x == 0) s_badblk = 1;
       blk = -1;
     }
-    for (int e = threadIdx.x; e < KT * D; e += kThreads) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + i * kThreads;
       const int r = e / D, d = e - r * D;
-      float kx = 0.f, vx = 0.f;
+      kn[i] = vn[i] = 0.f;
       if (blk >= 0 && t0 + r < T) {
         const size_t off = blk * blk_stride + head_off + static_cast<size_t>(r) * D + d;
-        kx = kg[off];
-        vx = vg[off];
+        kn[i] = kg[off];
+        vn[i] = vg[off];
       }
-      k_s[r * QS + d] = kx;
-      v_s[r * D + d] = vx;
+    }
+  };
+  const bool rows_here = 16 * static_cast<int>(threadIdx.x >> 6) < N;   // (wave-uniform)
+  fetch(k_begin);
+  for (int t0 = k_begin; t0 < k_end; t0 += KT) {
+    __syncthreads();   // previous tile fully consumed
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int r = e / D, d = e - r * D;
+      k_s[r * QS + d] = kn[i];
+      v_s[r * D + d] = vn[i];
     }
     __syncthreads();
+    if (t0 + KT < k_end) fetch(t0 + KT);      // in flight during this tile
+    if (!rows_here) continue;
+    const float4* qrow = reinterpret_cast<const float4*>(q_s + n * QS);
 #pragma unroll
     for (int j = 0; j < KT / 4; ++j) {
       const int r = 4 * g + j;
       const int t = t0 + r;
+      const float4* krow = reinterpret_cast<const float4*>(k_s + r * QS);
       float acc = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) acc = fmaf(q_s[n * QS + d], k_s[r * QS + d], acc);
+#pragma unroll 4
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const float4 qv = qrow[d4], kv = krow[d4];
+        acc = fmaf(qv.x, kv.x, acc);
+        acc = fmaf(qv.y, kv.y, acc);
+        acc = fmaf(qv.z, kv.z, acc);
+        acc = fmaf(qv.w, kv.w, acc);
+      }
       bool vis = t < k_end;
       if (t >= L) vis = vis && ((ancn >> ((t - L) & 63)) & 1ull);
       sc_s[n * (KT + 1) + r] = vis ? acc * a.scale_log2 : -INFINITY;
     }
-    __syncthreads();
+    // the four threads of query n exchange their scores through LDS (a
+    // wave's own writes and reads, in order)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < KT; ++r) mx = fmaxf(mx, sc_s[n * (KT + 1) + r]);
@@ -790,8 +821,15 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(AttnArgs a) {
     for (int r = 0; r < KT; ++r) {
       const float p = tv::exp2_fast(sc_s[n * (KT + 1) + r] - m_use);
       lrun += p;
+      const float4* vrow = reinterpret_cast<const float4*>(v_s + r * D + g * DQ);
 #pragma unroll
-      for (int j = 0; j < DQ; ++j) o[j] = fmaf(p, v_s[r * D + g * DQ + j], o[j]);
+      for (int j4 = 0; j4 < DQ / 4; ++j4) {
+        const float4 vv = vrow[j4];
+        o[4 * j4] = fmaf(p, vv.x, o[4 * j4]);
+        o[4 * j4 + 1] = fmaf(p, vv.y, o[4 * j4 + 1]);
+        o[4 * j4 + 2] = fmaf(p, vv.z, o[4 * j4 + 2]);
+        o[4 * j4 + 3] = fmaf(p, vv.w, o[4 * j4 + 3]);
+      }
     }
   }
   __syncthreads();
