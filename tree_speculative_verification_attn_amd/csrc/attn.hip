@@ -969,7 +969,7 @@ Plan make_plan(tv_dtype dt, int B, int N, int H, int D, int max_blocks) {
     }
   } else {
     long s = (512 + pairs - 1) / pairs;
-    s = std::min(s, (keys_max + 255) / 256);
+    s = std::min(s, (keys_max + 63) / 64);         // chunks of at least 64 keys
     s = std::max(1L, std::min(s, static_cast<long>(kMaxSplits)));
     c = (keys_max + s - 1) / s;
     c = (c + 63) / 64 * 64;
