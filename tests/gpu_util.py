@@ -23,7 +23,7 @@ def u64(t):
     return t.cpu().numpy().view(np.uint64)
 
 
-class GpuRun:
+class DeviceRun:
     """One workload on the device plus the outputs of each call."""
 
     def __init__(self, w):
@@ -201,5 +201,5 @@ def oracle_masks(w):
     return o_tree.build_mask_batch(w.parent)
 
 
-__all__ = ["GpuRun", "to_dev", "u64", "compare_mss", "compare_naive", "bf16_tol_check", "out_to_f64", "oracle_masks",
+__all__ = ["DeviceRun", "to_dev", "u64", "compare_mss", "compare_naive", "bf16_tol_check", "out_to_f64", "oracle_masks",
            "o_attn", "o_commit", "o_tree", "o_verify", "DEV"]

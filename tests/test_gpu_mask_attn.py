@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_util import GpuRun, o_attn, o_tree, out_to_f64, to_dev, u64
+from tests.gpu_util import DeviceRun, o_attn, o_tree, out_to_f64, to_dev, u64
 import tree_speculative_verification_attn_amd as tv
 
 pytestmark = pytest.mark.gpu
@@ -39,8 +39,8 @@ def _raw(t):
 
 
 def _both(w, mutate=None, stale=-99):
-    seq = GpuRun(w)
-    fus = GpuRun(w)
+    seq = DeviceRun(w)
+    fus = DeviceRun(w)
     for r in (seq, fus):
         r.status.fill_(stale)                  # the mask stage writes every status
         r.anc.fill_(-1)
@@ -154,7 +154,7 @@ def test_fused_empty_tree():
     w = synth.make_workload(dict(name="e", B=3, H=2, D=128, V=50, dtype="bf16", tree=("parents", []), L=10,
                                  sig_t=1.0, sig_s=1.0), 3)
     _case("mask+attn", "N = 0")
-    run = GpuRun(w)
+    run = DeviceRun(w)
     run.status.fill_(-99)
     run.child.fill_(-1)
     run.mask_attn()

@@ -12,7 +12,7 @@ import torch
 import synth
 from oracle import commit as o_commit
 from oracle import verify as o_verify
-from tests.gpu_util import GpuRun, compare_mss
+from tests.gpu_util import DeviceRun, compare_mss
 
 pytestmark = pytest.mark.gpu
 
@@ -26,8 +26,8 @@ def _raw(t):
 
 
 def _run_both(w, mutate=None, seed=None, offset=None):
-    seq = GpuRun(w).mask()
-    fus = GpuRun(w).mask()
+    seq = DeviceRun(w).mask()
+    fus = DeviceRun(w).mask()
     if mutate:
         mutate(seq)
         mutate(fus)

@@ -10,7 +10,7 @@ import torch
 
 import synth
 from oracle import exact, verify as o_verify
-from tests.gpu_util import DEV, GpuRun, compare_mss, to_dev
+from tests.gpu_util import DEV, DeviceRun, compare_mss, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -36,9 +36,9 @@ def test_identity_proposals_equal_mss(name):
     cfg, kw = SHAPES[name]
     _case("multi identity", name)
     w = synth.make_workload(cfg, **kw)
-    one = GpuRun(w).mask().mss()
+    one = DeviceRun(w).mask().mss()
     pn, pr = _identity(w)
-    multi = GpuRun(w).mask().mss_multi(pn, pr)
+    multi = DeviceRun(w).mask().mss_multi(pn, pr)
     torch.cuda.synchronize()
     for k in ("m_acc", "m_num", "m_bonus", "m_rounds", "status"):
         assert np.array_equal(getattr(one, k).cpu().numpy(), getattr(multi, k).cpu().numpy()), k
@@ -78,7 +78,7 @@ def test_merged_trees_vs_oracle(name):
     per_node = 3 if w.N <= 21 else 2
     for off in range(3):
         pn, pr = _random_proposals(w, rng, per_node)
-        run = GpuRun(w).mask().mss_multi(pn, pr, offset=w.offset + off)
+        run = DeviceRun(w).mask().mss_multi(pn, pr, offset=w.offset + off)
         torch.cuda.synchronize()
         ref = o_verify.verify_mss_multi(w.parent, w.token, w.target_logits, w.ssm_probs, pn, pr, [0] * w.B,
                                         w.seed, w.offset + off)
@@ -160,7 +160,7 @@ def test_proposal_status_paths():
     pn[2, N] = N - 1
     pn[3, N + 1] = N
     pn[4, :] = -1
-    run = GpuRun(w).mask().mss_multi(pn, pr)
+    run = DeviceRun(w).mask().mss_multi(pn, pr)
     torch.cuda.synchronize()
     st = run.status.cpu().numpy()
     assert st.tolist()[1:4] == [3, 3, 3], st

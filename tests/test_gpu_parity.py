@@ -17,7 +17,7 @@ from tests.golden.load import read_mask_fixture
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from tests.gpu_util import (GpuRun, compare_mss, compare_naive, o_attn, o_commit, o_tree, o_verify,
+    from tests.gpu_util import (DeviceRun, compare_mss, compare_naive, o_attn, o_commit, o_tree, o_verify,
                                 out_to_f64, to_dev, u64)
 
 TOL = {"bf16": (2e-2, 2e-2), "f32": (1e-5, 1e-5)}
@@ -121,7 +121,7 @@ def _check_attn(run, pairs=None):
 def test_attention_small(name):
     _print_case("attention", name)
     w = _small(name)
-    run = GpuRun(w).mask().attn()
+    run = DeviceRun(w).mask().attn()
     torch.cuda.synchronize()
     worst = _check_attn(run)
     print(f"{name}: max abs err {worst:.3e}")
@@ -136,7 +136,7 @@ def test_attention_edge_shapes():
                 _print_case("attention edge", kw, tree_, dt)
                 w = synth.make_workload(dict(name="e", B=2, H=2, D=128, V=50, dtype=dt, tree=tree_,
                                              sig_t=1.0, sig_s=1.0, **kw), 77)
-                run = GpuRun(w).mask().attn()
+                run = DeviceRun(w).mask().attn()
                 torch.cuda.synchronize()
                 _check_attn(run)
 
@@ -144,7 +144,7 @@ def test_attention_edge_shapes():
 def test_attention_status_paths():
     w = synth.make_workload(2, B=3, L=40, H=2, V=100)
     _print_case("attention status")
-    run = GpuRun(w).mask()
+    run = DeviceRun(w).mask()
     # request 0 malformed upstream, request 1 over capacity, request 2 fine
     run.status[0] = 1
     pl = w.prefix_len.copy()
@@ -165,7 +165,7 @@ def test_attention_status_paths():
     # a bad block id is reported as status 7
     bt = w.block_table.copy()
     bt[2, 0] = w.num_blocks + 5
-    run2 = GpuRun(w).mask()
+    run2 = DeviceRun(w).mask()
     run2.bt = to_dev(bt)
     run2.attn()
     torch.cuda.synchronize()
@@ -199,10 +199,10 @@ def _check_mss(run, label):
 def test_verify_small(name):
     _print_case("verify", name)
     w = _small(name)
-    run = GpuRun(w).mask().greedy()
+    run = DeviceRun(w).mask().greedy()
     torch.cuda.synchronize()
     _check_greedy(run)
-    run = GpuRun(w).mask().mss()
+    run = DeviceRun(w).mask().mss()
     torch.cuda.synchronize()
     _check_mss(run, name)
 
@@ -219,7 +219,7 @@ def test_greedy_forced_paths():
     tl[0, path[-1] + 1, :] = 0
     tl[0, path[-1] + 1, 7] = 5.0
     w.target_logits = tl
-    run = GpuRun(w).mask().greedy()
+    run = DeviceRun(w).mask().greedy()
     torch.cuda.synchronize()
     assert run.g_num.cpu().numpy()[0] == 3 and run.g_bonus.cpu().numpy()[0] == 7
     _check_greedy(run)
@@ -238,7 +238,7 @@ def test_verify_status_paths():
     tl[5, 0, :5] = -np.inf          # masked entries are fine
     w.token, w.q_row, w.target_logits, w.ssm_probs = tok, qr, tl, sp
     _print_case("verify status")
-    run = GpuRun(w).mask()
+    run = DeviceRun(w).mask()
     run.status[0] = 1               # upstream fault
     run.greedy()
     torch.cuda.synchronize()
@@ -246,7 +246,7 @@ def test_verify_status_paths():
     ref_g = o_verify.verify_greedy(w.parent, w.token, w.target_logits, [1, 0, 0, 0, 0, 0])
     assert list(st_g) == list(ref_g["status"])
     assert np.array_equal(run.g_num.cpu().numpy(), ref_g["num_accepted"])
-    run = GpuRun(w).mask()
+    run = DeviceRun(w).mask()
     run.status[0] = 1
     run.mss()
     torch.cuda.synchronize()
@@ -261,13 +261,13 @@ def test_verify_status_paths():
 def test_mss_q_row_problems():
     # a negative draft probability on a tested child, and a NaN in a row read in full
     w = synth.make_workload(1)
-    base_run = GpuRun(w).mask().mss()
+    base_run = DeviceRun(w).mask().mss()
     torch.cuda.synchronize()
     sp = w.ssm_probs.copy()
     sp[0, :, :] = np.where(sp[0] > 0, sp[0], 0)
     sp[0, 0, 5] = np.nan            # row 0 proposes the root's children
     w.ssm_probs = sp
-    run = GpuRun(w).mask().mss()
+    run = DeviceRun(w).mask().mss()
     torch.cuda.synchronize()
     ref = o_verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0], w.seed)
     exact, excused, bad = compare_mss(run, ref)
@@ -277,8 +277,8 @@ def test_mss_q_row_problems():
 
 def test_mss_offsets_and_determinism():
     w = _small("c2_small")
-    a = GpuRun(w).mask().mss(offset=3)
-    b = GpuRun(w).mask().mss(offset=3)
+    a = DeviceRun(w).mask().mss(offset=3)
+    b = DeviceRun(w).mask().mss(offset=3)
     torch.cuda.synchronize()
     for x, y in ((a.m_acc, b.m_acc), (a.m_bonus, b.m_bonus), (a.m_rounds, b.m_rounds)):
         assert torch.equal(x, y)
@@ -291,10 +291,10 @@ def test_mss_offsets_and_determinism():
 def test_empty_tree_verify():
     w = synth.make_workload(dict(name="e", B=3, H=1, D=64, L=5, V=300, dtype="f32",
                                  tree=("parents", []), sig_t=2.0, sig_s=1.0), 3)
-    run = GpuRun(w).mask().greedy()
+    run = DeviceRun(w).mask().greedy()
     torch.cuda.synchronize()
     _check_greedy(run)
-    run = GpuRun(w).mask().mss()
+    run = DeviceRun(w).mask().mss()
     torch.cuda.synchronize()
     _check_mss(run, "empty tree")
 
@@ -306,10 +306,10 @@ def test_verify_row_vocab(V):
     for cfg, kw in ((2, dict(B=3, L=20, H=1)), (4, dict(B=2, H=1))):
         w = synth.make_workload(cfg, V=V, **kw)
         _print_case("verify row", cfg, V)
-        run = GpuRun(w).mask().greedy()
+        run = DeviceRun(w).mask().greedy()
         torch.cuda.synchronize()
         _check_greedy(run)
-        run = GpuRun(w).mask().mss()
+        run = DeviceRun(w).mask().mss()
         torch.cuda.synchronize()
         _check_mss(run, f"row cfg{cfg} V={V}")
 
@@ -322,10 +322,10 @@ def test_verify_sliced_vocab(V):
     for cfg, kw in ((2, dict(B=3, L=20, H=1)), (4, dict(B=2, H=1))):
         w = synth.make_workload(cfg, V=V, **kw)
         _print_case("verify sliced", cfg, V)
-        run = GpuRun(w).mask().greedy()
+        run = DeviceRun(w).mask().greedy()
         torch.cuda.synchronize()
         _check_greedy(run)
-        run = GpuRun(w).mask().mss()
+        run = DeviceRun(w).mask().mss()
         torch.cuda.synchronize()
         _check_mss(run, f"sliced cfg{cfg} V={V}")
         assert int(run.ws_v.count_nonzero()) == 0
@@ -337,7 +337,7 @@ def test_verify_workspace_reuse(V):
     # one workgroup per request (ragged tail, scalar loads), V = 40003 splits
     # rows over 20 workgroups that exchange through the workspace
     w = synth.make_workload(3, B=3, L=77, H=3, V=V)
-    run = GpuRun(w).mask()
+    run = DeviceRun(w).mask()
     outs = []
     for rep in range(3):
         _print_case("verify workspace reuse", rep)
@@ -360,7 +360,7 @@ def test_verify_many_requests(V):
     w = synth.make_workload(dict(name="many", B=200, H=1, D=64, L=3, V=V, dtype="f32",
                                  tree=("parents", [-1, 0, 0, 1, -1, 4, 5]), sig_t=2.0, sig_s=1.0), 11)
     _print_case("verify many requests", w.B, w.V)
-    run = GpuRun(w).mask().greedy().mss()
+    run = DeviceRun(w).mask().greedy().mss()
     torch.cuda.synchronize()
     _check_greedy(run)
     ref = _check_mss(run, "many requests")
@@ -372,7 +372,7 @@ def test_verify_many_requests(V):
 def test_naive_small(name):
     _print_case("naive", name)
     w = _small(name)
-    run = GpuRun(w).mask().naive()
+    run = DeviceRun(w).mask().naive()
     torch.cuda.synchronize()
     ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [0] * w.B, w.seed, w.offset)
     ex, excused, bad = compare_naive(run, ref)
@@ -396,7 +396,7 @@ def test_naive_both_kernels(V):
             tl[b, 0, w.token[b, roots[0]]] += 12.0
         w.target_logits = tl
         _print_case("naive", cfg, V)
-        run = GpuRun(w).mask().naive(offset=7)
+        run = DeviceRun(w).mask().naive(offset=7)
         torch.cuda.synchronize()
         ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [0] * w.B, w.seed, 7)
         ex, excused, bad = compare_naive(run, ref)
@@ -414,7 +414,7 @@ def test_naive_status_and_rejection_rate():
     tl[3, 0, 17] = np.nan
     tl[4, 0, :] = -np.inf
     w.token, w.target_logits = tok, tl
-    run = GpuRun(w).mask()
+    run = DeviceRun(w).mask()
     run.status[0] = 1
     run.naive()
     torch.cuda.synchronize()
@@ -474,7 +474,7 @@ def _check_commit(run, w, acc, num, st_in, k_before, v_before):
 def test_commit_small(name):
     _print_case("commit", name)
     w = _small(name)
-    run = GpuRun(w).mask().mss()
+    run = DeviceRun(w).mask().mss()
     torch.cuda.synchronize()
     acc = run.m_acc.cpu().numpy()
     num = run.m_num.cpu().numpy()
@@ -493,7 +493,7 @@ def test_commit_hazard_and_errors():
     acc[0, :3] = [1, 2, 4]
     acc[1, :2] = [6, 0]
     acc[2, :3] = [1, 2, 7]          # 7 >= N: bad accepted list
-    run = GpuRun(w).mask()
+    run = DeviceRun(w).mask()
     torch.cuda.synchronize()
     st_in = run.status.cpu().numpy().copy()
     run.commit(to_dev(acc), to_dev(num))
@@ -510,7 +510,7 @@ def test_full_config(cfg):
     _print_case("full config", cfg, "generate")
     w = synth.make_config(cfg)
     _print_case("full config", cfg, "mask+attn")
-    run = GpuRun(w).mask().attn()
+    run = DeviceRun(w).mask().attn()
     torch.cuda.synchronize()
     rng = np.random.default_rng(cfg)
     pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(3)]

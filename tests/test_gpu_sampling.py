@@ -122,13 +122,13 @@ def test_transform_special_rows_in_place_and_errors():
 def test_mss_on_transformed_rows():
     import tree_speculative_verification_attn_amd as tv
     from oracle import verify as o_verify
-    from tests.gpu_util import GpuRun, compare_mss
+    from tests.gpu_util import DeviceRun, compare_mss
     for V, (T, k, p) in ((3000, (0.8, 40, 0.9)), (40000, (1.2, 0, 0.8))):
         w = synth.make_workload(2, B=4, L=20, H=1, V=V)
         print(f"[case] MSS on transformed rows V={V}", flush=True)
         with np.errstate(divide="ignore"):
             logq = np.log(w.ssm_probs).astype(np.float32)
-        run = GpuRun(w).mask()
+        run = DeviceRun(w).mask()
         tv.tree_logits_transform(run.tl, run.tl, T, k, p, tv.TV_OUT_LOGITS)
         lq = torch.from_numpy(logq).cuda()
         tv.tree_logits_transform(lq, run.sp, T, k, p, tv.TV_OUT_PROBS)

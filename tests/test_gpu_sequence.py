@@ -43,10 +43,10 @@ def _attn(tv, q, k, v, bt, pl, parent, dtype, scale, H, D):
 def test_paths_match_tree(cfg, kw):
     import tree_speculative_verification_attn_amd as tv
     from tree_speculative_verification_attn_amd import per_sequence
-    from tests.gpu_util import GpuRun, out_to_f64
+    from tests.gpu_util import DeviceRun, out_to_f64
     w = synth.make_workload(cfg, **kw)
     print(f"[case] per-sequence cfg{cfg}", flush=True)
-    run = GpuRun(w).mask().attn()
+    run = DeviceRun(w).mask().attn()
     torch.cuda.synchronize()
     tree_out = out_to_f64(run.out)
     sb = per_sequence.build(w.parent, w.prefix_len, run.q, run.k, run.v, run.bt)
