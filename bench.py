@@ -278,6 +278,9 @@ def main():
                 "mean_tokens_emitted_per_request": round(acc_tokens, 3)},
     }
     res["verify_variants"] = variants
+    res["per_call_ms"] = per_call_table(torch, tv, w, copies, per_call_ms, pl0, parent, anc, child, depth, status,
+                                        token, qr, bt, m_acc, m_num, m_bonus, m_rounds, ws_v, t_attn, t_attn_only,
+                                        t_mss, variants)
     res["tree_vs_sequence"] = tree_vs_sequence(torch, tv, w, copies, bt, t_attn_only, stream)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, value)
@@ -319,6 +322,38 @@ def verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status,
             "sampling_transform": f"tree_logits_transform of all {B * (N + 1)} target rows, T 0.8, top-k 50, top-p 0.9",
             "note": "synthetic rows (draft = target + noise); tokens per step = accepted + bonus, mean over "
                     f"{reps} random streams"}
+
+
+def per_call_table(torch, tv, w, copies, per_call_ms, pl0, parent, anc, child, depth, status, token, qr, bt,
+                   m_acc, m_num, m_bonus, m_rounds, ws_v, t_attn, t_attn_only, t_mss, variants):
+    """Every entry point on this workload, per call, from graphs of
+    back-to-back calls over the rotating input copies.  The two calls that
+    grow the prefix lengths are timed as (restore + call) minus (restore
+    alone), so each call sees the same lengths; kv_commit_accepted moves the
+    path of the benchmark's last MSS call."""
+    t_mask = per_call_ms(lambda c: tv.tree_build_mask(parent, anc, child, depth, status))
+    t_restore = per_call_ms(lambda c: c["pl"].copy_(pl0))
+    t_commit = per_call_ms(lambda c: (c["pl"].copy_(pl0),
+                                      tv.kv_commit_accepted(c["k"], c["v"], bt, c["pl"], m_acc, m_num, status)))
+    acc = torch.empty_like(m_acc)
+    num = torch.empty_like(m_num)
+    bonus = torch.empty_like(m_bonus)
+    rounds = torch.empty_like(m_rounds)
+    t_mss_commit = per_call_ms(lambda c: (c["pl"].copy_(pl0),
+                                          tv.tree_verify_mss_commit(c["tl"], c["sp"], qr, token, child, status, w.seed,
+                                                                    w.offset, acc, num, bonus, rounds, ws_v, c["k"],
+                                                                    c["v"], bt, c["pl"])))
+    for cp in copies:
+        cp["pl"].copy_(pl0)
+    assert int((status != 0).sum()) == 0, "a request failed in the per-call timings"
+    ml = variants["ms_per_launch"]
+    return {"tree_build_mask": round(t_mask, 5), "tree_attn_verify": round(t_attn_only, 5),
+            "tree_mask_attn_verify": round(t_attn, 5), "tree_verify_greedy": ml["greedy"],
+            "tree_verify_mss": round(t_mss, 5), "tree_verify_naive": ml["naive"],
+            "kv_commit_accepted": round(t_commit - t_restore, 5),
+            "tree_verify_mss_commit": round(t_mss_commit - t_restore, 5),
+            "tree_logits_transform": variants["sampling_transform_ms"],
+            "prefix_len_restore": round(t_restore, 5)}
 
 
 def compare_sequence_all(torch, cfgs):
