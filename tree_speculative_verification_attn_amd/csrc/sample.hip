@@ -10,27 +10,30 @@
 // therefore {x : l'(x) > v} plus {x : l'(x) = v, x <= c} for a cut value v and
 // index c.
 //
-// One workgroup per row.  A row of up to 32768 entries lives in the registers
-// of 512 threads (E entries each), so LDS holds only the bins and a candidate
-// list and two workgroups share a CU; a longer row is re-read from memory on
-// every pass by 1024 threads (E = 0).  Once the candidates (the picked bin's
-// entries, the top-k survivors for the top-p stage, or the entries above a
-// lower bound of the top-k cut) fit a list of 4096 (index, value) pairs in
-// LDS, the remaining levels, tie counts and the top-p stage scan that list
-// instead of the row.  The top-k bound needs no pass of its own: in each
-// wave, the ceil(k/8)-th largest of the lanes' maxima has ceil(k/8) entries
-// at or above it (one per lane), so the smallest of these over the 8 waves of
-// a 512-thread workgroup (or 16 of a 1024-thread one, with ceil(k/16)) has at
-// least k entries at or above it and cannot exceed the cut value.  Each cut is found without sorting: a pass histograms the
-// candidates into 256 bins that are linear in the value over the current
-// value range, the bin where the cumulative weight (count, or mass in fixed
-// point) crosses the target becomes the next range, and a few such levels
-// isolate the cut value; ties at the cut are split by bisection over the
-// index.  Bins linear in the value spread logits over many bins, so the LDS
-// atomics rarely collide (bins over the key bits would put almost every logit
-// into a handful of exponent bins).  Masses are accumulated as 32.32 fixed
-// point integers, so every sum, and every decision taken from one, is the same
-// on every run.
+// One workgroup per row, in three layouts: rows of up to 32768 entries in
+// the registers of 512 threads; such rows staged in LDS by 1024 threads where
+// the register kernel has no short path; longer rows read from memory on
+// every pass.  Top-k first bounds its cut from below with no pass of its own:
+// in each wave, the ceil(k/8)-th largest of the lanes' maxima has ceil(k/8)
+// entries at or above it (one per lane), so the smallest of these over the 8
+// waves of a 512-thread workgroup (16 of a 1024-thread one, with ceil(k/16))
+// has at least k entries at or above it and cannot exceed the cut value.  The
+// entries above the bound go to a list of (index, value) pairs in LDS.  A list
+// of at most 512 kept entries is cut exactly by ranking: each entry's rank in
+// the order (value descending, index ascending), counted by all threads at
+// once, and the first rank whose count or prefix of masses reaches the
+// target.  Otherwise (top-p alone, a large k, a list that overflows) each cut
+// is found without sorting: a pass histograms the candidates into 256 bins
+// that are linear in the value over the current value range, the bin where
+// the cumulative weight (count, or mass in fixed point) crosses the target
+// becomes the next range, and a few such levels isolate the cut value; ties at
+// the cut are split by bisection over the index.  Bins linear in the value
+// spread logits over many bins, so the LDS atomics rarely collide (bins over
+// the key bits would put almost every logit into a handful of exponent bins).
+// Once such a search's candidates fit the list, its later levels scan the
+// list instead of the row.  Masses are accumulated as 32.32 fixed point
+// integers, so every sum, and every decision taken from one, is the same on
+// every run.
 #include "tv_common.h"
 
 namespace {
@@ -76,7 +79,7 @@ __device__ __forceinline__ float fkey_inv(uint32_t k) {
 // there.  E = 0: 1024 threads, thread t owns entries t, t + 1024, ..., read
 // from the input row and scaled on every full pass.  E = kStaged: the same
 // threads, with the scaled row staged in LDS once (for the searches the
-// register kernel does not shortcut: top-p alone, top-k above 512, a whole
+// register kernel does not shortcut: top-p alone, top-k above 256, a whole
 // row of probabilities); the list then keeps only indices.  Either way the
 // code of the searches exists once, so the kernel fits the instruction cache.
 template <int E>
