@@ -29,7 +29,13 @@
 //     (A = V^T from LDS transpose reads, B = P^T straight from the S^T
 //      accumulator, which already has the B-operand layout)
 //
-// fp32 path (vector ALU): same chunking, K/V tiles staged in LDS, all
+// The bf16 kernel can also build the masks itself (tree_mask_attn_verify):
+// every workgroup rebuilds its request's masks from the parents with the
+// one-wave builder that tree_build_mask uses, and the request's first
+// workgroup writes the mask outputs and the status.
+//
+// fp32 path (vector ALU): chunks of at least 64 keys, 16-key tiles (one
+// cache block) staged in LDS with the next tile's loads in flight, all
 // queries of the (b, h) per workgroup.
 #include "tree_mask.h"
 
