@@ -505,9 +505,10 @@ def measured_traffic(workload):
 
 
 def cpu_baseline(w, budget_s, gpu_value):
-    """The float64 oracle on a bounded sample of the same workload, scaled
-    to a whole step: attention is timed on a few (request, head) pairs,
-    verification on a few requests."""
+    """The float64 oracle on a bounded sample of the same workload (about
+    budget_s seconds of work), scaled to a whole step: attention is timed on
+    (request, head) pairs drawn at random, verification on requests taken in
+    turn, each until its share of the budget is spent."""
     import threadpoolctl
 
     from oracle import attention, commit, tree, verify
@@ -519,7 +520,7 @@ def cpu_baseline(w, budget_s, gpu_value):
         pairs_done = 0
         t_attn = 0.0
         rng = np.random.default_rng(0)
-        while t_attn < budget_s * 0.6 and pairs_done < w.B * w.H:
+        while t_attn < budget_s * 0.6:
             b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
             t = time.perf_counter()
             attention.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len, anc, st,
@@ -528,20 +529,21 @@ def cpu_baseline(w, budget_s, gpu_value):
             pairs_done += 1
         reqs = 0
         t_ver = 0.0
-        while t_ver < budget_s * 0.3 and reqs < w.B:
+        while t_ver < budget_s * 0.3:
+            r = reqs % w.B
             t = time.perf_counter()
-            verify.verify_greedy(w.parent[reqs:reqs + 1], w.token[reqs:reqs + 1],
-                                 w.target_logits[reqs:reqs + 1], [0])
+            verify.verify_greedy(w.parent[r:r + 1], w.token[r:r + 1], w.target_logits[r:r + 1], [0])
             verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0] * w.B,
-                              w.seed, requests=[reqs])
+                              w.seed, requests=[r])
             t_ver += time.perf_counter() - t
             reqs += 1
     full = (t_mask + t_attn * (w.B * w.H) / pairs_done + t_ver * w.B / reqs)
     v = w.B * w.N / full
     return {"value": round(v, 3), "unit": "verified tree tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 NumPy oracle, 1 thread: masks for all {w.B} requests, attention on "
-                      f"{pairs_done} of {w.B * w.H} (request, head) pairs, greedy + MSS on {reqs} of "
-                      f"{w.B} requests; scaled to one full step ({full:.1f} s)",
+            "sample": f"float64 NumPy oracle, 1 thread, {t_mask + t_attn + t_ver:.1f} s of work: masks for all "
+                      f"{w.B} requests, attention on {pairs_done} (request, head) pairs drawn at random from "
+                      f"{w.B * w.H}, greedy + MSS on {reqs} requests taken in turn from {w.B}; scaled to one "
+                      f"full step ({full:.2f} s)",
             "host_cpus": os.cpu_count(), "gpu_over_cpu": round(gpu_value / v, 1)}
 
 
