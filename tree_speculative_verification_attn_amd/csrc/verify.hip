@@ -277,6 +277,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   __shared__ int s_ga[2][kMaxG];
   __shared__ float s_rx2[2][TV_MAX_NODES];
   __shared__ float s_lxq[2][2];                  // MSS: p and q at the candidate's token, from wave 0
+  __shared__ uint32_t s_spec[2][2][8];           // the next pass's words and candidate per outcome, from wave 0
   __shared__ double s_gt[NW][kMaxG];             // slice totals of the current distribution (per wave)
   __shared__ double s_scan[NW];
   __shared__ int s_status0, s_timeout, s_found, s_last, s_xs;
@@ -374,6 +375,14 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   int rs_no = 0;                // workgroup sums done (bank parity)
   int pre = 0;                  // greedy/naive: the entered node's row is in lvn (1), qn (2), or not loaded (0)
   int c1 = -1, c2 = -1;         // greedy/naive: the children whose rows are prefetched
+
+  // MSS: the next pass's Philox words and candidate (node, token, draft row),
+  // worked out during the previous exchange for both outcomes of its test;
+  // absent before the first test.  zdraw: the word of the final draw at u.
+  bool have_next = false;
+  tv::u32x4 w_next{0u, 0u, 0u, 0u};
+  int c_next = -1, node_next = -1, tok_next = 0, qr_next = 0;
+  uint32_t zdraw = 0u;
 
   // The slice holding u2 * total, from the slice totals in index order, and
   // the threshold inside it (every wave, same values).
@@ -538,19 +547,35 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     int cand = -1;
     tv::u32x4 w{0u, 0u, 0u, 0u};
     float lx_c = 0.f, qx_c = 0.f;
+    if (mss && (U || pass == P_ENTER)) {
+      // the word of round j at u (a P_ENTER pass is round 0, whose third
+      // word also serves the final draw at u)
+      w = have_next ? w_next : tv::mss_words(a.seed, a.offset, b, u + 1, j);
+      if (pass == P_ENTER) zdraw = w.z;
+    }
     if (mss && U) {
-      w = tv::mss_words(a.seed, a.offset, b, u + 1, j);
-      cand = nth_bit(U, tv::pick_index(w.x, __builtin_popcountll(U)));
-      const float* qrow_c = sbase + static_cast<size_t>(s_qrow[cand]) * V;
+      int node_c, tok_c, qr_c;
+      if (have_next) {
+        cand = c_next;
+        node_c = node_next;
+        tok_c = tok_next;
+        qr_c = qr_next;
+      } else {
+        cand = nth_bit(U, tv::pick_index(w.x, __builtin_popcountll(U)));
+        node_c = MULTI ? s_node[cand] : cand;
+        tok_c = s_tok[cand];
+        qr_c = s_qrow[cand];
+      }
+      const float* qrow_c = sbase + static_cast<size_t>(qr_c) * V;
       // p and q at the candidate's token go out before the rows, so that
       // waiting for them does not wait for the rows; the poll wave loads
       // nothing here and takes them from wave 0 after the exchange
       if (wave != kPollWave) {
-        lx_c = lrow[s_tok[cand]];
-        qx_c = qrow_c[s_tok[cand]];
+        lx_c = lrow[tok_c];
+        qx_c = qrow_c[tok_c];
       }
       load8(qrow_c, qn, 0.f);
-      load8(lbase + static_cast<size_t>((MULTI ? s_node[cand] : cand) + 1) * V, lvn, -INFINITY);
+      load8(lbase + static_cast<size_t>(node_c + 1) * V, lvn, -INFINITY);
     }
     const uint32_t tag = static_cast<uint32_t>(ex_no + 1);
     const int par = ex_no & 1;
@@ -648,6 +673,40 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       }
     }
 
+    // ---- while the exchange is under way: the next pass's words ----
+    // MSS: lane 0 takes the outcome "accepted" (round 0 at the candidate's
+    // node), lane 1 "rejected" (round j + 1 at u, the candidate removed);
+    // each works out the Philox words, the next candidate and its node,
+    // token and draft row, so that none of it follows the decision.  Naive:
+    // the word of the draw at u.  The poll wave is polling; it takes wave
+    // 0's values from LDS after the exchange.
+    uint32_t spec[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    const bool speculate = (mss && cand >= 0) || (naive && pass == P_ENTER);
+    if (speculate && wave != kPollWave) {
+      const bool acc_lane = mss && lane == 0;
+      const int node = mss ? (MULTI ? s_node[cand] : cand) : u;
+      const tv::u32x4 ws = tv::mss_words(a.seed, a.offset, b, acc_lane || !mss ? node + 1 : u + 1,
+                                         acc_lane || !mss ? 0 : j + 1);
+      spec[0] = ws.x;
+      spec[1] = ws.y;
+      spec[2] = ws.z;
+      spec[3] = ws.w;
+      if (mss) {
+        const uint64_t Un = acc_lane ? s_child[node + 1] : U & ~(1ull << cand);
+        const int cs = Un ? nth_bit(Un, tv::pick_index(ws.x, __builtin_popcountll(Un))) : -1;
+        spec[4] = static_cast<uint32_t>(cs);
+        if (cs >= 0) {
+          spec[5] = static_cast<uint32_t>(MULTI ? s_node[cs] : cs);
+          spec[6] = static_cast<uint32_t>(s_tok[cs]);
+          spec[7] = static_cast<uint32_t>(s_qrow[cs]);
+        }
+      }
+      if (wave == 0 && lane < 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_spec[par][lane][i] = spec[i];
+      }
+    }
+
     // ---- the poll wave gathers every workgroup's words into LDS ----
     // (A wave reads a bank only between this exchange's barrier and the next
     // pass's first barrier, and the poll wave refills the bank two exchanges
@@ -683,6 +742,10 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     if (mss && cand >= 0 && wave == kPollWave) {
       lx_c = s_lxq[par][0];
       qx_c = s_lxq[par][1];
+    }
+    if (speculate && wave == kPollWave) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) spec[i] = s_spec[par][lane < 2 ? lane : 1][i];
     }
     ++ex_no;
     if (s_timeout) {
@@ -774,12 +837,22 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
             ++j;
             pass = P_RESID;
           }
+          const int from = accept ? 0 : 1;
+          w_next.x = __builtin_amdgcn_readlane(spec[0], from);
+          w_next.y = __builtin_amdgcn_readlane(spec[1], from);
+          w_next.z = __builtin_amdgcn_readlane(spec[2], from);
+          w_next.w = __builtin_amdgcn_readlane(spec[3], from);
+          c_next = static_cast<int>(__builtin_amdgcn_readlane(spec[4], from));
+          node_next = static_cast<int>(__builtin_amdgcn_readlane(spec[5], from));
+          tok_next = static_cast<int>(__builtin_amdgcn_readlane(spec[6], from));
+          qr_next = static_cast<int>(__builtin_amdgcn_readlane(spec[7], from));
+          have_next = true;
         }
       }
     } else if (need_z) {
       // MSS with no child left, or naive having entered u: locate the slice
       // of the draw (the next pass makes it)
-      locate(tv::mss_words(a.seed, a.offset, b, u + 1, 0).z);
+      locate(mss ? zdraw : __builtin_amdgcn_readlane(spec[2], 0));
       pass = mss ? P_FINAL : P_NSAMPLE;
     }
   }
