@@ -92,7 +92,7 @@ def main():
 
     import synth
     import tree_speculative_verification_attn_amd as tv
-    from tests.gpu_util import to_dev
+    from synth.device import to_dev
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -360,7 +360,7 @@ def compare_sequence_all(torch, cfgs):
     """Tree against per-path attention on the given workloads (one JSON line each)."""
     import synth
     import tree_speculative_verification_attn_amd as tv
-    from tests.gpu_util import to_dev
+    from synth.device import to_dev
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
     for cfg in cfgs:

@@ -33,9 +33,19 @@ Readings where the pages are silent:
 
 Rows: target_logits[b][0] is the root's context, row 1 + i node i's context.
 Outputs per request: accepted node ids (list), bonus token, number of ratio
-tests ("rounds"), status, and a trace of decision margins used to count near
-ties (|u - ratio| for every ratio test; the distance of u*sum(p) to the two
-cumulative sums bracketing the sampled token for the final sample).
+tests ("rounds"), status, and a trace of the walk's decisions in the order they
+are taken, each with its margin, used to count near ties: ("ratio", |u -
+ratio|) for every ratio test and ("sample", distance of u*sum(p) to the nearer
+of the two cumulative sums bracketing the sampled token, relative to sum(p))
+for every inverse-CDF draw.  A zero normaliser after a rejection is recorded
+as ("zero_residual", None): an event, not a decision.
+
+For the comparison with an implementation in other arithmetic, the walks take
+`flip`, the index of one decision (in trace order) to take the other way: a
+ratio test's outcome inverted, or a draw's neighbouring token on the side of
+the nearer cumulative sum.  Everything else is unchanged, so a result that
+equals the walk with decision k flipped, k a near tie, differs from the
+oracle first at that near tie.
 """
 import math
 
@@ -174,13 +184,47 @@ def sample_from(p_cur, u):
     return x, margin
 
 
+def sample_other(p_cur, u, x):
+    """The token a draw at u lands on when the cumulative sum nearer to the
+    threshold u*sum(p) falls on its other side: the last token before x with
+    nonzero mass (threshold near the sum below x) or the first one after x
+    (near the sum at x).  None if there is no such token."""
+    c = np.cumsum(p_cur)
+    t = u * c[-1]
+    lo = c[x - 1] if x > 0 else 0.0
+    if abs(t - lo) <= abs(c[x] - t):
+        nz = np.nonzero(p_cur[:x] > 0)[0]
+        return int(nz[-1]) if len(nz) else None
+    nz = np.nonzero(p_cur[x + 1:] > 0)[0]
+    return int(x + 1 + nz[0]) if len(nz) else None
+
+
+def _draw(p_cur, u, trace, flip):
+    """One inverse-CDF draw as a traced decision (see `flip` above)."""
+    x, margin = sample_from(p_cur, u)
+    if len([e for e in trace if e[1] is not None]) == flip:
+        alt = sample_other(p_cur, u, x)
+        x = x if alt is None else alt
+    trace.append(("sample", margin))
+    return x
+
+
+def _ratio_test(u1, ratio, trace, flip):
+    """One accept test as a traced decision (see `flip` above)."""
+    accept = u1 <= ratio
+    if len([e for e in trace if e[1] is not None]) == flip:
+        accept = not accept
+    trace.append(("ratio", abs(u1 - ratio) if math.isfinite(ratio) else math.inf))
+    return accept
+
+
 def select_child(untested, word0):
     """The random untested child: idx-th in ascending node order."""
     idx = philox.pick_index(word0, len(untested))
     return untested[idx]
 
 
-def mss_one(b, parent, token, logits, ssm, q_row, seed, offset):
+def mss_one(b, parent, token, logits, ssm, q_row, seed, offset, flip=None):
     """Multi-step speculative sampling for request b (assumes the data checks
     passed).  Returns (accepted, bonus, rounds, status, trace)."""
     accepted = []
@@ -206,8 +250,7 @@ def mss_one(b, parent, token, logits, ssm, q_row, seed, offset):
             ratio = ratio_of(p_cur[x], q_x)
             u1 = philox.unit_open0(w[1])
             rounds += 1
-            trace.append(("ratio", abs(u1 - ratio) if math.isfinite(ratio) else math.inf))
-            if u1 <= ratio:
+            if _ratio_test(u1, ratio, trace, flip):
                 accepted.append(s)
                 u = s
                 if not row_ok(logits[s + 1]):
@@ -219,7 +262,7 @@ def mss_one(b, parent, token, logits, ssm, q_row, seed, offset):
                 return accepted, -1, rounds, ST_NONFINITE, trace
             p_new, z = residual(p_cur, qrow)
             if z == 0.0:
-                trace.append(("zero_residual", 0.0))
+                trace.append(("zero_residual", None))
             p_cur = p_new
             untested = [c for c in untested if c != s]
             j += 1
@@ -227,16 +270,17 @@ def mss_one(b, parent, token, logits, ssm, q_row, seed, offset):
             continue
         # every child rejected, or a leaf reached by acceptance
         w = philox.words(seed, offset, b, slot, 0)
-        x, margin = sample_from(p_cur, philox.unit_open0(w[2]))
-        trace.append(("sample", margin))
+        x = _draw(p_cur, philox.unit_open0(w[2]), trace, flip)
         return accepted, x, rounds, ST_OK, trace
 
 
 def verify_mss(parent, token, target_logits, ssm_probs, q_row, status, seed, offset=0,
-               requests=None):
+               requests=None, flips=None):
     """Batched MSS verification.  Returns dict of accepted [B][N] (-1 padded),
-    num_accepted [B], bonus [B], rounds [B], status [B] and traces (list per
-    request).  `requests` restricts the work to a subset (others stay -1)."""
+    num_accepted [B], bonus [B], rounds [B], status [B], traces (list per
+    request) and redo(b, k), the same call for request b alone with its
+    decision k flipped.  `requests` restricts the work to a subset (others
+    stay -1); `flips` maps a request to the decision to flip."""
     B, N = token.shape
     V = target_logits.shape[2]
     R = ssm_probs.shape[1]
@@ -252,7 +296,7 @@ def verify_mss(parent, token, target_logits, ssm_probs, q_row, status, seed, off
         if st[b] != ST_OK:
             continue
         path, bn, rd, s_b, tr = mss_one(b, parent[b], token[b], target_logits[b], ssm_probs[b],
-                                        q_row[b], seed, offset)
+                                        q_row[b], seed, offset, (flips or {}).get(b))
         traces[b] = tr
         st[b] = s_b
         if s_b != ST_OK:
@@ -262,7 +306,9 @@ def verify_mss(parent, token, target_logits, ssm_probs, q_row, status, seed, off
         bonus[b] = bn
         rounds[b] = rd
     return dict(accepted=acc, num_accepted=num, bonus=bonus, rounds=rounds,
-                status=np.array(st), traces=traces)
+                status=np.array(st), traces=traces,
+                redo=lambda b, k: verify_mss(parent, token, target_logits, ssm_probs, q_row, status, seed,
+                                             offset, requests=[b], flips={b: k}))
 
 
 # ----------------------------------------------------------------------------
@@ -306,7 +352,7 @@ def _proposal_checks(parent_b, token_b, V, prop_node_b, prop_row_b, R):
     return ST_OK
 
 
-def mss_multi_one(b, parent, token, logits, ssm, prop_node, prop_row, seed, offset):
+def mss_multi_one(b, parent, token, logits, ssm, prop_node, prop_row, seed, offset, flip=None):
     """VerifyStochastic over proposals for request b (assumes the checks
     passed).  Returns (accepted nodes, bonus, rounds, status, trace) as
     mss_one."""
@@ -334,8 +380,7 @@ def mss_multi_one(b, parent, token, logits, ssm, prop_node, prop_row, seed, offs
             ratio = ratio_of(p_cur[x], q_x)
             u1 = philox.unit_open0(w[1])
             rounds += 1
-            trace.append(("ratio", abs(u1 - ratio) if math.isfinite(ratio) else math.inf))
-            if u1 <= ratio:
+            if _ratio_test(u1, ratio, trace, flip):
                 accepted.append(c)
                 u = c
                 if not row_ok(logits[c + 1]):
@@ -347,22 +392,22 @@ def mss_multi_one(b, parent, token, logits, ssm, prop_node, prop_row, seed, offs
                 return accepted, -1, rounds, ST_NONFINITE, trace
             p_new, z = residual(p_cur, qrow)
             if z == 0.0:
-                trace.append(("zero_residual", 0.0))
+                trace.append(("zero_residual", None))
             p_cur = p_new
             untested = [t for t in untested if t != s]
             j += 1
         if moved:
             continue
         w = philox.words(seed, offset, b, slot, 0)
-        x, margin = sample_from(p_cur, philox.unit_open0(w[2]))
-        trace.append(("sample", margin))
+        x = _draw(p_cur, philox.unit_open0(w[2]), trace, flip)
         return accepted, x, rounds, ST_OK, trace
 
 
 def verify_mss_multi(parent, token, target_logits, ssm_probs, prop_node, prop_row, status, seed,
-                     offset=0):
-    """Batched VerifyStochastic over proposals; outputs as verify_mss.
-    prop_node, prop_row: [B][S] int arrays (S <= 64)."""
+                     offset=0, requests=None, flips=None):
+    """Batched VerifyStochastic over proposals; outputs (redo included),
+    `requests` and `flips` as verify_mss.  prop_node, prop_row: [B][S] int
+    arrays (S <= 64)."""
     B, N = token.shape
     V = target_logits.shape[2]
     R = ssm_probs.shape[1]
@@ -372,13 +417,13 @@ def verify_mss_multi(parent, token, target_logits, ssm_probs, prop_node, prop_ro
     rounds = np.full(B, -1, dtype=np.int64)
     st = [int(x) for x in status]
     traces = [[] for _ in range(B)]
-    for b in range(B):
+    for b in (range(B) if requests is None else requests):
         if st[b] == ST_OK:
             st[b] = _proposal_checks(parent[b], token[b], V, prop_node[b], prop_row[b], R)
         if st[b] != ST_OK:
             continue
         path, bn, rd, s_b, tr = mss_multi_one(b, parent[b], token[b], target_logits[b], ssm_probs[b],
-                                              prop_node[b], prop_row[b], seed, offset)
+                                              prop_node[b], prop_row[b], seed, offset, (flips or {}).get(b))
         traces[b] = tr
         st[b] = s_b
         if s_b != ST_OK:
@@ -388,7 +433,9 @@ def verify_mss_multi(parent, token, target_logits, ssm_probs, prop_node, prop_ro
         bonus[b] = bn
         rounds[b] = rd
     return dict(accepted=acc, num_accepted=num, bonus=bonus, rounds=rounds,
-                status=np.array(st), traces=traces)
+                status=np.array(st), traces=traces,
+                redo=lambda b, k: verify_mss_multi(parent, token, target_logits, ssm_probs, prop_node, prop_row,
+                                                   status, seed, offset, requests=[b], flips={b: k}))
 
 
 # ----------------------------------------------------------------------------
@@ -401,7 +448,7 @@ def naive_reject_prob(p, child_tokens):
     return 1.0 - float(sum(p[t] for t in toks))
 
 
-def naive_one(b, parent, token, logits, seed, offset):
+def naive_one(b, parent, token, logits, seed, offset, flip=None):
     """Naive sampling verification for request b (Theorem 4.3's comparator):
     at node u draw x from P_LLM(.|u); if a child of u carries token x, move to
     the lowest such child, otherwise x is the bonus token and the walk stops.
@@ -420,8 +467,7 @@ def naive_one(b, parent, token, logits, seed, offset):
             return accepted, -1, ST_NONFINITE, trace
         p = softmax_row(logits[u + 1])
         w = philox.words(seed, offset, b, u + 1, 0)
-        x, margin = sample_from(p, philox.unit_open0(w[2]))
-        trace.append(("sample", margin))
+        x = _draw(p, philox.unit_open0(w[2]), trace, flip)
         nxt = next((c for c in children_of(parent, u) if int(token[c]) == x), None)
         if nxt is None:
             return accepted, x, ST_OK, trace
@@ -429,9 +475,9 @@ def naive_one(b, parent, token, logits, seed, offset):
         u = nxt
 
 
-def verify_naive(parent, token, target_logits, status, seed, offset=0):
+def verify_naive(parent, token, target_logits, status, seed, offset=0, requests=None, flips=None):
     """Batched naive sampling verification; same outputs as verify_greedy plus
-    traces."""
+    traces and redo, with `requests` and `flips` as verify_mss."""
     B, N = token.shape
     V = target_logits.shape[2]
     acc = np.full((B, N), -1, dtype=np.int64)
@@ -439,12 +485,13 @@ def verify_naive(parent, token, target_logits, status, seed, offset=0):
     bonus = np.full(B, -1, dtype=np.int64)
     st = [int(s) for s in status]
     traces = [[] for _ in range(B)]
-    for b in range(B):
+    for b in (range(B) if requests is None else requests):
         if st[b] == ST_OK:
             st[b] = _request_checks(parent[b], token[b], V)
         if st[b] != ST_OK:
             continue
-        path, bn, s_b, tr = naive_one(b, parent[b], token[b], target_logits[b], seed, offset)
+        path, bn, s_b, tr = naive_one(b, parent[b], token[b], target_logits[b], seed, offset,
+                                      (flips or {}).get(b))
         traces[b] = tr
         st[b] = s_b
         if s_b != ST_OK:
@@ -452,4 +499,6 @@ def verify_naive(parent, token, target_logits, status, seed, offset=0):
         acc[b, : len(path)] = path
         num[b] = len(path)
         bonus[b] = bn
-    return dict(accepted=acc, num_accepted=num, bonus=bonus, status=np.array(st), traces=traces)
+    return dict(accepted=acc, num_accepted=num, bonus=bonus, status=np.array(st), traces=traces,
+                redo=lambda b, k: verify_naive(parent, token, target_logits, status, seed, offset,
+                                               requests=[b], flips={b: k}))

@@ -8,14 +8,7 @@ from oracle import attention as o_attn
 from oracle import commit as o_commit
 from oracle import tree as o_tree
 from oracle import verify as o_verify
-
-DEV = "cuda:0"
-
-
-def to_dev(a, bf16=False):
-    if bf16:
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
-    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+from synth.device import DEV, to_dev
 
 
 def u64(t):
@@ -153,10 +146,29 @@ def out_to_f64(t):
     return t.cpu().numpy().astype(np.float64)
 
 
+NEAR_TIE = 1e-6
+
+
+def _near_tie_excused(ref, b, same):
+    """True iff the oracle's walk of request b, with one of its near-tie
+    decisions (margin < 1e-6) taken the other way, gives the device's result
+    (`same` compares one request of an oracle result with the device's).
+    Everything before the flipped decision is the oracle's own walk, so the
+    device's result then first departs from the oracle at that near tie."""
+    margins = [m for _, m in ref["traces"][b] if m is not None]
+    for k, m in enumerate(margins):
+        if m < NEAR_TIE and same(ref["redo"](b, k)):
+            return True
+    return False
+
+
 def compare_mss(run, ref):
-    """Compare GPU MSS outputs with the oracle; mismatches are allowed only
-    for requests whose oracle trace holds a near tie (margin < 1e-6).
-    Returns (n_exact, n_near_tie_excused, list of unexcused request ids)."""
+    """Compare GPU MSS outputs with the oracle.  A request may differ only
+    where its first divergent decision is a near tie of the oracle's walk
+    (|u - ratio| < 1e-6, or a draw within 1e-6 of a cumulative-sum boundary):
+    the oracle's walk with that one decision flipped must give the device's
+    result.  Returns (n_exact, n_near_tie_excused, list of unexcused request
+    ids)."""
     acc = run.m_acc.cpu().numpy()
     num = run.m_num.cpu().numpy()
     bonus = run.m_bonus.cpu().numpy()
@@ -165,14 +177,13 @@ def compare_mss(run, ref):
     exact = excused = 0
     bad = []
     for b in range(len(num)):
-        same = (num[b] == ref["num_accepted"][b] and bonus[b] == ref["bonus"][b]
-                and rounds[b] == ref["rounds"][b] and st[b] == ref["status"][b]
-                and np.array_equal(acc[b], ref["accepted"][b]))
-        if same:
+        def same(r, b=b):
+            return (num[b] == r["num_accepted"][b] and bonus[b] == r["bonus"][b]
+                    and rounds[b] == r["rounds"][b] and st[b] == r["status"][b]
+                    and np.array_equal(acc[b], r["accepted"][b]))
+        if same(ref):
             exact += 1
-            continue
-        tr = ref["traces"][b]
-        if tr and min(m for _, m in tr) < 1e-6:
+        elif _near_tie_excused(ref, b, same):
             excused += 1
         else:
             bad.append(b)
@@ -181,16 +192,19 @@ def compare_mss(run, ref):
 
 def compare_naive(run, ref):
     """Naive verification against the oracle: exact, except requests whose
-    oracle trace holds a draw within 1e-6 of a cumulative-mass boundary.
-    Returns (n_exact, n_near_tie_excused, list of unexcused request ids)."""
+    first divergent draw is within 1e-6 of a cumulative-mass boundary (as
+    compare_mss).  Returns (n_exact, n_near_tie_excused, list of unexcused
+    request ids)."""
     acc, num, bonus, st = (t.cpu().numpy() for t in (run.n_acc, run.n_num, run.n_bonus, run.status))
     exact = excused = 0
     bad = []
     for b in range(len(num)):
-        if (num[b] == ref["num_accepted"][b] and bonus[b] == ref["bonus"][b] and st[b] == ref["status"][b]
-                and np.array_equal(acc[b], ref["accepted"][b])):
+        def same(r, b=b):
+            return (num[b] == r["num_accepted"][b] and bonus[b] == r["bonus"][b] and st[b] == r["status"][b]
+                    and np.array_equal(acc[b], r["accepted"][b]))
+        if same(ref):
             exact += 1
-        elif ref["traces"][b] and min(m for _, m in ref["traces"][b]) < 1e-6:
+        elif _near_tie_excused(ref, b, same):
             excused += 1
         else:
             bad.append(b)

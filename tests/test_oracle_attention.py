@@ -150,3 +150,92 @@ def test_status_paths():
     bt[0, 0] = w.num_blocks
     out, s = attention.tree_attention(w.q, w.k_cache, w.v_cache, bt, w.prefix_len, anc, st, "f32", w.scale)
     assert s == [ST_BAD_BLOCK]
+
+
+# ----------------------------------------------------------------------------
+# The bf16 widening and the paged-slot read, pinned without the oracle's own
+# helpers: bfloat16 is the upper half of an IEEE-754 binary32 (1 sign bit,
+# 8 exponent bits with bias 127, 7 fraction bits), so its value follows from
+# the fields alone.
+# ----------------------------------------------------------------------------
+def _bf16_value(bits):
+    """Value of a bfloat16 bit pattern from its fields (pure Python)."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * float("inf") if f == 0 else float("nan")
+    if e == 0:
+        return sign * (f / 128.0) * 2.0 ** -126
+    return sign * (1.0 + f / 128.0) * 2.0 ** (e - 127)
+
+
+BF16_TABLE = [
+    (0x0000, 0.0), (0x8000, -0.0), (0x3F80, 1.0), (0xBF80, -1.0), (0x4000, 2.0), (0xC040, -3.0),
+    (0x3F81, 1.0 + 2.0 ** -7), (0x3F00, 0.5), (0x4049, 3.140625), (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127),
+    (0x0080, 2.0 ** -126), (0x0001, 2.0 ** -133), (0x007F, 127 * 2.0 ** -133), (0x7F80, float("inf")),
+    (0xFF80, float("-inf")), (0x3DCD, 0.10009765625), (0x42F7, 123.5),
+]
+
+
+def test_widen_bf16_bit_patterns():
+    bits = np.array([b for b, _ in BF16_TABLE], dtype=np.uint16)
+    got = widen(bits, "bf16")
+    for (b, v), g in zip(BF16_TABLE, got):
+        assert g == v and np.signbit(g) == np.signbit(v), (hex(b), g, v)
+        assert _bf16_value(b) == v
+    # every finite pattern against the field formula
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((allb >> 7) & 0xFF) != 0xFF
+    g = widen(allb[finite], "bf16")
+    ref = np.array([_bf16_value(int(b)) for b in allb[finite]])
+    assert np.array_equal(g, ref)
+    assert np.all(np.isnan(widen(np.array([0x7FC0, 0xFFC1], dtype=np.uint16), "bf16")))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_paged_read_against_contiguous(dtype):
+    """The oracle's attention over a paged cache equals attention computed by
+    hand on the same keys held contiguously: the test scatters contiguous
+    K/V into blocks of 16 slots through its own permuted block table."""
+    rng = np.random.default_rng(17)
+    H, D, L = 3, 16, 45
+    parent = [-1, 0, 0, 1, -1, 4]
+    N = len(parent)
+    T = L + N
+    nblk = (T + 15) // 16
+    if dtype == "bf16":
+        bits = rng.integers(0x3C00, 0x4100, size=(3, T, H, D)) | (rng.integers(0, 2, size=(3, T, H, D)) << 15)
+        bits = bits.astype(np.uint16)
+        vals = np.vectorize(_bf16_value)(bits.astype(np.int64))
+        kc_cont, vc_cont, q_cont = bits[0], bits[1], bits[2][:N]
+        kf, vf, qf = vals[0], vals[1], vals[2][:N]
+        dt_np = np.uint16
+    else:
+        vals = rng.standard_normal((3, T, H, D)).astype(np.float32)
+        kc_cont, vc_cont, q_cont = vals[0], vals[1], vals[2][:N]
+        kf, vf, qf = (x.astype(np.float64) for x in (vals[0], vals[1], vals[2][:N]))
+        dt_np = np.float32
+    # physical blocks in a random order, with unused blocks between them
+    num_blocks = 3 * nblk
+    table = rng.permutation(num_blocks)[:nblk].astype(np.int32)
+    kc = np.zeros((num_blocks, H, 16, D), dtype=dt_np)
+    vc = np.zeros((num_blocks, H, 16, D), dtype=dt_np)
+    for t in range(T):
+        for h in range(H):
+            kc[table[t // 16], h, t % 16] = kc_cont[t, h]
+            vc[table[t // 16], h, t % 16] = vc_cont[t, h]
+    q = q_cont[None]                                # [1][N][H][D]
+    anc, _, _, st = tree.build_mask_batch(np.array([parent], dtype=np.int32))
+    scale = 1.0 / np.sqrt(D)
+    out, st2 = attention.tree_attention(q, kc, vc, table[None], np.array([L], dtype=np.int32), anc, st,
+                                        dtype, scale)
+    assert st2 == [ST_OK]
+    for i in range(N):
+        path = tree.path_to(parent, i)
+        keys = list(range(L)) + [L + j for j in path]
+        for h in range(H):
+            s = np.array([sum(qf[i, h, d] * kf[t, h, d] for d in range(D)) * scale for t in keys])
+            p = np.exp(s - s.max())
+            ref = (p[:, None] * vf[keys, h]).sum(axis=0) / p.sum()
+            np.testing.assert_allclose(out[0, i, h], ref, rtol=1e-12, atol=1e-13)

@@ -504,3 +504,79 @@ def test_rounds_and_determinism():
     b = verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, st, w.seed)
     assert a["bonus"][0] == b["bonus"][0] and np.array_equal(a["accepted"], b["accepted"])
     assert a["rounds"][0] >= a["num_accepted"][0]
+
+
+# ----------------------------------------------------------------------------
+# Flipped decisions: the near-tie comparison replays the oracle's walk with
+# one decision taken the other way.
+# ----------------------------------------------------------------------------
+def test_sample_other_neighbours():
+    p = np.array([0.2, 0.0, 0.3, 0.0, 0.5])
+    # threshold just below the sum up to token 2 (0.5): drawn 2, other side 4
+    x, m = verify.sample_from(p, 0.5 - 1e-9)
+    assert x == 2 and m < 1e-8 and verify.sample_other(p, 0.5 - 1e-9, x) == 4
+    # threshold just above the sum up to token 0 (0.2): drawn 2, other side 0
+    x, m = verify.sample_from(p, 0.2 + 1e-9)
+    assert x == 2 and verify.sample_other(p, 0.2 + 1e-9, x) == 0
+    # no token on the other side
+    assert verify.sample_other(p, 1e-12, 0) is None
+    assert verify.sample_other(p, 1.0, 4) is None
+
+
+def test_flip_inverts_one_decision():
+    # one root child whose ratio test rejects (p(x) tiny, q(x) large); with
+    # the test flipped the child is accepted and the bonus comes from its
+    # own one-hot row; flipping the final draw moves it to a neighbour
+    V = 16
+    parent = np.array([[-1]])
+    token = np.array([[5]])
+    tl = np.zeros((1, 2, V), dtype=np.float32)
+    tl[0, 0] = _onehot_logits(V, 9)
+    tl[0, 1] = _onehot_logits(V, 11, big=120.0)
+    sp = np.full((1, 1, V), 0.5 / (V - 1), dtype=np.float32)
+    sp[0, 0, 5] = 0.5
+    qr = np.zeros((1, 1), dtype=np.int32)
+    r = verify.verify_mss(parent, token, tl, sp, qr, [0], 3)
+    assert r["num_accepted"][0] == 0 and [k for k, _ in r["traces"][0]] == ["ratio", "sample"]
+    f0 = r["redo"](0, 0)
+    assert f0["num_accepted"][0] == 1 and list(f0["accepted"][0][:1]) == [0] and f0["bonus"][0] == 11
+    assert f0["rounds"][0] == 1
+    # decisions past the end of the walk change nothing
+    f9 = r["redo"](0, 9)
+    assert f9["bonus"][0] == r["bonus"][0] and f9["num_accepted"][0] == r["num_accepted"][0]
+    # the draw: its neighbour on the nearer side, or itself if it has none
+    f1 = r["redo"](0, 1)
+    p_res = np.maximum(0.0, verify.softmax_row(tl[0, 0]) - sp[0, 0].astype(np.float64))
+    p_res /= p_res.sum()
+    u2 = philox.unit_open0(philox.words(3, 0, 0, 0, 0)[2])
+    alt = verify.sample_other(p_res, u2, int(r["bonus"][0]))
+    assert f1["bonus"][0] == (r["bonus"][0] if alt is None else alt)
+
+
+def test_zero_residual_is_an_event_not_a_decision():
+    # q = 2p on the root row: the rejection leaves p unchanged and the trace
+    # records the event without a margin
+    V = 6
+    parent = np.array([[-1]])
+    token = np.array([[2]])
+    logits = np.log(np.array([0.1, 0.2, 0.3, 0.1, 0.2, 0.1])).astype(np.float32)
+    tl = np.stack([logits, logits])[None]
+    p = verify.softmax_row(logits)
+    sp = (2 * p).astype(np.float32)[None, None]
+    r = verify.verify_mss(parent, token, tl, sp, np.zeros((1, 1), dtype=np.int32), [0], 0)
+    assert r["num_accepted"][0] == 0            # (this seed rejects the child)
+    assert [k for k, _ in r["traces"][0]] == ["ratio", "zero_residual", "sample"]
+    assert r["traces"][0][1][1] is None
+    # the draw is decision 1, so flipping decision 1 moves the bonus
+    x = int(r["bonus"][0])
+    alt = r["redo"](0, 1)["bonus"][0]
+    assert alt != x and abs(alt - x) >= 1
+
+
+def test_naive_redo_flips_the_draw():
+    w = synth.make_workload(1)
+    r = verify.verify_naive(w.parent, w.token, w.target_logits, [0], w.seed)
+    n = len(r["traces"][0])
+    f = r["redo"](0, n - 1)          # the last draw taken the other way
+    assert f["num_accepted"][0] == r["num_accepted"][0]
+    assert np.array_equal(f["accepted"], r["accepted"])
