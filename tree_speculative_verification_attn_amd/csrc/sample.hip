@@ -36,6 +36,8 @@
 // every run.
 #include "tv_common.h"
 
+#include <atomic>
+
 namespace {
 
 constexpr int kTfBins = 256;
@@ -791,13 +793,17 @@ extern "C" tv_status tree_logits_transform(int rows, int V, const float* in, flo
     else if (V <= 8 * kRgQuad) hipLaunchKernelGGL(transform_kernel<32>, grid, rg, 0, stream, a);
     else hipLaunchKernelGGL(transform_kernel<64>, grid, rg, 0, stream, a);
   } else if (V <= kStagedMax) {
-    static bool lds_ok = false;          // a function attribute: set once per process
-    if (!lds_ok) {
+    // the kernel's dynamic LDS limit is raised once per device (a repeated
+    // call from another thread sets the same value)
+    static std::atomic<bool> lds_ok[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TV_EHIP;
+    if (dev < 0 || dev >= 64 || !lds_ok[dev].load(std::memory_order_acquire)) {
       if (hipFuncSetAttribute(reinterpret_cast<const void*>(transform_kernel<kStaged>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(kStagedMax * sizeof(float))) != hipSuccess)
         return TV_EHIP;
-      lds_ok = true;
+      if (dev >= 0 && dev < 64) lds_ok[dev].store(true, std::memory_order_release);
     }
     const size_t row_bytes = static_cast<size_t>((V + 3) / 4 * 4) * sizeof(float);
     hipLaunchKernelGGL(transform_kernel<kStaged>, grid, st, row_bytes, stream, a);

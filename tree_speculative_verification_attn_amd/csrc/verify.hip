@@ -41,6 +41,8 @@
 #include "kv_move.h"
 
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 
 namespace {
 
@@ -94,7 +96,8 @@ struct WalkArgs {
   int32_t* num_accepted;
   int32_t* bonus;
   int32_t* rounds;
-  uint32_t* done;
+  uint32_t* done;            // [B][64]: word 0 counts the workgroups that left; words 2-3 hold
+                            // MSS's sampled token, tagged, from the slice that found it
   uint64_t* hdr;
   uint64_t* kid;
   bool commit;              // MSS: also compact the accepted path in the KV cache
@@ -103,6 +106,7 @@ struct WalkArgs {
   int S;                    //   slots per request
   const int32_t* prop_node; //   [B][S] node of each proposal, -1 = unused slot
   const int32_t* prop_row;  //   [B][S] its proposer's row of ssm
+  unsigned spin_limit;      // polls of one exchanged word before a wait gives up
 };
 constexpr int kMoveChunks = 8;                     // 16-byte chunks per thread per batch of the move
 
@@ -122,10 +126,10 @@ __device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t tag, uint32_t v
 }
 
 // Poll n consecutive tagged words until all carry `tag`; their data go to
-// out[0..n).  Returns false when the poll bound runs out.
+// out[0..n).  Returns false when `limit` polls did not see it.
 template <int n>
-__device__ __forceinline__ bool take_tagged(uint64_t* p, uint32_t tag, uint32_t (&out)[kHdr]) {
-  for (unsigned polls = 0; polls < kSpinLimit; ++polls) {
+__device__ __forceinline__ bool take_tagged(uint64_t* p, uint32_t tag, uint32_t (&out)[kHdr], unsigned limit) {
+  for (unsigned polls = 0; polls < limit; ++polls) {
     uint64_t x[n];
 #pragma unroll
     for (int i = 0; i < n; ++i) x[i] = ld_u64(p + i);
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         bool to = false;
         if (lane == 0) {
           uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
-          if (!take_tagged<1>(kid + par * 64, tag, v)) to = true;
+          if (!take_tagged<1>(kid + par * 64, tag, v, a.spin_limit)) to = true;
           s_xs = static_cast<int>(v[0]);
         }
         if (__any(to) && lane == 0) s_timeout = 1;
@@ -715,13 +719,13 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       bool to = false;
       if (pass == P_RESID && (MULTI || lane < N) && ((U >> lane) & 1ull)) {
         uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
-        if (!take_tagged<1>(kid + par * 64 + lane, tag, v)) to = true;
+        if (!take_tagged<1>(kid + par * 64 + lane, tag, v, a.spin_limit)) to = true;
         s_rx2[par][lane] = __uint_as_float(v[0]);
       }
       for (int gg = lane; gg < G; gg += 64) {
         uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
-        const bool okp = pass == P_ENTER ? take_tagged<4>(bank + static_cast<size_t>(gg) * kHdr, tag, v)
-                                         : take_tagged<3>(bank + static_cast<size_t>(gg) * kHdr, tag, v);
+        const bool okp = pass == P_ENTER ? take_tagged<4>(bank + static_cast<size_t>(gg) * kHdr, tag, v, a.spin_limit)
+                                         : take_tagged<3>(bank + static_cast<size_t>(gg) * kHdr, tag, v, a.spin_limit);
         if (!okp) to = true;
         if (pass == P_ENTER) {
           s_gm[par][gg] = __uint_as_float(v[0]);
@@ -861,10 +865,16 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   __syncthreads();
   const bool ok = status == TV_REQ_OK && !s_timeout;
 
-  // ---- MSS's final sample: the owner slice's workgroup finds the token ----
-  if (mss && ok && pass == P_FINAL && g == owner) {
+  // ---- MSS's final sample: the owner slice's workgroup finds the token.
+  // Workgroup 0 writes every output of the request, so an owner other than
+  // workgroup 0 hands the token over in a tagged word of the request's
+  // workspace line (workgroup 0 waits for it below). ----
+  uint64_t* const xword = reinterpret_cast<uint64_t*>(done + 2);
+  const bool final_draw = mss && ok && pass == P_FINAL;
+  if (final_draw && g == owner) {
     const int x = slice_search();
-    if (t == 0) a.bonus[b] = x;
+    if (g == 0) bonus = x;
+    else if (t == 0) put_tagged(xword, 1u, static_cast<uint32_t>(x));
   }
 
   int stt = status;
@@ -885,8 +895,24 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     }
   }
 
-  // ---- results: workgroup 0 writes the path (and the greedy / naive bonus) ----
+  // ---- results: workgroup 0 writes the path, the bonus and the status.
+  // MSS's token from another slice arrives in the tagged word; if it does not
+  // within the wait bound, the request times out like any other wait (no
+  // output, no move), so the outputs always come from one decision. ----
   if (g == 0) {
+    if (final_draw && owner != 0) {
+      if (t == 0) {
+        uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
+        s_xs = take_tagged<1>(xword, 1u, v, a.spin_limit) ? static_cast<int>(v[0]) : -1;
+      }
+      __syncthreads();
+      if (s_xs >= 0) {
+        bonus = s_xs;
+      } else {
+        stt = TV_REQ_TIMEOUT;
+        mres = -1;
+      }
+    }
     if (t == 0) {
       if (stt != TV_REQ_OK) {
         a.status[b] = stt;
@@ -895,11 +921,11 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         if (a.rounds) a.rounds[b] = -1;
       } else {
         a.num_accepted[b] = k;
-        if (!mss || owner < 0) a.bonus[b] = bonus;   // MSS: the owner slice writes it
+        a.bonus[b] = bonus;
         if (a.rounds) a.rounds[b] = rounds;
       }
     }
-    const int kk = ok ? k : 0;
+    const int kk = stt == TV_REQ_OK ? k : 0;
     for (int i = t; i < N; i += kCoThreads) a.accepted[static_cast<size_t>(b) * N + i] = i < kk ? s_acc[i] : -1;
   }
 
@@ -926,7 +952,10 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   if (s_last) {          // every workgroup has finished reading
     for (int i = t; i < 2 * G * kHdr; i += kCoThreads) st_u64(hdr + i, 0ull);
     if (t < 128) st_u64(kid + t, 0ull);
-    if (t == 0) st_u32(done, 0u);
+    if (t == 0) {
+      st_u32(done, 0u);
+      st_u64(xword, 0ull);
+    }
   }
 }
 
@@ -1502,16 +1531,22 @@ const void* walk_kernel_of(int variant) {
   return reinterpret_cast<const void*>(walk_kernel<MODE_GREEDY, VEC, false>);
 }
 
+// Workgroups of a walk variant resident at once on device dev (cached per
+// device; every thread that fills an entry computes the same value, so
+// relaxed atomics suffice).
 int walk_capacity(int dev, int variant, bool vec) {
-  static int cache[2][5][64];
+  static std::atomic<int> cache[2][5][64];
   const bool cached = dev >= 0 && dev < 64 && variant >= 0 && variant < 5;
-  if (cached && cache[vec][variant][dev] > 0) return cache[vec][variant][dev];
+  if (cached) {
+    const int c = cache[vec][variant][dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   const void* fn = vec ? walk_kernel_of<true>(variant) : walk_kernel_of<false>(variant);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kCoThreads, 0) != hipSuccess) return 0;
   const int cap = cus * std::max(1, per_cu);
-  if (cached) cache[vec][variant][dev] = cap;
+  if (cached) cache[vec][variant][dev].store(cap, std::memory_order_relaxed);
   return cap;
 }
 
@@ -1580,9 +1615,23 @@ tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
   return TV_OK;
 }
 
+// The wait bound of the sliced walk's exchanges: kSpinLimit polls, or the
+// value of TREEVERIFY_WALK_WAIT_POLLS (a decimal count; 0 makes every wait
+// give up at once, which tests the time-out path without a hang).
+unsigned wait_limit() {
+  const char* e = std::getenv("TREEVERIFY_WALK_WAIT_POLLS");
+  if (e && *e) {
+    char* end = nullptr;
+    const unsigned long v = std::strtoul(e, &end, 10);
+    if (end && *end == '\0') return static_cast<unsigned>(std::min<unsigned long>(v, kSpinLimit));
+  }
+  return kSpinLimit;
+}
+
 WalkArgs make_args(int mode, int N, int V, int R, void* workspace, int B) {
   WalkArgs a{};
   a.mode = mode;
+  a.spin_limit = wait_limit();
   a.N = N;
   a.V = V;
   a.R = R;
