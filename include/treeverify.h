@@ -11,7 +11,9 @@
  *
  * Conventions shared by every entry point
  *  - All array pointers are DEVICE pointers owned by the caller.  The library
- *    allocates nothing, frees nothing and keeps no state between calls.
+ *    allocates nothing, frees nothing and keeps no state between calls (it
+ *    caches, per device, only what the device reports about itself: its
+ *    compute unit count and the occupancy of its kernels).
  *  - Every call is asynchronous on `stream` (0 = the null stream).
  *  - The return value reports host-checkable problems only: bad sizes or
  *    dtypes, null pointers, a workspace that is too small, a failed launch.
@@ -71,9 +73,11 @@ enum {
   TV_REQ_KV_CAPACITY = 6,   /* prefix_len < 0 or prefix_len + N > max_blocks * block_size */
   TV_REQ_BAD_BLOCK = 7,     /* a block_table entry the call needs is outside [0, num_blocks) */
   TV_REQ_BAD_ACCEPTED = 8,  /* num_accepted > N or an accepted id outside [0, N) */
-  TV_REQ_TIMEOUT = 9        /* a verify call's workgroups did not meet within the
-                               wait bound (they were not all resident); the
-                               request's outputs are as for a skipped request */
+  TV_REQ_TIMEOUT = 9        /* a wait inside a call ran out: the workgroups of
+                               a sliced verify walk did not meet within the
+                               wait bound (they were not all resident), or an
+                               attention group barrier did; the request's
+                               outputs are as for a skipped request */
 };
 
 /*
@@ -125,9 +129,20 @@ tv_status tree_build_mask(int B, int N, const int32_t* parent, uint64_t* anc,
  *                 set at run time, so repeated calls agree to rounding, not bit
  *                 for bit
  *   workspace     ws_bytes >= tree_attn_verify_workspace(...) bytes of device
- *                 memory for per-chunk partial results (may be null when that
- *                 size is 0); contents on entry do not matter.  Calls that
- *                 overlap in time must not share a workspace.
+ *                 memory (may be null when that size is 0: fp32 with one
+ *                 chunk per (request, head)).  For bf16 its first 1024 bytes
+ *                 hold the counters from which the workgroups take their
+ *                 (request, head, chunk) items: they must be ALL ZERO before
+ *                 the first call, and every call that completes leaves them
+ *                 zero again, so one zero fill at allocation serves any number
+ *                 of later calls.  The rest (per-chunk partial results, when
+ *                 a (request, head) is split) may hold anything on entry.
+ *                 Calls that overlap in time must not share a workspace.
+ * Work split (bf16): one workgroup per CU (at most one per item) takes items
+ * in order of decreasing prefix length (batches of up to 64 requests; larger
+ * ones in request order), the first one by its grid index and every later one
+ * from one of eight counters, so a ragged batch does not end on a few long
+ * requests.
  * Errors: TV_EINVAL for N < 0, B < 0, H < 1, D not 64/128, block_size != 16,
  * max_blocks < 1, num_blocks < 1 or null pointers; TV_ETOOBIG for N > 64;
  * TV_EDTYPE; TV_EWORKSPACE.
@@ -153,9 +168,10 @@ tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
  * TV_REQ_BAD_BLOCK or TV_REQ_OK (a request that fails a check gets the later
  * call's treatment: zero output for a malformed tree or a prefix past the
  * table, unspecified output for a bad block id).  With bf16 and a chunk plan of
- * one chunk per (request, head) (tree_attn_verify_workspace gives 0) it is one
- * kernel: every workgroup derives its request's masks from parent; otherwise
- * the two kernels run one after the other.  N = 0 only builds the (empty) masks.
+ * one chunk per (request, head) (tree_attn_verify_workspace gives 1024, the
+ * item counters alone) it is one kernel: every item derives its request's
+ * masks from parent; otherwise the two kernels run one after the other.
+ * N = 0 only builds the (empty) masks.
  *
  *   parent        [B][N] int32 in; anc [B][N], child [B][N+1] uint64, depth
  *                 [B][N] int32 out, as tree_build_mask
@@ -191,12 +207,22 @@ tv_status tree_mask_attn_verify(tv_dtype dt, int B, int N, int H, int D, float s
  *                 allocation serves any number of later calls.  It holds the
  *                 counters and values the workgroups of one request exchange.
  *                 Calls that overlap in time must not share a workspace.
- * Work split: each request is walked by ceil(V / 2048) workgroups that must
- * all be resident at once; with more than one the launch is cooperative, in
- * batches of requests that fit the device.  Their waits are bounded: a wait
- * that runs out sets TV_REQ_TIMEOUT instead of hanging.
+ * Work split: up to V = 16384 one workgroup walks a request.  Above, each
+ * request is walked by ceil(V / 2048) workgroups that exchange values through
+ * the workspace and so must be resident at the same time.  They are started
+ * by ordinary launches in batches of requests sized so that every workgroup
+ * of a batch fits on the device at once (by the occupancy the device reports
+ * for the kernel); that residency is not guaranteed when other work occupies
+ * the device's compute units.  Every wait is bounded (2^22 polls, about 0.1 s,
+ * or TREEVERIFY_WALK_WAIT_POLLS from the environment): a wait that runs out
+ * sets TV_REQ_TIMEOUT for its request instead of hanging, every workgroup
+ * still leaves, and the workspace is still left zero.  Workgroup 0 of a
+ * request writes all of the request's outputs, so they always come from one
+ * decision: a request is either complete or timed out (no bonus from one
+ * workgroup beside a status from another).
  * Errors: TV_EINVAL (B, N < 0, V < 1 or V > 2^20, null pointers),
- * TV_ETOOBIG, TV_EWORKSPACE, TV_EHIP (the cooperative launch failed).
+ * TV_ETOOBIG, TV_EWORKSPACE, TV_EHIP (a launch failed, or the device's
+ * occupancy query did).
  */
 size_t tree_verify_workspace(int B, int N, int V);
 tv_status tree_verify_greedy(int B, int N, int V, const float* target_logits,

@@ -172,6 +172,47 @@ def test_attention_status_paths():
     assert run2.status.cpu().numpy()[2] == 7
 
 
+@pytest.mark.parametrize("B", [40, 70])
+@pytest.mark.parametrize("fused", [False, True])
+def test_attention_ragged_order(B, fused):
+    """Ragged prefixes: requests are dispatched longest first (ranked per
+    launch up to 64 requests, grid order above), with equal lengths, an empty
+    prefix, a request skipped upstream and one past the cache's capacity in
+    the batch; every (request, head) output is checked."""
+    _print_case("attention ragged order", B, "fused" if fused else "plain")
+    w = synth.make_workload(dict(name="ragged", B=B, H=2, D=128, V=50, dtype="bf16", tree=("expand", (2, 2, 1)),
+                                 L=("uniform", 0, 300), sig_t=1.0, sig_s=1.0), 91)
+    pl = w.prefix_len.copy()
+    pl[3] = pl[7] = pl[11] = pl[5]          # ties: rank by request index
+    pl[10] = 0
+    pl[12] = pl.max()
+    pl[20] = w.max_blocks * 16              # past the table: TV_REQ_KV_CAPACITY
+    w.prefix_len = pl
+    run = DeviceRun(w)
+    anc, _, _, st0 = o_tree.build_mask_batch(w.parent)
+    st_in = list(st0)
+    if fused:
+        run.mask_attn()
+    else:
+        run.mask()
+        run.status[2] = 1                   # skipped upstream
+        st_in[2] = 1
+        run.attn()
+    torch.cuda.synchronize()
+    ref, rst = o_attn.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len, anc, st_in,
+                                     w.dtype, w.scale)
+    assert list(run.status.cpu().numpy()) == rst
+    got = out_to_f64(run.out)
+    atol, rtol = TOL[w.dtype]
+    for b in range(B):
+        if rst[b] != 0:
+            if rst[b] == 1:
+                assert np.all(got[b] == 0)
+            continue
+        err = np.abs(got[b] - ref[b])
+        assert not (err > atol + rtol * np.abs(ref[b])).any(), (b, float(err.max()))
+
+
 # ----------------------------------------------------------------------------
 # greedy / MSS
 # ----------------------------------------------------------------------------
