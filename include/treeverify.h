@@ -129,20 +129,9 @@ tv_status tree_build_mask(int B, int N, const int32_t* parent, uint64_t* anc,
  *                 set at run time, so repeated calls agree to rounding, not bit
  *                 for bit
  *   workspace     ws_bytes >= tree_attn_verify_workspace(...) bytes of device
- *                 memory (may be null when that size is 0: fp32 with one
- *                 chunk per (request, head)).  For bf16 its first 1024 bytes
- *                 hold the counters from which the workgroups take their
- *                 (request, head, chunk) items: they must be ALL ZERO before
- *                 the first call, and every call that completes leaves them
- *                 zero again, so one zero fill at allocation serves any number
- *                 of later calls.  The rest (per-chunk partial results, when
- *                 a (request, head) is split) may hold anything on entry.
- *                 Calls that overlap in time must not share a workspace.
- * Work split (bf16): one workgroup per CU (at most one per item) takes items
- * in order of decreasing prefix length (batches of up to 64 requests; larger
- * ones in request order), the first one by its grid index and every later one
- * from one of eight counters, so a ragged batch does not end on a few long
- * requests.
+ *                 memory for per-chunk partial results (may be null when that
+ *                 size is 0); contents on entry do not matter.  Calls that
+ *                 overlap in time must not share a workspace.
  * Errors: TV_EINVAL for N < 0, B < 0, H < 1, D not 64/128, block_size != 16,
  * max_blocks < 1, num_blocks < 1 or null pointers; TV_ETOOBIG for N > 64;
  * TV_EDTYPE; TV_EWORKSPACE.
@@ -168,10 +157,9 @@ tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, float scale,
  * TV_REQ_BAD_BLOCK or TV_REQ_OK (a request that fails a check gets the later
  * call's treatment: zero output for a malformed tree or a prefix past the
  * table, unspecified output for a bad block id).  With bf16 and a chunk plan of
- * one chunk per (request, head) (tree_attn_verify_workspace gives 1024, the
- * item counters alone) it is one kernel: every item derives its request's
- * masks from parent; otherwise the two kernels run one after the other.
- * N = 0 only builds the (empty) masks.
+ * one chunk per (request, head) (tree_attn_verify_workspace gives 0) it is one
+ * kernel: every workgroup derives its request's masks from parent; otherwise
+ * the two kernels run one after the other.  N = 0 only builds the (empty) masks.
  *
  *   parent        [B][N] int32 in; anc [B][N], child [B][N+1] uint64, depth
  *                 [B][N] int32 out, as tree_build_mask

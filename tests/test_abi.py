@@ -70,9 +70,7 @@ def test_host_argument_checks(L):
     assert need > 0
     assert attn(mb=400, ws=None) == TV_EWORKSPACE
     assert attn(mb=400, ws=_p(), ws_bytes=need - 1) == TV_EWORKSPACE
-    assert L.tree_attn_verify_workspace(1, 2, 5, 2, 128, 4) == 1024  # one chunk (bf16): the item counters
-    assert L.tree_attn_verify_workspace(0, 2, 5, 2, 128, 4) == 0     # one chunk (fp32): nothing
-    assert attn(ws=None) == TV_EWORKSPACE                            # bf16 always needs the counter
+    assert L.tree_attn_verify_workspace(1, 2, 5, 2, 128, 4) == 0     # one chunk: no workspace
     del args
 
     def fused(dt=1, B=2, D=128, N=5, bs=16, ws=None, ws_bytes=0, mb=4, par=True, anc=True, ch=True, st=True):

@@ -93,8 +93,7 @@ def _oracle(run, pairs=None):
 
 def _kernels(w):
     code = tv.TV_BF16 if w.dtype == "bf16" else tv.TV_F32
-    # bf16 with one chunk per (request, head): the workspace is the item counters alone
-    one = w.dtype == "bf16" and tv.tree_attn_verify_workspace(code, w.B, w.N, w.H, w.D, w.max_blocks) <= 1024
+    one = w.dtype == "bf16" and tv.tree_attn_verify_workspace(code, w.B, w.N, w.H, w.D, w.max_blocks) == 0
     return "one kernel" if one else "two kernels"
 
 

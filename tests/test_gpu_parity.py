@@ -175,10 +175,10 @@ def test_attention_status_paths():
 @pytest.mark.parametrize("B", [40, 70])
 @pytest.mark.parametrize("fused", [False, True])
 def test_attention_ragged_order(B, fused):
-    """Ragged prefixes: requests are dispatched longest first (ranked per
-    launch up to 64 requests, grid order above), with equal lengths, an empty
-    prefix, a request skipped upstream and one past the cache's capacity in
-    the batch; every (request, head) output is checked."""
+    """Ragged prefixes in one batch (B on both sides of 64), with equal
+    lengths, an empty prefix, the longest prefix repeated, a request skipped
+    upstream and one past the cache's capacity; every (request, head) output
+    is checked."""
     _print_case("attention ragged order", B, "fused" if fused else "plain")
     w = synth.make_workload(dict(name="ragged", B=B, H=2, D=128, V=50, dtype="bf16", tree=("expand", (2, 2, 1)),
                                  L=("uniform", 0, 300), sig_t=1.0, sig_s=1.0), 91)

@@ -52,7 +52,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
 constexpr int kMaxSplits = 64;                      // chunks per (request, head)
-constexpr int kMaxChunkKeys = 16384;                // keys per chunk (bf16 path)
+constexpr int kMaxChunkKeys = 32768;                // keys per workgroup chunk (bf16 path)
 constexpr int kMaxChunkBlocks = kMaxChunkKeys / TV_BLOCK + 1;
 
 struct AttnArgs {
@@ -79,25 +79,6 @@ struct AttnArgs {
   int chunk;                 // keys per chunk (multiple of 128)
   int splits;                // S
   int npad;                  // queries padded to a multiple of 16
-  void* ctl;                 // bf16: the item counter (workspace head, 0 between calls)
-};
-
-// The pointers that only an item's setup and its results use (bf16 kernel):
-// a copy in LDS, written field by field (a copy of the whole argument block
-// would go through scratch memory).
-struct ItemPtrs {
-  const int32_t* block_table;
-  const int32_t* prefix_len;
-  const int32_t* parent;
-  const uint64_t* anc;
-  int32_t* status;
-  uint64_t* anc_out;
-  uint64_t* child_out;
-  int32_t* depth_out;
-  uint16_t* out;
-  float* part_o;
-  float* part_ml;
-  unsigned* ctl;
 };
 
 // Request-level checks done by every workgroup of request b.  Returns
@@ -114,8 +95,8 @@ __device__ __forceinline__ int request_gate(const AttnArgs& a, int b) {
 // A status written while other workgroups of the request run (in-kernel
 // masks): a device-scope store, so it reaches memory in the order it is made
 // rather than with its XCD's cache at the end of the kernel.
-__device__ __forceinline__ void store_status(int32_t* status, int b, int v) {
-  __hip_atomic_store(status + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_status(const AttnArgs& a, int b, int v) {
+  __hip_atomic_store(a.status + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T>
@@ -127,15 +108,12 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) { *p =
 
 // Zero the output rows of (b, h): used for requests that are skipped.
 template <typename T>
-__device__ void zero_out(T* out, int N, int H, int D, int b, int h) {
-  for (int e = threadIdx.x; e < N * D; e += blockDim.x) {
-    const int n = e / D, d = e - n * D;
-    store_out<T>(out + ((static_cast<size_t>(b) * N + n) * H + h) * D + d, 0.f);
-  }
-}
-template <typename T>
 __device__ void zero_out(const AttnArgs& a, int b, int h) {
-  zero_out<T>(static_cast<T*>(a.out), a.N, a.H, a.D, b, h);
+  T* out = static_cast<T*>(a.out);
+  for (int e = threadIdx.x; e < a.N * a.D; e += blockDim.x) {
+    const int n = e / a.D, d = e - n * a.D;
+    store_out<T>(out + ((static_cast<size_t>(b) * a.N + n) * a.H + h) * a.D + d, 0.f);
+  }
 }
 
 // Epilogue shared by both paths: the workgroup's combined (O, m, l) for
@@ -192,56 +170,35 @@ __device__ __forceinline__ int tile_off(int r, int c16) {   // byte offset
   return r * (2 * D) + swz<D>(r, c16) * 16;
 }
 
-// Persistent workgroups over (request b, head h, key chunk s) items, one
-// workgroup per CU, each made of kGroups groups of 4 waves.
-//
-// Items.  Item i is request rank i / (H S), head (i % (H S)) / S, chunk
-// i % S, where requests are ranked by prefix length, longest first (ties by
-// request index, so equal lengths keep request order; batches above kRankMax
-// requests keep request order).  Workgroup w starts with item w; every later
-// item is claimed from a counter in the workspace, so the items are taken in
-// order by whichever workgroup frees up first: a greedy list schedule,
-// longest first, which keeps a ragged batch from ending on a few long items.
-// The claim for the item after the current one goes out while the current
-// item is set up, and that item's request data (status, prefix length,
-// masks or parents, block ids) are fetched while the current item's groups
-// merge, so moving to the next item costs no round trip of its own and no
-// dispatch of a new workgroup.  The claim that runs past the last item
-// (every workgroup makes exactly one) and returns the last counter value
-// belongs to the last claimer: it stores 0 back, so the counter is 0 again
-// for the next call.
-//
-// Within an item, the chunk is cut into stages of 32 keys, which the groups
-// claim as they go (see the loop below); each group runs as if it were a
-// workgroup of its own: a two-buffer ring of K/V stages filled HBM -> LDS
-// with direct-to-LDS loads (no registers), one stage in flight while the
-// other is read, and its own barrier (an LDS counter), so the groups drift
-// independently and one group's loads overlap another's matrix work.  NQT
-// waves of a group each own one 16-query tile of the tree; every LDS read of
-// a stage is issued before its products, so the reads' latency hides behind
-// them.  Per 32 keys and query tile:
+// One workgroup per (request b, head h, key chunk s), made of kGroups groups of 4
+// waves.  The chunk is cut into stages of 32 keys, which the groups claim
+// as they go (see the loop below); each group runs as if it were a workgroup of its own: a
+// two-buffer ring of K/V stages filled HBM -> LDS with direct-to-LDS loads
+// (no registers), one stage in flight while the other is read, and its own
+// barrier (an LDS counter), so the groups drift independently and one
+// group's loads overlap another's matrix work.  NQT waves of a group each own
+// one 16-query tile of the tree; every LDS read of a stage is issued before
+// its products, so the reads' latency hides behind them.  Per 32 keys and
+// query tile:
 //   S^T[key][query] = K . Q^T     (A = K rows from LDS, B = Q^T in registers)
 //   O^T[dim][query] += V^T . P^T  (A = V^T via LDS transpose reads,
 //                                  B = P^T straight from the S^T accumulator)
-// At the end of an item the groups' softmax states are merged through LDS;
-// with several chunks per (b, h) the merged state is written as an
-// unnormalised partial that attn_merge_kernel combines.
+// At the end the groups' softmax states are merged through LDS; with several
+// chunks per (b, h) the merged state is written as an unnormalised partial
+// that attn_merge_kernel combines.
 constexpr int kGroups = 3;                  // 4-wave groups per workgroup
 constexpr int kRing = 2;                    // stage buffers per group
 constexpr int kGroupThreads = 256;
 constexpr int kAttnThreads = kGroups * kGroupThreads;
 constexpr unsigned kGroupSpinLimit = 1u << 26;
-constexpr int kRankMax = 64;                // requests ranked by length (one per lane)
-constexpr int kQueues = 8;                  // item queues (counters in the workspace head)
-constexpr int kQueueStride = 32;            // 128 bytes between two counters
 
 // MASK: the kernel also builds the request's tree masks (one chunk per
-// (request, head) only).  Every item of request b reads the parents and
+// (request, head) only).  Every workgroup of request b reads the parents and
 // derives the ancestor masks of its query rows, the tree's validity and the
-// request's status from its own loads; item (b, 0, 0) alone writes the
+// request's status from its own loads; workgroup (b, 0, 0) alone writes the
 // status (device-scope stores) and the mask outputs of tree_build_mask, so no
-// two items write the same word, except a timeout (which comes only after
-// a group's spin limit, long after the first item's setup).
+// two workgroups write the same word, except a timeout (which comes only after
+// a workgroup's spin limit, long after the first workgroup's setup).
 template <int D, int NQT, bool MASK>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KC = D / 32;               // contraction steps over D
@@ -255,10 +212,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   static_assert((kGroups - 1) * NQT * SLOT * 4 <= kGroups * kRing * 2 * TILE, "merge area");
   static_assert(kRing >= 2 && kRing <= 4, "ring depth");
 
-  // (the wave index is made scalar, so the group's LDS addresses and the
-  // load indices derived from it are scalar values)
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = wave >> 2, gw = wave & 3;          // group, wave within the group
   const int lr = lane & 15, lg = lane >> 4;
 
@@ -270,44 +225,37 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   static_assert(QBYTES % 1024 == 0, "Q copy in whole wave loads");
   __shared__ __attribute__((aligned(16))) uint8_t sq[kGroups * QBYTES];
   __shared__ int s_hung;
-  __shared__ int s_wflag[2][kAttnThreads / 64];   // per item parity, per wave: 1 = request skipped, 2 = bad block id
-  __shared__ int s_claim[2];                // per item parity: the item after it
+  __shared__ int s_wflag[kAttnThreads / 64];      // per wave: 1 = request skipped, 2 = bad block id
   __shared__ int s_gbar[kGroups];
   __shared__ int s_next;                    // next stage of the chunk not yet claimed
   __shared__ int s_sel[kGroups][2];         // stage a group's wave 0 claimed for the group
-  // request data of the current item and of the next one (by item parity):
-  // block ids of the chunk, status and prefix length, and the parents (MASK)
-  // or ancestor masks, filled by direct-to-LDS loads
-  __shared__ int s_blk[2][kMaxChunkBlocks];
-  __shared__ int s_meta[2][2];              // status (non-MASK), prefix length
-  __shared__ int s_par[2][TV_MAX_NODES];    // MASK: parent of each node
-  __shared__ __attribute__((aligned(8))) uint64_t s_anc[2][TV_MAX_NODES];   // ancestor masks
-  __shared__ unsigned long long s_childw[TV_MAX_NODES + 1];   // MASK: child words of the item's tree
-  __shared__ int s_rank[kRankMax];          // rank of each request by prefix length
-  // The pointers that only an item's setup and its results use are read
-  // from a copy in LDS: kernel arguments are invariant, so the compiler would
-  // otherwise keep every one of them in scalar registers across the stage
-  // loop, and that loop needs those registers.
-  __shared__ ItemPtrs s_a;
+  __shared__ int s_blk[kMaxChunkBlocks];
 
+  // Every load that depends on nothing goes out first, in every thread:
+  // the request's status and prefix length (same address in all threads),
+  // this wave's Q tile and ancestor masks, and the chunk's block ids.  The
+  // prefix length is not written during the launch, so every thread sees
+  // the same value; the status can be (another workgroup of the request may
+  // flag a bad block), so the workgroup agrees on it at a barrier below.
+  // Status and prefix length are read with vector loads (the request index
+  // is moved to a vector register first): as scalar loads of a uniform
+  // address the compiler issues them where they are first used, after the
+  // wait below, and every workgroup would start with two more dependent
+  // trips to memory.
   // The kernel arguments the start reads are fetched in one batch of scalar
   // loads (otherwise a second batch waits on the first).
   if constexpr (MASK)
     asm volatile("" :: "s"(a.q), "s"(a.kc), "s"(a.vc), "s"(a.block_table), "s"(a.prefix_len), "s"(a.parent),
-                 "s"(a.ctl), "s"(a.B), "s"(a.N), "s"(a.H), "s"(a.num_blocks), "s"(a.max_blocks), "s"(a.chunk),
-                 "s"(a.splits));
+                 "s"(a.N), "s"(a.H), "s"(a.num_blocks), "s"(a.max_blocks), "s"(a.chunk));
   else
     asm volatile("" :: "s"(a.q), "s"(a.kc), "s"(a.vc), "s"(a.block_table), "s"(a.prefix_len), "s"(a.anc),
-                 "s"(a.status), "s"(a.ctl), "s"(a.B), "s"(a.N), "s"(a.H), "s"(a.num_blocks), "s"(a.max_blocks),
-                 "s"(a.chunk), "s"(a.splits));
+                 "s"(a.status), "s"(a.N), "s"(a.H), "s"(a.num_blocks), "s"(a.max_blocks), "s"(a.chunk));
   const int N = a.N;
-  const int HS = a.H * a.splits;            // items per request
-  const int n_items = a.B * HS;
+  int b_v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(b_v) : "s"(b));
+  const int st_v = MASK ? TV_REQ_OK : a.status[b_v];
+  const int L_v = a.prefix_len[b_v];
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
-  const uint8_t* __restrict__ kg = static_cast<const uint8_t*>(a.kc);
-  const uint8_t* __restrict__ vg = static_cast<const uint8_t*>(a.vc);
-  const size_t head_bytes = static_cast<size_t>(TV_BLOCK) * D * 2;
-  const size_t blk_bytes = static_cast<size_t>(a.H) * head_bytes;
   // Query tile of this wave.  Wave gw of a group runs on SIMD gw, so the
   // tile index is rotated by the group: with fewer tiles than waves, the
   // idle waves of different groups sit on different SIMDs and every SIMD
@@ -316,154 +264,115 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   const bool computes = qt < NQT;
   const int n_q = 16 * qt + lr;
   bf16x8 qv[KC];            // this wave's Q tile: read from the group's copy at its first stage
-  const int nblk_cap = a.chunk / TV_BLOCK + 1;     // <= kMaxChunkBlocks
+  uint64_t ancq = 0;
+  int par = -2;             // MASK: parent of node `lane` (every wave builds the masks)
+  if constexpr (MASK) {
+    if (lane < N) par = a.parent[static_cast<size_t>(b) * N + lane];
+  } else {
+    if (computes && n_q < N) ancq = a.anc[static_cast<size_t>(b) * N + n_q];
+  }
+  // Block ids of every block the chunk can cover, before the prefix length
+  // is known (the table index is clamped to the table).  Ids outside
+  // [0, num_blocks) are stored as 0, so every K/V load stays in bounds; the
+  // ones that matter (blocks covering the chunk's keys) are reported below.
+  const int32_t* __restrict__ bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  const int k_begin = s * a.chunk;          // < max_blocks * 16 (the plan's last chunk starts inside)
+  const int blk_first = k_begin / TV_BLOCK;
+  const int nblk_max = min(a.chunk / TV_BLOCK + 1, a.max_blocks - blk_first);   // <= kMaxChunkBlocks
   constexpr int kPer = (kMaxChunkBlocks + kAttnThreads - 1) / kAttnThreads;
-
-  // ---- request data of an item, fetched into LDS (no registers, no wait) ----
-  // The request's status and prefix length, its parents (MASK) or ancestor
-  // masks, and the block ids of every block the chunk can cover, before the
-  // prefix length is known (the table index is clamped to the table; ids
-  // outside [0, num_blocks) are replaced by 0 when the item is set up, so
-  // every K/V load stays in bounds, and the ones that matter are reported).
-  // The loads go HBM -> LDS directly (lane i's dword lands at M0 + 4 i), so
-  // the next item's data can be requested at the start of the current item
-  // and have its whole stream time to land.  The prefix length is not written
-  // during the launch; the status can be (another item of the request may
-  // flag a bad block), so the workgroup agrees on it at a barrier.
-  // Values derived from the thread index that only the item switch uses are
-  // derived from an opaque copy of it, taken where they are used: otherwise
-  // the compiler computes them once, before the item loop, and keeps them in
-  // registers across every stage loop, which needs those registers.
-  auto opaque_tid = []() {
-    int t = static_cast<int>(threadIdx.x);
-    asm volatile("" : "+v"(t));
-    return t;
-  };
-  auto lds_dword = [](const void* src, const void* lds_base) {
-    // (the LDS offset is taken through an LDS-typed pointer, not a generic one)
-    const auto lp = (__attribute__((address_space(3))) const void*)lds_base;
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lp)));
-    asm volatile("global_load_lds_dword %0, off" :: "v"(src), "{m0}"(m0) : "memory");
-  };
-  auto fetch_item = [&](const ItemPtrs& aa, int rb, int rs, int buf) {   // request rb, chunk rs
-    const int ln = opaque_tid() & 63;
-    const int bf = rs * a.chunk / TV_BLOCK;
-    const int nbm = min(nblk_cap, a.max_blocks - bf);
-    const int32_t* bt = aa.block_table + static_cast<size_t>(rb) * a.max_blocks + bf;
-    for (int j = wave; 64 * j < nbm; j += kAttnThreads / 64)
-      if (64 * j + ln < nbm) lds_dword(bt + 64 * j + ln, &s_blk[buf][64 * j]);
-    if (wave == 0 && ln < 2) {
-      const int32_t* src = ln == 1 ? aa.prefix_len + rb : (MASK ? aa.prefix_len + rb : aa.status + rb);
-      lds_dword(src, &s_meta[buf][0]);
-    }
-    if constexpr (MASK) {
-      if (wave == 1 && ln < N) lds_dword(aa.parent + static_cast<size_t>(rb) * N + ln, &s_par[buf][0]);
-    } else {
-      if (wave == 1 || wave == 2) {
-        const int d = 64 * (wave - 1) + ln;             // dword of the request's masks
-        if ((d >> 1) < N)
-          lds_dword(reinterpret_cast<const uint32_t*>(aa.anc + static_cast<size_t>(rb) * N) + d,
-                    reinterpret_cast<const uint32_t*>(&s_anc[buf][0]) + 64 * (wave - 1));
+  int raw[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kAttnThreads;
+    raw[r] = i < nblk_max ? bt[blk_first + i] : 0;
+  }
+  // A wait the compiler can see: every load above is complete from here on,
+  // so it adds no wait of its own inside the stage loop, where a wait would
+  // also drain the stage loads in flight, which it does not know about.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
+  const int L = __builtin_amdgcn_readfirstlane(L_v);
+  const bool first_wg = h == 0 && s == 0;
+  int st;
+  if constexpr (MASK) {
+    uint64_t anc_l;
+    int dep_l;
+    const bool bad_tree = tv::wave_tree_masks(N, par, anc_l, dep_l);
+    st = bad_tree ? TV_REQ_BAD_PARENT : TV_REQ_OK;
+    const int src = n_q & 63;
+    const uint32_t lo = __shfl(static_cast<uint32_t>(anc_l), src, 64);
+    const uint32_t hi = __shfl(static_cast<uint32_t>(anc_l >> 32), src, 64);
+    ancq = (computes && n_q < N) ? (static_cast<uint64_t>(hi) << 32 | lo) : 0ull;
+    if (first_wg && wave == 0) {
+      if (lane < N) {
+        a.anc_out[static_cast<size_t>(b) * N + lane] = anc_l;
+        a.depth_out[static_cast<size_t>(b) * N + lane] = dep_l;
       }
+      // (the ring is not written before the barrier below)
+      tv::wave_child_masks(N, par, bad_tree, reinterpret_cast<unsigned long long*>(ring),
+                           a.child_out + static_cast<size_t>(b) * (N + 1));
     }
-  };
-  // A wait the compiler can see: every load issued so far is complete, so it
-  // adds no wait of its own inside the stage loop, where a wait would also
-  // drain the stage loads in flight, which it does not know about.
-  auto wait_all = [&]() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); };    // vmcnt(0)
-
-  // ---- the request order (every wave ranks the lengths itself) ----
-  const bool ranked = a.B > 1 && a.B <= kRankMax;
-  int len_l = INT_MIN;
-  if (ranked && lane < a.B) len_l = a.prefix_len[lane];
-  // the ranks stay in LDS between items (s_rank[lane]: rank of request lane)
-  auto request_of = [&](int r) -> int {     // request of rank r (wave-uniform)
-    if (!ranked) return r;
-    const int ln = opaque_tid() & 63;
-    const uint64_t hit = __ballot(ln < a.B && s_rank[ln] == r);
-    return hit ? __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit))) : r;
-  };
-  // Item queues.  Items are dealt to kQueues queues by index (item i to
-  // queue i % kQueues) and workgroup w serves queue w % kQueues, taking its
-  // first item, w, statically and the queue's later items in order from the
-  // queue's counter.  Device-scope atomics on one address serialise, so
-  // eight counters (one per XCD of the usual dispatch) keep the claims of a
-  // round of items that end together from queueing behind one another.
-  // With no more items than workgroups nothing is claimed.
-  const int n_wg = static_cast<int>(gridDim.x);
-  const bool dyn = n_items > n_wg;
-  const int qx = static_cast<int>(blockIdx.x) % kQueues;            // this workgroup's queue
-  const int q_wgs = (n_wg - qx + kQueues - 1) / kQueues;            // workgroups serving it
-  const int q_items = (n_items - qx + kQueues - 1) / kQueues;       // items dealt to it
-  auto claim = [&](const ItemPtrs& aa) -> unsigned {          // thread 0 only
-    return __hip_atomic_fetch_add(aa.ctl + kQueueStride * qx, 1u, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-  };
-  // thread 0: publish the claimed item.  A queue sees q_items claims in all
-  // (one that runs past its items per workgroup); the one that returns the
-  // last value stores 0 back.
-  auto settle_claim = [&](const ItemPtrs& aa, unsigned c, int parity) {
-    if (!dyn) {
-      s_claim[parity] = n_items;
-      return;
-    }
-    if (c == static_cast<unsigned>(q_items - 1))
-      __hip_atomic_store(aa.ctl + kQueueStride * qx, 0u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    const long nx = qx + static_cast<long>(kQueues) * (q_wgs + static_cast<long>(c));
-    s_claim[parity] = static_cast<int>(min(nx, static_cast<long>(n_items)));
-  };
-
-  // ---- first item: blockIdx.x, fetched for request order before the
-  // ranking is known (they agree when the lengths do) ----
-  const ItemPtrs pa{a.block_table, a.prefix_len, a.parent, a.anc, a.status, a.anc_out, a.child_out, a.depth_out,
-                    static_cast<uint16_t*>(a.out), a.part_o, a.part_ml, static_cast<unsigned*>(a.ctl)};
-  int item = blockIdx.x;
-  int b = item / HS;
-  fetch_item(pa, b, item % a.splits, 0);
-  unsigned claim_v = 0;
-  if (threadIdx.x == 0) {
-    if (dyn) claim_v = claim(pa);
-    // (read after the first barrier, or by wave 0 itself)
-    s_a.block_table = pa.block_table;
-    s_a.prefix_len = pa.prefix_len;
-    s_a.parent = pa.parent;
-    s_a.anc = pa.anc;
-    s_a.status = pa.status;
-    s_a.anc_out = pa.anc_out;
-    s_a.child_out = pa.child_out;
-    s_a.depth_out = pa.depth_out;
-    s_a.out = pa.out;
-    s_a.part_o = pa.part_o;
-    s_a.part_ml = pa.part_ml;
-    s_a.ctl = pa.ctl;
+  } else {
+    st = __builtin_amdgcn_readfirstlane(st_v);
   }
-  wait_all();
-  if (ranked) {
-    int rank_l = 0;
-    for (int j = 0; j < a.B; ++j) {
-      const int lj = __builtin_amdgcn_readlane(len_l, j);
-      rank_l += (lj > len_l) | ((lj == len_l) & (j < lane));
-    }
-    if (wave == 0) s_rank[lane] = rank_l;   // (read after the first barrier; every wave has its own copy here)
-    const uint64_t hit0 = __ballot(lane < a.B && rank_l == item / HS);
-    const int rb = hit0 ? __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit0))) : item / HS;
-    if (rb != b) {                           // (the same branch in every wave)
-      b = rb;
-      fetch_item(pa, b, item % a.splits, 0);
-      wait_all();
-    }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kAttnThreads;
+    if (i < nblk_max) s_blk[i] = (raw[r] < 0 || raw[r] >= a.num_blocks) ? 0 : raw[r];
   }
-  if (threadIdx.x == 0) settle_claim(pa, claim_v, 0);
+  if (L < 0 || static_cast<int64_t>(L) + N > static_cast<int64_t>(a.max_blocks) * TV_BLOCK) {
+    // no workgroup of this request gets further, so no bad-block flag can race this
+    if constexpr (MASK) {
+      if (first_wg && threadIdx.x == 0) store_status(a, b, st != TV_REQ_OK ? st : TV_REQ_KV_CAPACITY);
+    } else {
+      if (threadIdx.x == 0 && st == TV_REQ_OK) a.status[b] = TV_REQ_KV_CAPACITY;
+    }
+    if (s == 0) zero_out<uint16_t>(a, b, h);
+    return;
+  }
+  const int T = L + N;
+  if (k_begin >= T) return;                 // empty chunk (never chunk 0): not counted by the merge
+  const int k_end = min(T, k_begin + a.chunk);
+  const int nst = (k_end - k_begin + SK - 1) / SK;                // stages of the chunk
+  const int nblk = (k_end - 1) / TV_BLOCK - blk_first + 1;        // blocks covering the chunk's keys
+
+  const uint8_t* __restrict__ kg = static_cast<const uint8_t*>(a.kc);
+  const uint8_t* __restrict__ vg = static_cast<const uint8_t*>(a.vc);
+  const size_t head_bytes = static_cast<size_t>(TV_BLOCK) * D * 2;
+  const size_t blk_bytes = static_cast<size_t>(a.H) * head_bytes;
+  const int last_blk = (T - 1) / TV_BLOCK, last_row = (T - 1) % TV_BLOCK;
+
+  int bad = 0;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kAttnThreads;
+    if (i < nblk && (raw[r] < 0 || raw[r] >= a.num_blocks)) bad = 1;
+  }
   if (threadIdx.x < kGroups) s_gbar[threadIdx.x] = 0;
-  int phase = 0;            // group barriers passed by this wave (the count only grows)
-  __syncthreads();          // the first item's data, the ranks and the pointer table are visible
+  if (threadIdx.x < 2 * kGroups) s_sel[threadIdx.x >> 1][threadIdx.x & 1] = INT_MAX;
+  if (threadIdx.x == 0) {
+    s_hung = 0;
+    s_next = kGroups * kRing;               // the ones before are handed out statically below
+  }
+  // The workgroup agrees on the status (another workgroup of the request
+  // may flag a bad block meanwhile) and on the bad-block flag with one
+  // barrier: each wave leaves its flags in a slot of its own.
+  const bool wave_bad = __any(bad);          // (voted by the whole wave)
+  if (lane == 0) s_wflag[wave] = (st != TV_REQ_OK ? 1 : 0) | (wave_bad ? 2 : 0);
+  __syncthreads();
+  int wflags = 0;
+#pragma unroll
+  for (int w = 0; w < kAttnThreads / 64; ++w) wflags |= s_wflag[w];
+  if (wflags & 1) {                          // a skipped request: zero output
+    if (MASK && first_wg && threadIdx.x == 0) store_status(a, b, st);
+    if (s == 0) zero_out<uint16_t>(a, b, h);
+    return;
+  }
+  const int badblk = wflags & 2;
+  // (MASK: one chunk, so this chunk's blocks are all the request's blocks)
+  if (MASK && first_wg && threadIdx.x == 0) store_status(a, b, badblk ? TV_REQ_BAD_BLOCK : TV_REQ_OK);
 
-  // per-item values the lambdas below read
-  int h = 0, s = 0, L = 0, T = 0, k_begin = 0, blk_first = 0, last_blk = 0, last_row = 0, cur = 0;
-  uint64_t ancq = 0;        // ancestor mask of this lane's query row
-  uint8_t* const gring = ring + grp * kRing * 2 * TILE;   // this group's stage buffers
-  uint8_t* const gq = sq + grp * QBYTES;                   // this group's Q copy
+  uint8_t* gring = ring + grp * kRing * 2 * TILE;   // this group's stage buffers
+  uint8_t* gq = sq + grp * QBYTES;                   // this group's Q copy
 
   // The group's Q copy goes HBM -> LDS by direct-to-LDS loads issued just
   // before the group's first stages, so Q is not waited for at the start: a
@@ -472,9 +381,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   // N - 1 (the tile reads zero them).
   auto issue_q = [&]() {
     constexpr int RPL = 1024 / (2 * D);            // rows per 1 KB wave load
-    const int ln = opaque_tid() & 63;              // (lane offsets formed here, not kept across items)
     for (int li = gw; li < QBYTES / 1024; li += 4) {
-      const int row = li * RPL + ln / CPR, phys = ln % CPR;
+      const int row = li * RPL + lane / CPR, phys = lane % CPR;
       const int n = min(row, N - 1);
       const uint8_t* src = reinterpret_cast<const uint8_t*>(qg + ((static_cast<size_t>(b) * N + n) * a.H + h) * D) +
                            swz<D>(row, phys) * 16;
@@ -489,7 +397,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   // LDS directly; they are issued and awaited by hand (see below).
   auto issue = [&](int st, uint8_t* dst) {
     const int t0 = k_begin + SK * st;
-    const int ln = opaque_tid() & 63;              // (lane offsets formed here, not kept across items)
 #pragma unroll
     for (int r = 0; r < LPW; ++r) {
       const int li = gw * LPW + r;                   // 1 KB load index within the stage
@@ -499,8 +406,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       int blk_i = (t0 + key0) / TV_BLOCK;
       const bool past_blk = blk_i > last_blk;
       if (past_blk) blk_i = last_blk;
-      const int blk = __builtin_amdgcn_readfirstlane(s_blk[cur][blk_i - blk_first]);
-      const int p = lt * 64 + ln;                    // 16-byte slot within the tile
+      const int blk = __builtin_amdgcn_readfirstlane(s_blk[blk_i - blk_first]);
+      const int p = lt * 64 + lane;                  // 16-byte slot within the tile
       const int key = p / CPR, phys = p % CPR;
       const int c16 = swz<D>(key, phys);             // XOR swizzle is its own inverse
       int row = (t0 + key) % TV_BLOCK;
@@ -515,6 +422,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
 
   f32x4 o[DT];
   float mrun = -INFINITY, lrun = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int st, const uint8_t* cur) {
     const int t0 = k_begin + SK * st;
@@ -617,17 +526,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]), pb, o[dt], 0, 0, 0);
   };
 
-
   // ---- the group's pipeline: kRing stage buffers, kRing - 1 stages in flight ----
   // Group barrier: the 4 waves of the group count into an LDS word; a wave
-  // leaves once all 4 have arrived at this barrier (the count only grows,
-  // across items too).  A wave arrives only after its LDS reads and its
-  // stage loads it waited for are complete, so a stage is read only after
-  // all its loads landed and refilled only after every wave of the group has
-  // read it.  The waits are explicit (the atomics are relaxed:
-  // acquire/release would also drain the loads of the stage in flight); the
-  // asm statements keep the compiler from moving LDS accesses across the
-  // barrier.
+  // leaves once all 4 have arrived at this barrier (the count only grows).
+  // A wave arrives only after its LDS reads and its stage loads it waited
+  // for are complete, so a stage is read only after all its loads landed
+  // and refilled only after every wave of the group has read it.  The
+  // waits are explicit (the atomics are relaxed: acquire/release would also
+  // drain the loads of the stage in flight); the asm statements keep the
+  // compiler from moving LDS accesses across the barrier.
+  int phase = 0;
   auto group_barrier = [&]() {
     ++phase;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -655,263 +563,139 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
+  // Stages are handed to the groups at run time.  Group g starts with
+  // stages g, g + kGroups, ... (one per ring buffer, all loading now); after
+  // that, whenever a buffer frees up, the group claims the next unclaimed
+  // stage of the chunk from an LDS counter.  A group whose loads land late
+  // thus takes fewer stages, and the groups finish close together (with a
+  // fixed share, the group that started last decides when the workgroup
+  // ends).  Wave 0 of the group claims just before it arrives at the
+  // barrier and leaves the index in s_sel; the other waves read it after
+  // the barrier.  held[0] is the stage being computed, held[1..] the ones in
+  // flight; claims only grow, so once held[0] is past the chunk every later
+  // one is too.
+  //
+  // In the loop, one barrier per stage: after it, the stage's loads have
+  // landed for every wave, and every wave has finished reading the buffer
+  // of the stage before, which is then refilled with the newly claimed
+  // stage, in flight during this stage's compute.
+  int held[kRing];
+  issue_q();
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) {
+    held[r] = grp + kGroups * r;
+    if (held[r] < nst) issue(held[r], gring + r * 2 * TILE);
+  }
+  for (int it = 0;; ++it) {
+    if (held[0] >= nst) break;
+    // in flight: held[1 .. kRing - 1] at it = 0, held[1 .. kRing - 2] after
+    // (the last buffer is refilled after this iteration's barrier)
+    int later = 0;
+#pragma unroll
+    for (int r = 1; r < kRing; ++r)
+      if ((it == 0 || r < kRing - 1) && held[r] < nst) ++later;
+    wait_stage(later);
+    if (it >= 1 && gw == 0 && lane == 0)
+      s_sel[grp][it & 1] = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    group_barrier();
+    if (it >= 1) {
+      const int nx = s_sel[grp][it & 1];
+      held[kRing - 1] = nx;
+      if (nx >= 0 && nx < nst) issue(nx, gring + ((it + kRing - 1) % kRing) * 2 * TILE);
+    }
+    if (it == 0 && computes) {
+      // the group's Q copy has landed (its loads precede this stage's)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        qv[c] = n_q < N ? as_bf16x8(*reinterpret_cast<const uint4*>(gq + tile_off<D>(n_q, 4 * c + lg)))
+                        : as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+    if (computes) compute(held[0], gring + (it % kRing) * 2 * TILE);
+#pragma unroll
+    for (int r = 0; r + 1 < kRing; ++r) held[r] = held[r + 1];
+    held[kRing - 1] = INT_MAX;                // claimed at the next iteration
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lrun += __shfl_xor(lrun, 16, 64);
+  lrun += __shfl_xor(lrun, 32, 64);
+  __syncthreads();
 
-  for (;; cur ^= 1) {
-    // ---------------- set up the item from its request data ----------------
-    // (LDS buffer cur holds it: fetched at the start of the previous item, or
-    // in the start-up above; the barrier that ended the previous item made
-    // every wave's loads visible)
-    b = request_of(item / HS);
-    h = (item % HS) / a.splits;
-    s = item % a.splits;
-    L = __builtin_amdgcn_readfirstlane(s_meta[cur][1]);
-    k_begin = s * a.chunk;                  // < max_blocks * 16 (the plan's last chunk starts inside)
-    blk_first = k_begin / TV_BLOCK;
-    const int nblk_max = min(nblk_cap, a.max_blocks - blk_first);
-    const bool first_item = h == 0 && s == 0;
-    int st;
-    if constexpr (MASK) {
-      const int par = lane < N ? s_par[cur][lane] : -2;
-      uint64_t anc_l;
-      int dep_l;
-      const bool bad_tree = tv::wave_tree_masks(N, par, anc_l, dep_l);
-      st = bad_tree ? TV_REQ_BAD_PARENT : TV_REQ_OK;
-      const int src = n_q & 63;
-      const uint32_t lo = __shfl(static_cast<uint32_t>(anc_l), src, 64);
-      const uint32_t hi = __shfl(static_cast<uint32_t>(anc_l >> 32), src, 64);
-      ancq = (computes && n_q < N) ? (static_cast<uint64_t>(hi) << 32 | lo) : 0ull;
-      if (first_item && wave == 0) {
-        if (lane < N) {
-          s_a.anc_out[static_cast<size_t>(b) * N + lane] = anc_l;
-          s_a.depth_out[static_cast<size_t>(b) * N + lane] = dep_l;
-        }
-        tv::wave_child_masks(N, par, bad_tree, s_childw, s_a.child_out + static_cast<size_t>(b) * (N + 1));
-      }
-    } else {
-      st = __builtin_amdgcn_readfirstlane(s_meta[cur][0]);
-      ancq = (computes && n_q < N) ? s_anc[cur][n_q] : 0ull;
-    }
-    const bool cap_bad = L < 0 || static_cast<int64_t>(L) + N > static_cast<int64_t>(a.max_blocks) * TV_BLOCK;
-    T = L + N;
-    const bool empty = !cap_bad && k_begin >= T;          // (never chunk 0): not counted by the merge
-    const int k_end = min(T, k_begin + a.chunk);
-    const int nst = (empty || cap_bad) ? 0 : (k_end - k_begin + SK - 1) / SK;   // stages of the chunk
-    const int nblk = nst ? (k_end - 1) / TV_BLOCK - blk_first + 1 : 0;          // blocks covering its keys
-    last_blk = (T - 1) / TV_BLOCK;
-    last_row = (T - 1) % TV_BLOCK;
-    // block ids outside [0, num_blocks) become 0 (every load stays in
-    // bounds); one among the blocks the chunk covers is reported
-    int bad = 0;
-    const int tid_s = opaque_tid();
+  // ---- merge the groups' states through LDS (the ring is free now) ----
+  // Slot layout [group - 1][query tile][DT*4 + 2][lane] floats: each lane
+  // writes and reads only its own column, so there are no bank conflicts.
+  float* mg = reinterpret_cast<float*>(ring);
+  if (grp > 0 && computes) {
+    float* dst = mg + ((grp - 1) * NQT + qt) * SLOT + lane;
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int i = tid_s + r * kAttnThreads;
-      if (i < nblk_max) {
-        const int id = s_blk[cur][i];
-        if (id < 0 || id >= a.num_blocks) {
-          s_blk[cur][i] = 0;
-          if (i < nblk) bad = 1;
-        }
-      }
-    }
-    if (threadIdx.x < 2 * kGroups) s_sel[threadIdx.x >> 1][threadIdx.x & 1] = INT_MAX;
-    if (threadIdx.x == 0) {
-      s_hung = 0;
-      s_next = kGroups * kRing;               // the ones before are handed out statically below
-    }
-    // The workgroup agrees on the status (another item of the request may
-    // flag a bad block meanwhile) and on the bad-block flag with one
-    // barrier: each wave leaves its flags in a slot of its own (one set of
-    // slots per item parity, so a wave already at the next item cannot
-    // overwrite flags another wave still reads).  The barrier also publishes
-    // the claimed next item.
-    const bool wave_bad = __any(bad);          // (voted by the whole wave)
-    if (lane == 0) s_wflag[cur][wave] = (st != TV_REQ_OK ? 1 : 0) | (wave_bad ? 2 : 0);
-    __syncthreads();
-    int wflags = 0;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int w = 0; w < kAttnThreads / 64; ++w) wflags |= s_wflag[cur][w];
-    const int badblk = wflags & 2;
-    // ---- the next item: its request data go to the other buffer now ----
-    const int nxt = s_claim[cur];            // (rewritten only after the next item's barrier)
-    const bool more = nxt < n_items;
-    if (more) fetch_item(s_a, request_of(nxt / HS), nxt % a.splits, cur ^ 1);
-    bool run = false;
-    if (cap_bad) {
-      // every item of this request gets here, so no bad-block flag can race this
-      if constexpr (MASK) {
-        if (first_item && threadIdx.x == 0) store_status(s_a.status, b, st != TV_REQ_OK ? st : TV_REQ_KV_CAPACITY);
-      } else {
-        if (threadIdx.x == 0 && st == TV_REQ_OK) s_a.status[b] = TV_REQ_KV_CAPACITY;
-      }
-      if (s == 0) zero_out<uint16_t>(s_a.out, N, a.H, D, b, h);
-    } else if (empty) {
-    } else if (wflags & 1) {                 // a skipped request: zero output
-      if (MASK && first_item && threadIdx.x == 0) store_status(s_a.status, b, st);
-      if (s == 0) zero_out<uint16_t>(s_a.out, N, a.H, D, b, h);
-    } else {
-      run = true;
-      // (MASK: one chunk, so this chunk's blocks are all the request's blocks)
-      if (MASK && first_item && threadIdx.x == 0) store_status(s_a.status, b, badblk ? TV_REQ_BAD_BLOCK : TV_REQ_OK);
-    }
-
-    if (run) {
+      for (int i = 0; i < 4; ++i) dst[(dt * 4 + i) * 64] = o[dt][i];
+    dst[(DT * 4) * 64] = mrun;
+    dst[(DT * 4 + 1) * 64] = lrun;
+  }
+  __syncthreads();
+  if (!MASK && badblk && threadIdx.x == 0) a.status[b] = TV_REQ_BAD_BLOCK;
+  if (s_hung && threadIdx.x == 0) {
+    if (MASK) store_status(a, b, TV_REQ_TIMEOUT);
+    else a.status[b] = TV_REQ_TIMEOUT;
+  }
+  if (grp != 0 || !computes) return;
+  float mo[kGroups], lo_[kGroups];
+  mo[0] = mrun;
+  lo_[0] = lrun;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mrun = -INFINITY;
-      lrun = 0.f;
-      // Stages are handed to the groups at run time.  Group g starts with
-      // stages g, g + kGroups, ... (one per ring buffer, all loading now);
-      // after that, whenever a buffer frees up, the group claims the next
-      // unclaimed stage of the chunk from an LDS counter.  A group whose
-      // loads land late thus takes fewer stages, and the groups finish close
-      // together (with a fixed share, the group that started last decides
-      // when the item ends).  Wave 0 of the group claims just before it
-      // arrives at the barrier and leaves the index in s_sel; the other waves
-      // read it after the barrier.  held[0] is the stage being computed,
-      // held[1..] the ones in flight; claims only grow, so once held[0] is
-      // past the chunk every later one is too.
-      //
-      // In the loop, one barrier per stage: after it, the stage's loads have
-      // landed for every wave, and every wave has finished reading the
-      // buffer of the stage before, which is then refilled with the newly
-      // claimed stage, in flight during this stage's compute.
-      int held[kRing];
-      issue_q();
+  for (int g2 = 1; g2 < kGroups; ++g2) {
+    const float* src = mg + ((g2 - 1) * NQT + qt) * SLOT + lane;
+    mo[g2] = src[(DT * 4) * 64];
+    lo_[g2] = src[(DT * 4 + 1) * 64];
+  }
+  float M = mo[0];
 #pragma unroll
-      for (int r = 0; r < kRing; ++r) {
-        held[r] = grp + kGroups * r;
-        if (held[r] < nst) issue(held[r], gring + r * 2 * TILE);
-      }
-      for (int it = 0;; ++it) {
-        if (held[0] >= nst) break;
-        // in flight: held[1 .. kRing - 1] at it = 0, held[1 .. kRing - 2] after
-        // (the last buffer is refilled after this iteration's barrier)
-        int later = 0;
+  for (int g2 = 1; g2 < kGroups; ++g2) M = fmaxf(M, mo[g2]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float wgt[kGroups];
+  float lsum = 0.f;
 #pragma unroll
-        for (int r = 1; r < kRing; ++r)
-          if ((it == 0 || r < kRing - 1) && held[r] < nst) ++later;
-        wait_stage(later);
-        if (it >= 1 && gw == 0 && lane == 0)
-          s_sel[grp][it & 1] = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        group_barrier();
-        if (it >= 1) {
-          const int nx = s_sel[grp][it & 1];
-          held[kRing - 1] = nx;
-          if (nx >= 0 && nx < nst) issue(nx, gring + ((it + kRing - 1) % kRing) * 2 * TILE);
-        }
-        if (it == 0 && computes) {
-          // the group's Q copy has landed (its loads precede this stage's);
-          // the row index is hidden from the compiler here, so the tile's
-          // addresses are formed now rather than kept in registers (or
-          // spilled) across every item's stage loop
-          int qrow = n_q;
-          asm volatile("" : "+v"(qrow));
+  for (int g2 = 0; g2 < kGroups; ++g2) {
+    wgt[g2] = tv::exp2_fast(mo[g2] - Mu);
+    lsum += wgt[g2] * lo_[g2];
+  }
 #pragma unroll
-          for (int c = 0; c < KC; ++c)
-            qv[c] = qrow < N ? as_bf16x8(*reinterpret_cast<const uint4*>(gq + tile_off<D>(qrow, 4 * c + lg)))
-                             : as_bf16x8(make_uint4(0, 0, 0, 0));
-        }
-        if (computes) compute(held[0], gring + (it % kRing) * 2 * TILE);
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r + 1 < kRing; ++r) held[r] = held[r + 1];
-        held[kRing - 1] = INT_MAX;                // claimed at the next iteration
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      lrun += __shfl_xor(lrun, 16, 64);
-      lrun += __shfl_xor(lrun, 32, 64);
+    for (int i = 0; i < 4; ++i) {
+      float acc = wgt[0] * o[dt][i];
+#pragma unroll
+      for (int g2 = 1; g2 < kGroups; ++g2) acc += wgt[g2] * mg[((g2 - 1) * NQT + qt) * SLOT + (dt * 4 + i) * 64 + lane];
+      o[dt][i] = acc;
     }
 
-    // ---- claim the item after the next one; the claim lands during the merge ----
-    const int b_done = b, h_done = h, s_done = s;
-    if (more && dyn && threadIdx.x == 0) claim_v = claim(s_a);
-
-    if (run) {
-      __syncthreads();
-      // ---- merge the groups' states through LDS (the ring is free now) ----
-      // Slot layout [group - 1][query tile][DT*4 + 2][lane] floats: each lane
-      // writes and reads only its own column, so there are no bank conflicts.
-      float* mg = reinterpret_cast<float*>(ring);
-      if (grp > 0 && computes) {
-        float* dst = mg + ((grp - 1) * NQT + qt) * SLOT + lane;
+  if (a.splits == 1) {
+    if (n_q < N) {
+      uint16_t* out = static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(b) * N + n_q) * a.H + h) * D;
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[(dt * 4 + i) * 64] = o[dt][i];
-        dst[(DT * 4) * 64] = mrun;
-        dst[(DT * 4 + 1) * 64] = lrun;
-      }
-      __syncthreads();
-      if (!MASK && badblk && threadIdx.x == 0) s_a.status[b_done] = TV_REQ_BAD_BLOCK;
-      if (s_hung && threadIdx.x == 0) {
-        if (MASK) store_status(s_a.status, b_done, TV_REQ_TIMEOUT);
-        else s_a.status[b_done] = TV_REQ_TIMEOUT;
-      }
-      if (grp == 0 && computes) {
-        float mo[kGroups], lo_[kGroups];
-        mo[0] = mrun;
-        lo_[0] = lrun;
-#pragma unroll
-        for (int g2 = 1; g2 < kGroups; ++g2) {
-          const float* src = mg + ((g2 - 1) * NQT + qt) * SLOT + lane;
-          mo[g2] = src[(DT * 4) * 64];
-          lo_[g2] = src[(DT * 4 + 1) * 64];
-        }
-        float M = mo[0];
-#pragma unroll
-        for (int g2 = 1; g2 < kGroups; ++g2) M = fmaxf(M, mo[g2]);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        float wgt[kGroups];
-        float lsum = 0.f;
-#pragma unroll
-        for (int g2 = 0; g2 < kGroups; ++g2) {
-          wgt[g2] = tv::exp2_fast(mo[g2] - Mu);
-          lsum += wgt[g2] * lo_[g2];
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float acc = wgt[0] * o[dt][i];
-#pragma unroll
-            for (int g2 = 1; g2 < kGroups; ++g2)
-              acc += wgt[g2] * mg[((g2 - 1) * NQT + qt) * SLOT + (dt * 4 + i) * 64 + lane];
-            o[dt][i] = acc;
-          }
-        if (a.splits == 1) {
-          if (n_q < N) {
-            uint16_t* out = s_a.out + ((static_cast<size_t>(b_done) * N + n_q) * a.H + h_done) * D;
-            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              uint2 v;
-              v.x = tv::pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-              v.y = tv::pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-              *reinterpret_cast<uint2*>(out + 16 * dt + 4 * lg) = v;
-            }
-          }
-        } else {
-          // several chunks: this chunk's unnormalised partial, merged by
-          // attn_merge_kernel after this kernel (the kernel boundary makes
-          // the partials of every XCD's L2 visible)
-          const size_t pbase = ((static_cast<size_t>(b_done) * a.H + h_done) * a.splits + s_done) * a.npad;
-          if (n_q < N) {
-            float* po = s_a.part_o + (pbase + n_q) * D;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lg) = o[dt];
-            if (lg == 0) {
-              s_a.part_ml[(pbase + n_q) * 2 + 0] = M;
-              s_a.part_ml[(pbase + n_q) * 2 + 1] = lsum;
-            }
-          }
-        }
+      for (int dt = 0; dt < DT; ++dt) {
+        uint2 v;
+        v.x = tv::pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+        v.y = tv::pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+        *reinterpret_cast<uint2*>(out + 16 * dt + 4 * lg) = v;
       }
     }
-    if (!more) break;
-    wait_all();
-    if (threadIdx.x == 0) settle_claim(s_a, claim_v, cur ^ 1);
-    __syncthreads();         // the next item's data and its successor are visible
-    item = nxt;
+    return;
+  }
+  // ---- several chunks: write this chunk's unnormalised partial ----
+  // (merged by attn_merge_kernel after this kernel; the kernel boundary makes
+  // the partials of every XCD's L2 visible, no device-scope fence is needed)
+  const size_t pbase = ((static_cast<size_t>(b) * a.H + h) * a.splits + s) * a.npad;
+  if (n_q < N) {
+    float* po = a.part_o + (pbase + n_q) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lg) = o[dt];
+    if (lg == 0) {
+      a.part_ml[(pbase + n_q) * 2 + 0] = M;
+      a.part_ml[(pbase + n_q) * 2 + 1] = lsum;
+    }
   }
 }
 
@@ -1135,11 +919,10 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
 // ===========================================================================
 struct Plan {
   int chunk, splits, npad;
-  size_t off_part, off_ml, ws_bytes;   // bf16: the item counter, then the partials
+  size_t off_ml, ws_bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-constexpr size_t kCtlBytes = kQueues * kQueueStride * 4;   // bf16 workspace head: the item counters (1 KB)
 
 // bf16 attention workgroups resident at once on the current device
 // (compute units x workgroups per CU at head dim D; cached per device: every
@@ -1205,22 +988,14 @@ Plan make_plan(tv_dtype dt, int B, int N, int H, int D, int max_blocks) {
   }
   p.chunk = static_cast<int>(c);
   p.splits = static_cast<int>((keys_max + c - 1) / c);
-  p.off_part = dt == TV_BF16 ? kCtlBytes : 0;
   if (p.splits > 1) {
     const size_t rows = static_cast<size_t>(B) * H * p.splits * p.npad;
-    p.off_ml = p.off_part + align256(rows * D * sizeof(float));
+    p.off_ml = align256(rows * D * sizeof(float));
     p.ws_bytes = p.off_ml + align256(rows * 2 * sizeof(float));
   } else {
-    p.off_ml = p.ws_bytes = p.off_part;
+    p.off_ml = p.ws_bytes = 0;
   }
   return p;
-}
-
-// Persistent bf16 launch: one workgroup per resident slot, or one per item
-// when there are fewer items.
-unsigned attn_grid(int B, int H, int splits, int D) {
-  const long items = static_cast<long>(B) * H * splits;
-  return static_cast<unsigned>(std::min<long>(items, attn_slots(D)));
 }
 
 }  // namespace
@@ -1248,12 +1023,11 @@ static tv_status attn_setup(tv_dtype dt, int B, int N, int H, int D, float scale
       max_blocks < 1 || num_blocks < 1)
     return TV_EINVAL;
   if (N > TV_MAX_NODES) return TV_ETOOBIG;
-  if (B > 65535 || H > 65535) return TV_EINVAL;      // grid y/z limits (fp32), item count (bf16)
+  if (B > 65535 || H > 65535) return TV_EINVAL;      // grid y/z limits
   if (B == 0 || N == 0) return TV_OK;
   if (!q || !k_cache || !v_cache || !block_table || !prefix_len || !status || !out || !ptrs_ok)
     return TV_EINVAL;
   p = make_plan(dt, B, N, H, D, max_blocks);
-  if (static_cast<int64_t>(B) * H * p.splits > (1ll << 30)) return TV_EINVAL;   // items fit an int
   if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes)) return TV_EWORKSPACE;
 
   a = AttnArgs{};
@@ -1263,9 +1037,8 @@ static tv_status attn_setup(tv_dtype dt, int B, int N, int H, int D, float scale
   a.num_blocks = num_blocks; a.block_table = block_table; a.max_blocks = max_blocks;
   a.prefix_len = prefix_len; a.status = status; a.out = out;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.ctl = dt == TV_BF16 ? ws : nullptr;
-  a.part_o = p.splits > 1 ? reinterpret_cast<float*>(ws + p.off_part) : nullptr;
-  a.part_ml = p.splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
+  a.part_o = p.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_ml = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
   a.chunk = p.chunk; a.splits = p.splits; a.npad = p.npad;
   return TV_OK;
 }
@@ -1286,21 +1059,20 @@ extern "C" tv_status tree_attn_verify(tv_dtype dt, int B, int N, int H, int D, f
 
   const dim3 grid(p.splits, H, B);
   if (dt == TV_BF16) {
-    const dim3 pgrid(attn_grid(B, H, p.splits, D));
     const int nqt = (N + 15) / 16;
     if (D == 128) {
       switch (nqt) {
-        case 1: launch_mfma<128, 1>(pgrid, stream, a); break;
-        case 2: launch_mfma<128, 2>(pgrid, stream, a); break;
-        case 3: launch_mfma<128, 3>(pgrid, stream, a); break;
-        default: launch_mfma<128, 4>(pgrid, stream, a); break;
+        case 1: launch_mfma<128, 1>(grid, stream, a); break;
+        case 2: launch_mfma<128, 2>(grid, stream, a); break;
+        case 3: launch_mfma<128, 3>(grid, stream, a); break;
+        default: launch_mfma<128, 4>(grid, stream, a); break;
       }
     } else {
       switch (nqt) {
-        case 1: launch_mfma<64, 1>(pgrid, stream, a); break;
-        case 2: launch_mfma<64, 2>(pgrid, stream, a); break;
-        case 3: launch_mfma<64, 3>(pgrid, stream, a); break;
-        default: launch_mfma<64, 4>(pgrid, stream, a); break;
+        case 1: launch_mfma<64, 1>(grid, stream, a); break;
+        case 2: launch_mfma<64, 2>(grid, stream, a); break;
+        case 3: launch_mfma<64, 3>(grid, stream, a); break;
+        default: launch_mfma<64, 4>(grid, stream, a); break;
       }
     }
   } else if (D == 128) {
@@ -1346,7 +1118,7 @@ extern "C" tv_status tree_mask_attn_verify(tv_dtype dt, int B, int N, int H, int
   a.anc_out = anc;
   a.child_out = child;
   a.depth_out = depth;
-  const dim3 grid(attn_grid(B, H, 1, D));
+  const dim3 grid(1, H, B);
   const int nqt = (N + 15) / 16;
   if (D == 128) {
     switch (nqt) {
