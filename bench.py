@@ -3,22 +3,28 @@
 A step is the whole verification path over one batch of synthetic input:
 tree_build_mask -> tree_attn_verify -> tree_verify_greedy -> tree_verify_mss
 -> kv_commit_accepted, in three launches: tree_mask_attn_verify (the masks
-and the attention, with the results of the first two calls) and
-tree_verify_mss_commit (the results of the last two).  The default workload is the LLaMA-7B-shaped layer
-(bf16, 8 requests x 32 heads x 128 dims, 1024-token prefixes, a 46-node
-expansion tree <2,2,2,1,1,1,1>, fp32 logits over a 32000-token vocabulary).
+and the attention, with the results of the first two calls),
+tree_verify_greedy, and tree_verify_mss_commit (the results of the last two).
 
-Inputs stay resident in HBM.  Because one step's data (~250 MB) would fit in
-the 256 MB Infinity Cache, the timed loop rotates over several copies of the
-inputs whose total exceeds twice that cache, so each step reads from HBM.
-The commit grows each copy's prefix lengths; the timed graphs hold one step
-per copy and then one copy that restores every copy's prefix lengths, so each
-step sees the same workload.
+The headline workload is the LLaMA-65B-shaped layer, the largest of the
+five that runs on one GPU (bf16, 32 requests x 64 heads x 128 dims, ragged
+prefixes of 512..4096 tokens in a paged cache, random 64-node trees, fp32
+logits over a 32000-token vocabulary).  The LLaMA-7B, OPT-30B and
+long-context layers are measured the same way and reported beside it.
+
+Inputs stay resident in HBM.  The timed loop rotates over several copies of
+the inputs whose total exceeds twice the 256 MB Infinity Cache, so each step
+reads from HBM.  The commit grows each copy's prefix lengths; the timed
+graphs hold one step per copy and then one copy that restores every copy's
+prefix lengths, so each step sees the same workload.
 
 Prints ONE JSON line (rank 0, N = 1): throughput in verified tree tokens/s
 (B * N tree nodes per step), the roofline of the dominant kernel (attention,
-HBM-bound) from HIP events recorded on the launch stream, and the CPU oracle
-timed on a bounded sample of the same workload.
+HBM-bound) from HIP events recorded on the launch stream, the other
+workloads, and the CPU oracle timed on a bounded sample of the same workload
+on one host core and on all of the host's cores given to this GPU; the
+oracle also replays the step's MSS call, and the line reports how many
+requests match it exactly and how many differ only at a near tie.
 """
 import argparse
 import json
@@ -41,9 +47,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=None, help="workload id 1..5 (default 2 = LLaMA-7B layer)")
+    ap.add_argument("--config", type=int, default=None, help="workload id 1..5 (default 4 = LLaMA-65B layer)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU sample time")
+    ap.add_argument("--no-others", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU sample time per leg")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + steps eager steps and exit (for counter collection)")
@@ -81,22 +88,61 @@ def main():
               "(the verification step shards by request with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
-    import torch
-
-    if args.copy_calibration_mb:
-        copy_calibration(torch, args.copy_calibration_mb)
-        return
-    if args.compare_sequence:
-        compare_sequence_all(torch, [args.config] if args.config else [2, 3, 4, 5])
+    if args.copy_calibration_mb or args.compare_sequence:
+        import torch
+        if args.copy_calibration_mb:
+            copy_calibration(torch, args.copy_calibration_mb)
+        else:
+            compare_sequence_all(torch, [args.config] if args.config else [2, 3, 4, 5])
         return
 
     import synth
+    w = synth.make_config(args.config or 4)
+    note(f"built {w.name}")
+    # The CPU oracle runs first, while no GPU context exists in this process,
+    # so its all-cores leg can fork worker processes.
+    cpu = None
+    if not args.no_cpu and not args.profile_only:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        note("timed the CPU oracle")
+
+    import torch
     import tree_speculative_verification_attn_amd as tv
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    res = run_workload(torch, tv, w, args, full=True)
+    if res is None:                       # --profile-only
+        return
+    note(f"measured {w.name}")
+    mss_out = res.pop("_mss_out")
+    if not args.no_others and args.config is None:
+        others = {}
+        for c in (2, 3, 5):
+            wc = synth.make_config(c)
+            others[wc.name] = run_workload(torch, tv, wc, args, full=False)
+            note(f"measured {wc.name}")
+            del wc
+            torch.cuda.empty_cache()
+        res["other_workloads"] = others
+    if cpu is not None:
+        for leg in ("one_core", "all_cores"):
+            cpu[leg]["gpu_over_cpu"] = round(res["value"] / cpu[leg]["value"], 1)
+        cpu["mss_replay"] = mss_replay(w, mss_out)
+        res["cpu_baseline"] = cpu
+    print(json.dumps(res))
+
+
+def note(msg):
+    """Progress on stderr; the JSON line alone goes to stdout."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def run_workload(torch, tv, w, args, full):
+    """Time the step and its launches on one workload.  full: the headline
+    line (with the verify variants, every entry point, tree against per-path
+    attention, and the MSS outputs the oracle replays); otherwise a summary."""
     from synth.device import to_dev
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
-    w = synth.make_config(args.config or 2)
     bf = w.dtype == "bf16"
     B, N, H, D, V, R = w.B, w.N, w.H, w.D, w.V, w.R
     step_bytes = w.k_cache.nbytes * 2 + w.target_logits.nbytes + w.ssm_probs.nbytes
@@ -158,7 +204,7 @@ def main():
             step(args.warmup + i)
         torch.cuda.synchronize()
         print(f"ran {args.warmup} + {args.steps} eager steps of {w.name}")
-        return
+        return None
 
     # Eager pass with HIP events between the calls: per-call times on the
     # launch stream (the attention figure feeds the roofline).
@@ -240,12 +286,26 @@ def main():
     t_mss = per_call_ms(lambda c: tv.tree_verify_mss(c["tl"], c["sp"], qr, token, child, status, w.seed, w.offset,
                                                      m_acc, m_num, m_bonus, m_rounds, ws_v))
     assert int((status != 0).sum()) == 0, "a request failed during the benchmark"
-    variants = verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status, ws_v, t_mss)
+    t_greedy = per_call_ms(lambda c: tv.tree_verify_greedy(c["tl"], token, child, status, g_acc, g_num, g_bonus, ws_v))
     a_bytes = attn_bytes(w) + mask_bytes(w)
     l_bytes = logit_bytes(w)
     attn_gbs = a_bytes / (t_attn * 1e-3) / 1e9
     mss_gbs = l_bytes / (t_mss * 1e-3) / 1e9
     value = B * N / (ms_per_step * 1e-3)
+
+    if not full:
+        del copies
+        return {"workload": f"{w.name}: B={B} H={H} D={D} L={_lens(w)} N={N} V={V}",
+                "ms_per_step": round(ms_per_step, 5), "verified_tree_tokens_per_s": round(value, 1),
+                "attention": {"kernel": "tree_mask_attn_verify", "ms_per_launch": round(t_attn, 5),
+                              "achieved_GBps": round(attn_gbs, 1), "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                              "algorithmic_bytes": a_bytes,
+                              "tree_attn_verify_ms_per_launch": round(t_attn_only, 5)},
+                "mss": {"ms_per_launch": round(t_mss, 5), "achieved_GBps_on_logit_bytes": round(mss_gbs, 1),
+                        "frac": round(mss_gbs / HBM_PEAK_GBS, 4), "logit_bytes": l_bytes},
+                "greedy_ms_per_launch": round(t_greedy, 5),
+                "tree_attn_plus_mss_tokens_per_s": round(B * N / ((t_attn + t_mss) * 1e-3), 1),
+                "input_copies_rotated": n_copies}
 
     res = {
         "metric": METRIC,
@@ -260,9 +320,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic (seeded NumPy; page-shaped, no model weights)",
-        "config": {"workload": f"{w.name}: B={B} H={H} D={D} L={int(w.prefix_len.max())} N={N} V={V}",
+        "config": {"workload": f"{w.name}: B={B} H={H} D={D} L={_lens(w)} N={N} V={V}",
                    "tree": str(w.meta.get("tree")), "batch": B, "tree_nodes": N,
-                   "prefix_len": int(w.prefix_len.max()), "vocab": V,
+                   "prefix_len_min": int(w.prefix_len.min()), "prefix_len_max": int(w.prefix_len.max()),
+                   "prefix_len_mean": round(float(w.prefix_len.mean()), 2), "vocab": V,
                    "input_copies_rotated": n_copies},
         "roofline": {"bound": "hbm", "kernel": "tree_mask_attn_verify", "achieved": round(attn_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
@@ -277,17 +338,31 @@ def main():
                 "tree_attn_plus_mss_tokens_per_s": round(B * N / ((t_attn + t_mss) * 1e-3), 1),
                 "mean_tokens_emitted_per_request": round(acc_tokens, 3)},
     }
+    variants = verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status, ws_v, t_mss, t_greedy)
     res["verify_variants"] = variants
     res["per_call_ms"] = per_call_table(torch, tv, w, copies, per_call_ms, pl0, parent, anc, child, depth, status,
                                         token, qr, bt, m_acc, m_num, m_bonus, m_rounds, ws_v, t_attn, t_attn_only,
                                         t_mss, variants)
     res["tree_vs_sequence"] = tree_vs_sequence(torch, tv, w, copies, bt, t_attn_only, stream)
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, value)
-    print(json.dumps(res))
+    # the MSS call the oracle replays: input copy 0, the workload's own
+    # Philox key and offset, every request live
+    st0 = torch.zeros((B,), dtype=torch.int32, device=dev)
+    tv.tree_verify_mss(copies[0]["tl"], copies[0]["sp"], qr, token, child, st0, w.seed, w.offset, m_acc, m_num,
+                       m_bonus, m_rounds, ws_v)
+    torch.cuda.synchronize()
+    res["_mss_out"] = {k: t.cpu().numpy() for k, t in (("accepted", m_acc), ("num_accepted", m_num),
+                                                        ("bonus", m_bonus), ("rounds", m_rounds), ("status", st0))}
+    del copies
+    torch.cuda.empty_cache()
+    return res
 
 
-def verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status, ws_v, t_mss):
+def _lens(w):
+    lo, hi = int(w.prefix_len.min()), int(w.prefix_len.max())
+    return str(hi) if lo == hi else f"{lo}..{hi}"
+
+
+def verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status, ws_v, t_mss, t_greedy):
     """The Table 3 analogue on this synthetic workload (SpecInfer summary,
     Theorem 4.3 and Table 3: MSS against naive sampling, tokens per step), the
     greedy rule beside them, and the cost of a sampling transform of every
@@ -311,7 +386,6 @@ def verify_variants(torch, tv, w, copies, per_call_ms, qr, token, child, status,
     tokens["greedy"] = float((num.clamp(min=0) + 1).float().mean()) * reps
     t_naive = per_call_ms(lambda c: tv.tree_verify_naive(c["tl"], token, child, status, w.seed, w.offset,
                                                          acc, num, bonus, ws_v))
-    t_greedy = per_call_ms(lambda c: tv.tree_verify_greedy(c["tl"], token, child, status, acc, num, bonus, ws_v))
     scratch = torch.empty_like(copies[0]["tl"])
     t_tf = per_call_ms(lambda c: tv.tree_logits_transform(c["tl"], scratch, 0.8, 50, 0.9, tv.TV_OUT_LOGITS))
     assert int((status != 0).sum()) == 0, "a request failed in the verify variants"
@@ -504,47 +578,146 @@ def measured_traffic(workload):
         return None
 
 
-def cpu_baseline(w, budget_s, gpu_value):
-    """The float64 oracle on a bounded sample of the same workload (about
-    budget_s seconds of work), scaled to a whole step: attention is timed on
-    (request, head) pairs drawn at random, verification on requests taken in
-    turn, each until its share of the budget is spent."""
+_CPU = {}          # the workload and its masks, inherited by forked workers
+
+
+def _cpu_init():
+    import threadpoolctl
+    _CPU["limit"] = threadpoolctl.threadpool_limits(1)
+
+
+def _cpu_attn(pairs):
+    from oracle import attention
+    w, anc, st = _CPU["w"], _CPU["anc"], _CPU["st"]
+    t = time.perf_counter()
+    for b, h in pairs:
+        attention.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len, anc, st,
+                                 w.dtype, w.scale, pairs=[(b, h)])
+    return time.perf_counter() - t
+
+
+def _cpu_verify(reqs):
+    from oracle import verify
+    w = _CPU["w"]
+    t = time.perf_counter()
+    for r in reqs:
+        verify.verify_greedy(w.parent[r:r + 1], w.token[r:r + 1], w.target_logits[r:r + 1], [0])
+        verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0] * w.B,
+                          w.seed, w.offset, requests=[r])
+    return time.perf_counter() - t
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s):
+    """The float64 oracle on a bounded sample of the same workload, scaled to
+    one whole step, on one core and on all the cores this process may use (at
+    most 16, one worker process per core, each with one BLAS thread).
+    Attention is timed on (request, head) pairs drawn at random, verification
+    (greedy + MSS) on requests taken in turn; each leg spends about budget_s
+    seconds of wall time."""
+    import multiprocessing
+
     import threadpoolctl
 
-    from oracle import attention, commit, tree, verify
+    from oracle import tree
 
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads by default)"
+            for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    anc, child, depth, st = tree.build_mask_batch(w.parent)
+    _CPU.update(w=w, anc=anc, st=st)
+    rng = np.random.default_rng(0)
+    pair_stream = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4096)]
+
+    # one core
     with threadpoolctl.threadpool_limits(1):
         t = time.perf_counter()
-        anc, child, depth, st = tree.build_mask_batch(w.parent)
+        tree.build_mask_batch(w.parent)
         t_mask = time.perf_counter() - t
-        pairs_done = 0
-        t_attn = 0.0
-        rng = np.random.default_rng(0)
-        while t_attn < budget_s * 0.6:
-            b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
-            t = time.perf_counter()
-            attention.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len, anc, st,
-                                     w.dtype, w.scale, pairs=[(b, h)])
-            t_attn += time.perf_counter() - t
-            pairs_done += 1
-        reqs = 0
-        t_ver = 0.0
-        while t_ver < budget_s * 0.3:
-            r = reqs % w.B
-            t = time.perf_counter()
-            verify.verify_greedy(w.parent[r:r + 1], w.token[r:r + 1], w.target_logits[r:r + 1], [0])
-            verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0] * w.B,
-                              w.seed, requests=[r])
-            t_ver += time.perf_counter() - t
-            reqs += 1
-    full = (t_mask + t_attn * (w.B * w.H) / pairs_done + t_ver * w.B / reqs)
-    v = w.B * w.N / full
-    return {"value": round(v, 3), "unit": "verified tree tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 NumPy oracle, 1 thread, {t_mask + t_attn + t_ver:.1f} s of work: masks for all "
-                      f"{w.B} requests, attention on {pairs_done} (request, head) pairs drawn at random from "
-                      f"{w.B * w.H}, greedy + MSS on {reqs} requests taken in turn from {w.B}; scaled to one "
-                      f"full step ({full:.2f} s)",
-            "host_cpus": os.cpu_count(), "gpu_over_cpu": round(gpu_value / v, 1)}
+        n_pairs, t_attn = 0, 0.0
+        while t_attn < budget_s * 0.65 and n_pairs < len(pair_stream):
+            t_attn += _cpu_attn(pair_stream[n_pairs:n_pairs + 1])
+            n_pairs += 1
+        n_reqs, t_ver = 0, 0.0
+        while t_ver < budget_s * 0.35:
+            t_ver += _cpu_verify([n_reqs % w.B])
+            n_reqs += 1
+    step1 = t_mask + t_attn / n_pairs * (w.B * w.H) + t_ver / n_reqs * w.B
+    one = {"value": round(w.B * w.N / step1, 3), "unit": "verified tree tokens/s", "cores": 1,
+           "step_s": round(step1, 3),
+           "sample": f"{n_pairs} (request, head) pairs of {w.B * w.H} drawn at random, greedy + MSS on "
+                     f"{n_reqs} requests of {w.B} in turn, masks for all requests; "
+                     f"{t_mask + t_attn + t_ver:.1f} s of work"}
+
+    # all cores: the same units spread over worker processes
+    cores = min(16, len(os.sched_getaffinity(0)))
+    per_pair, per_req = t_attn / n_pairs, t_ver / n_reqs
+    k_pairs = max(cores, int(budget_s * 0.65 * cores / per_pair))
+    k_reqs = max(cores, int(budget_s * 0.35 * cores / per_req))
+    while len(pair_stream) < n_pairs + k_pairs:
+        pair_stream.append((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(cores, initializer=_cpu_init) as pool:
+        pool.map(_cpu_attn, [pair_stream[i:i + 1] for i in range(cores)])       # workers up
+        chunks = [pair_stream[n_pairs + i:n_pairs + k_pairs:cores] for i in range(cores)]
+        t = time.perf_counter()
+        pool.map(_cpu_attn, chunks, chunksize=1)
+        wall_attn = time.perf_counter() - t
+        reqs = [(n_reqs + i) % w.B for i in range(k_reqs)]
+        t = time.perf_counter()
+        pool.map(_cpu_verify, [reqs[i::cores] for i in range(cores)], chunksize=1)
+        wall_ver = time.perf_counter() - t
+    stepn = t_mask + wall_attn / k_pairs * (w.B * w.H) + wall_ver / k_reqs * w.B
+    alln = {"value": round(w.B * w.N / stepn, 3), "unit": "verified tree tokens/s", "cores": cores,
+            "step_s": round(stepn, 3),
+            "sample": f"{k_pairs} (request, head) pairs and {k_reqs} requests over {cores} worker processes "
+                      f"(one BLAS thread each), {wall_attn + wall_ver:.1f} s wall; masks as one core"}
+    return {"value": alln["value"], "unit": "verified tree tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 NumPy oracle of {w.name}, scaled from a bounded sample to one full step; "
+                      f"all-cores leg: {alln['sample']}",
+            "one_core": one, "all_cores": alln, "cpu_model": _cpu_model(),
+            "host_cpus": os.cpu_count(), "cpus_usable": len(os.sched_getaffinity(0)),
+            "blas": "; ".join(blas) or "none found"}
+
+
+NEAR_TIE = 1e-6
+
+
+def mss_replay(w, dev_out):
+    """The oracle's MSS walk of every request of the step's MSS call (the
+    workload's key and offset) against the device's outputs.  A request
+    counts as a near tie when it differs and the oracle's walk with one
+    decision of margin below 1e-6 taken the other way gives the device's
+    result; anything else is a mismatch."""
+    from oracle import verify
+    t = time.perf_counter()
+    ref = verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, [0] * w.B, w.seed, w.offset)
+    exact = near = 0
+    bad = []
+    for b in range(w.B):
+        def same(r, b=b):
+            return (dev_out["num_accepted"][b] == r["num_accepted"][b] and dev_out["bonus"][b] == r["bonus"][b]
+                    and dev_out["rounds"][b] == r["rounds"][b] and dev_out["status"][b] == r["status"][b]
+                    and np.array_equal(dev_out["accepted"][b], r["accepted"][b]))
+        if same(ref):
+            exact += 1
+            continue
+        margins = [m for _, m in ref["traces"][b] if m is not None]
+        if any(m < NEAR_TIE and same(ref["redo"](b, k)) for k, m in enumerate(margins)):
+            near += 1
+        else:
+            bad.append(b)
+    return {"requests": w.B, "exact": exact, "near_tie": near, "mismatch": len(bad), "mismatched_requests": bad,
+            "oracle_s": round(time.perf_counter() - t, 2)}
 
 
 if __name__ == "__main__":
