@@ -13,7 +13,9 @@
  *  - All array pointers are DEVICE pointers owned by the caller.  The library
  *    allocates nothing, frees nothing and keeps no state between calls (it
  *    caches, per device, only what the device reports about itself: its
- *    compute unit count and the occupancy of its kernels).
+ *    compute unit count and the occupancy of its kernels).  The one
+ *    exception is tree_verify_mss_noalloc, whose workspace is a fixed
+ *    device array of the library.
  *  - Every call is asynchronous on `stream` (0 = the null stream).
  *  - The return value reports host-checkable problems only: bad sizes or
  *    dtypes, null pointers, a workspace that is too small, a failed launch.
@@ -55,8 +57,13 @@ typedef enum {
   TV_ETOOBIG = 2,     /* N > 64 */
   TV_EDTYPE = 3,      /* unknown tv_dtype */
   TV_EWORKSPACE = 4,  /* workspace smaller than the *_workspace() size */
-  TV_EHIP = 5         /* a HIP launch failed */
+  TV_EHIP = 5,        /* a HIP launch failed */
+  TV_ESCRATCH = 6     /* the call needs more than the library's fixed scratch
+                         (tree_verify_mss_noalloc) */
 } tv_status;
+
+/* Bytes of the fixed device array tree_verify_mss_noalloc uses as workspace. */
+#define TV_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 
@@ -255,6 +262,33 @@ tv_status tree_verify_mss(int B, int N, int V, int R, const float* target_logits
                           uint64_t offset, int32_t* accepted, int32_t* num_accepted,
                           int32_t* bonus, int32_t* rounds, void* workspace, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * tree_verify_mss_noalloc - tree_verify_mss for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * and harnesses that forbid hipMalloc.  It takes no workspace argument and
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *
+ * Arguments, outputs, status codes and results are those of tree_verify_mss;
+ * the workspace is a fixed array of TV_NOALLOC_SCRATCH_BYTES bytes of device
+ * memory inside the library, one per device, held until the process ends.
+ * The first call on a device (with that device current) looks up the
+ * array's address and queues a zero fill of it on `stream` ahead of the walk;
+ * every completed call leaves it zero again.  Every call on a device shares
+ * that device's array: calls that overlap in time on one device (on
+ * different streams, or from different threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe.  A first call
+ * made while `stream` is being captured also records the fill in the graph,
+ * and the next call outside a capture fills again.
+ * Errors: those of tree_verify_mss (without TV_EWORKSPACE), TV_ESCRATCH when
+ * tree_verify_workspace(B, N, V) exceeds TV_NOALLOC_SCRATCH_BYTES (about 1800
+ * requests at V = 32000), TV_EHIP when the array's address cannot be found.
+ */
+tv_status tree_verify_mss_noalloc(int B, int N, int V, int R, const float* target_logits,
+                                  const float* ssm_probs, const int32_t* q_row, const int32_t* token,
+                                  const uint64_t* child, int32_t* status, uint64_t seed,
+                                  uint64_t offset, int32_t* accepted, int32_t* num_accepted,
+                                  int32_t* bonus, int32_t* rounds, hipStream_t stream);
 
 /*
  * kv_commit_accepted - keep only the accepted path's KV entries.

@@ -10,7 +10,7 @@ import pytest
 import tree_speculative_verification_attn_amd as tv_pkg
 
 HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "treeverify.h")
-TV_OK, TV_EINVAL, TV_ETOOBIG, TV_EDTYPE, TV_EWORKSPACE = 0, 1, 2, 3, 4
+TV_OK, TV_EINVAL, TV_ETOOBIG, TV_EDTYPE, TV_EWORKSPACE, TV_ESCRATCH = 0, 1, 2, 3, 4, 6
 
 
 @pytest.fixture(scope="module")
@@ -42,8 +42,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(6):
-        assert tv_pkg.tv_status_string(code)
+    for code in range(7):
+        assert tv_pkg.tv_status_string(code) != "unknown status"
     assert tv_pkg.tv_status_string(99) == "unknown status"
 
 
@@ -100,6 +100,19 @@ def test_host_argument_checks(L):
                              None, _p(), wsv, None) == TV_EINVAL
     assert L.tree_verify_mss(2, 5, 1 << 21, 3, _p(), _p(), _p(), _p(), _p(), _p(), 1, 0, _p(), _p(),
                              _p(), None, _p(), wsv, None) == TV_EINVAL
+
+    def noalloc(B=2, N=5, V=1000, R=3, logits=True):
+        return L.tree_verify_mss_noalloc(B, N, V, R, _p() if logits else None, _p(), _p(), _p(), _p(), _p(),
+                                         1, 0, _p(), _p(), _p(), None, None)
+    assert noalloc(R=0) == TV_EINVAL
+    assert noalloc(V=1 << 21) == TV_EINVAL
+    assert noalloc(N=65) == TV_ETOOBIG
+    assert noalloc(logits=False) == TV_EINVAL
+    assert noalloc(B=0) == TV_OK
+    # the fixed scratch holds 1820 requests' exchange words at V = 32000
+    assert L.tree_verify_workspace(1820, 5, 32000) <= tv_pkg.TV_NOALLOC_SCRATCH_BYTES
+    assert noalloc(B=1821, V=32000) == TV_ESCRATCH
+    assert noalloc(B=200, V=1 << 20) == TV_ESCRATCH
     assert L.kv_commit_accepted(5, 2, 5, 2, 128, _p(), _p(), 10, 16, _p(), 4, _p(), _p(), _p(), _p(),
                                 None) == TV_EDTYPE
     assert L.kv_commit_accepted(1, 2, 65, 2, 128, _p(), _p(), 10, 16, _p(), 4, _p(), _p(), _p(), _p(),

@@ -15,7 +15,8 @@ __all__ = [
     "tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
     "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss", "kv_commit_accepted",
     "tree_verify_naive", "tree_logits_transform", "TV_OUT_LOGITS", "TV_OUT_PROBS", "tv_status_string",
-    "tree_verify_mss_commit", "tree_verify_mss_multi", "tree_mask_attn_verify",
+    "tree_verify_mss_commit", "tree_verify_mss_multi", "tree_mask_attn_verify", "tree_verify_mss_noalloc",
+    "TV_NOALLOC_SCRATCH_BYTES",
 ]
 
 TV_F32 = 0
@@ -25,7 +26,9 @@ TV_OUT_PROBS = 1
 EXPORTS = ("tree_build_mask", "tree_attn_verify_workspace", "tree_attn_verify",
            "tree_verify_workspace", "tree_verify_greedy", "tree_verify_mss",
            "kv_commit_accepted", "tree_verify_naive", "tree_logits_transform", "tv_status_string",
-           "tree_verify_mss_commit", "tree_verify_mss_multi", "tree_mask_attn_verify")
+           "tree_verify_mss_commit", "tree_verify_mss_multi", "tree_mask_attn_verify",
+           "tree_verify_mss_noalloc")
+TV_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libtreeverify.so")
@@ -49,6 +52,7 @@ def _load():
         "tree_verify_workspace": ([I, I, I], SZ),
         "tree_verify_greedy": ([I, I, I, P, P, P, P, P, P, P, P, SZ, P], I),
         "tree_verify_mss": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ, P], I),
+        "tree_verify_mss_noalloc": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P], I),
         "kv_commit_accepted": ([I, I, I, I, I, P, P, I, I, P, I, P, P, P, P, P], I),
         "tree_verify_mss_commit": ([I, I, I, I, P, P, P, P, P, P, U64, U64, P, P, P, P, P, SZ,
                                     I, I, I, P, P, I, I, P, I, P, P], I),
@@ -166,6 +170,18 @@ def tree_verify_mss(target_logits, ssm_probs, q_row, token, child, status, seed,
                                _ptr(token), _ptr(child), _ptr(status), int(seed), int(offset),
                                _ptr(accepted), _ptr(num_accepted), _ptr(bonus), _ptr(rounds),
                                _ptr(workspace), ws_bytes, _stream(stream)), "tree_verify_mss")
+
+
+def tree_verify_mss_noalloc(target_logits, ssm_probs, q_row, token, child, status, seed, offset,
+                            accepted, num_accepted, bonus, rounds, stream=None):
+    """tree_verify_mss with the library's fixed device scratch as its
+    workspace: allocates nothing."""
+    B, N1, V = target_logits.shape
+    R = ssm_probs.shape[1]
+    _check(lib().tree_verify_mss_noalloc(B, N1 - 1, V, R, _ptr(target_logits), _ptr(ssm_probs), _ptr(q_row),
+                                       _ptr(token), _ptr(child), _ptr(status), int(seed), int(offset),
+                                       _ptr(accepted), _ptr(num_accepted), _ptr(bonus), _ptr(rounds),
+                                       _stream(stream)), "tree_verify_mss_noalloc")
 
 
 def tree_verify_mss_commit(target_logits, ssm_probs, q_row, token, child, status, seed, offset,

@@ -54,6 +54,7 @@ extern "C" const char* tv_status_string(tv_status s) {
     case TV_EDTYPE: return "unsupported dtype";
     case TV_EWORKSPACE: return "workspace too small";
     case TV_EHIP: return "HIP launch failed";
+    case TV_ESCRATCH: return "call needs more than the fixed scratch";
   }
   return "unknown status";
 }

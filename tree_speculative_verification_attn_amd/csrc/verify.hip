@@ -43,6 +43,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdlib>
+#include <mutex>
 
 namespace {
 
@@ -1805,4 +1806,80 @@ extern "C" tv_status tree_verify_naive(int B, int N, int V, const float* target_
   a.num_accepted = num_accepted;
   a.bonus = bonus;
   return launch_walk(a, B, stream);
+}
+
+// ---------------------------------------------------------------------------
+// tree_verify_mss_noalloc: tree_verify_mss with its workspace in a fixed
+// device array of the library instead of a caller's buffer.
+//
+// `scratch` holds the exchange words of the sliced walk exactly as a caller's
+// workspace would (same layout, same all-zero rule between calls).  Each
+// device holds its own copy at its own address, so host code never passes the
+// array's name to a kernel: the first call on a device (that device current)
+// looks its address up with hipGetSymbolAddress and keeps it for the device,
+// and launches a zero fill of the array on the call's stream ahead of the
+// walk.  From then on every completed walk leaves the words zero, as with a
+// caller's workspace.  A first call made while its stream is being captured
+// records the fill in the graph and is not counted as the clearing one, so
+// the next call outside a capture clears again.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[TV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+__global__ void __launch_bounds__(256) scratch_fill_zero(uint4* p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];       // the array's device address, per device
+bool scratch_clear[kMaxDevices];      // a zero fill has run outside a capture
+
+tv_status scratch_for_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return TV_EINVAL;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TV_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  if (!scratch_clear[dev]) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return TV_EHIP;
+    const size_t n = TV_NOALLOC_SCRATCH_BYTES / sizeof(uint4);
+    hipLaunchKernelGGL(scratch_fill_zero, dim3(256), dim3(256), 0, stream,
+                       static_cast<uint4*>(scratch_ptr[dev]), n);
+    if (hipGetLastError() != hipSuccess) return TV_EHIP;
+    scratch_clear[dev] = cs == hipStreamCaptureStatusNone;
+  }
+  *out = scratch_ptr[dev];
+  return TV_OK;
+}
+
+}  // namespace
+
+extern "C" tv_status tree_verify_mss_noalloc(int B, int N, int V, int R, const float* target_logits,
+                                             const float* ssm_probs, const int32_t* q_row, const int32_t* token,
+                                             const uint64_t* child, int32_t* status, uint64_t seed,
+                                             uint64_t offset, int32_t* accepted, int32_t* num_accepted,
+                                             int32_t* bonus, int32_t* rounds, hipStream_t stream) {
+  const tv_status c = check_verify_args(B, N, V);
+  if (c != TV_OK) return c;
+  if (R < 1) return TV_EINVAL;
+  if (B == 0) return TV_OK;
+  if (!target_logits || !ssm_probs || !child || !status || !num_accepted || !bonus ||
+      (N > 0 && (!token || !accepted || !q_row)))
+    return TV_EINVAL;
+  const size_t need = ws_layout(B, V).total;
+  if (need > TV_NOALLOC_SCRATCH_BYTES) return TV_ESCRATCH;
+  void* ws = nullptr;
+  const tv_status s = scratch_for_device(stream, &ws);
+  if (s != TV_OK) return s;
+  return tree_verify_mss(B, N, V, R, target_logits, ssm_probs, q_row, token, child, status, seed, offset,
+                         accepted, num_accepted, bonus, rounds, ws, need, stream);
 }
