@@ -122,8 +122,19 @@ def test_fused_repeated_offsets():
         _run_both(w, offset=w.offset + off)
 
 
-def test_fused_full_config2():
-    _case("mss_commit full config 2")
-    w = synth.make_config(2)
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_fused_full_config(cfg):
+    """The step's verify launch at full size: identical to the two calls, the
+    MSS results equal to the oracle's (or differing only at a near tie of its
+    walk), and the whole K/V caches equal to the oracle's compaction."""
+    _case(f"mss_commit full config {cfg}")
+    w = synth.make_config(cfg)
     seq, fus, st_mask, st_verify = _run_both(w)
-    print(f"config 2: accepted {fus.m_num.cpu().numpy().tolist()}")
+    print(f"config {cfg}: accepted {fus.m_num.cpu().numpy().tolist()}")
+    ref = o_verify.verify_mss(w.parent, w.token, w.target_logits, w.ssm_probs, w.q_row, st_mask, w.seed,
+                              w.offset)
+    exact, excused, bad = compare_mss(fus, ref)
+    assert not bad, f"requests {bad} differ from the oracle"
+    print(f"config {cfg}: {exact} exact, {excused} at a near tie")
+    del seq
+    _oracle_commit(w, fus, st_verify, w.k_cache, w.v_cache, w.block_table, w.prefix_len)

@@ -1,7 +1,9 @@
 """Per-sequence layout on the GPU: every root-to-leaf path run as a chain of
 its own through tree_attn_verify gives, at each chain node, the tree output of
-the node it copies (both within the attention bar of the parity tests:
-2e-2 + 2e-2*|ref| for bf16, 1e-5 + 1e-5*|ref| for fp32)."""
+the node it copies, and the oracle's attention over the same chains (causal
+attention along each path over its prefix) gives the same outputs; both
+within the attention bar of the parity tests: 2e-2 + 2e-2*|ref| for bf16,
+1e-5 + 1e-5*|ref| for fp32."""
 import numpy as np
 import pytest
 import torch
@@ -17,6 +19,13 @@ TOL = {"bf16": (2e-2, 2e-2), "f32": (1e-5, 1e-5)}
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+
+
+def _host(t):
+    """Device tensor -> numpy array in the oracle's input form (bf16 as bit patterns)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
 
 
 def _attn(tv, q, k, v, bt, pl, parent, dtype, scale, H, D):
@@ -59,3 +68,17 @@ def test_paths_match_tree(cfg, kw):
         ref = tree_out[b, path]
         bad = np.abs(got - ref) > atol + rtol * np.abs(ref)
         assert not bad.any(), (s, b, path, float(np.abs(got - ref).max()))
+    # the chains against the oracle, every chain node and head
+    from oracle import attention as o_attn
+    from oracle import tree as o_tree
+    par = sb.parent.cpu().numpy()
+    anc_o, _, _, st_o = o_tree.build_mask_batch(par)
+    ref_seq, st_ref = o_attn.tree_attention(_host(sb.q), _host(sb.k_cache), _host(sb.v_cache),
+                                            sb.block_table.cpu().numpy(), sb.prefix_len.cpu().numpy(), anc_o,
+                                            st_o, w.dtype, w.scale)
+    assert all(x == 0 for x in st_ref)
+    for s, (b, path) in enumerate(sb.paths):
+        got = seq_out[s, :len(path)]
+        ref = ref_seq[s, :len(path)]
+        bad = np.abs(got - ref) > atol + rtol * np.abs(ref)
+        assert not bad.any(), ("oracle", s, b, path, float(np.abs(got - ref).max()))
