@@ -131,10 +131,9 @@ tv_status tree_build_mask(int B, int N, const int32_t* parent, uint64_t* anc,
  *   status        [B] int32 in/out: requests with status != 0 get zero output;
  *                 the call may set TV_REQ_KV_CAPACITY or TV_REQ_BAD_BLOCK
  *                 (then that request's output is unspecified)
- *   out           [B][N][H][D]; for bf16, a (request, head) whose keys span
- *                 more than 6 stages of 32 keys per chunk sums them in an order
- *                 set at run time, so repeated calls agree to rounding, not bit
- *                 for bit
+ *   out           [B][N][H][D]; every key is summed in an order fixed by
+ *                 the shapes alone, so repeated calls on the same inputs give
+ *                 the same bits
  *   workspace     ws_bytes >= tree_attn_verify_workspace(...) bytes of device
  *                 memory for per-chunk partial results (may be null when that
  *                 size is 0); contents on entry do not matter.  Calls that

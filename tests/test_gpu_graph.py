@@ -1,7 +1,7 @@
 """The whole verification step captured in a HIP graph: every replay must
-match the eager step bit for bit (the attention output to rounding where a
-chunk has more than 6 stages of 32 keys, whose summation order is set at run
-time).
+match the eager step bit for bit, the attention output included (chunks of
+a few and of more than 100 stages of 32 keys: each group sums a fixed set of
+stages in a fixed order).
 
 The step is tree_build_mask -> tree_attn_verify -> tree_verify_greedy ->
 tree_verify_mss -> kv_commit_accepted on one seeded workload, either as five
@@ -79,9 +79,6 @@ OUTS = ("anc", "child", "depth", "status", "out", "g_acc", "g_num", "g_bonus", "
 
 
 def _same(name, got, ref, w):
-    if name == "out" and int(w.prefix_len.max()) + w.N > 6 * 32:
-        g, r = got.float(), ref.float()
-        return bool(torch.all((g - r).abs() <= 2e-3 + 8e-3 * r.abs()))
     return torch.equal(got, ref)
 
 

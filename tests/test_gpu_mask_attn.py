@@ -1,12 +1,10 @@
 """tree_mask_attn_verify against tree_build_mask followed by tree_attn_verify:
-the masks, depths and status codes must be identical bit for bit (the call
-promises the results of the two calls in sequence), and so must the outputs
-wherever the attention sums in a fixed order (chunks of at most 6 stages of
-32 keys); longer chunks hand stages to groups at run time, so there the two
-outputs agree to rounding.  Both where it is one kernel (bf16, one chunk per
-(request, head)) and where it runs the two (fp32, split chunk plans).
-Outputs are also checked against the oracle, masks against the oracle's tree
-builder."""
+the masks, depths, status codes and outputs must be identical bit for bit
+(the call promises the results of the two calls in sequence, and the
+attention sums every chunk in a fixed order), both where it is one kernel
+(bf16, one chunk per (request, head)) and where it runs the two (fp32, split
+chunk plans).  Outputs are also checked against the oracle, masks against the
+oracle's tree builder."""
 import numpy as np
 import pytest
 import torch
@@ -59,17 +57,8 @@ def _same(seq, fus):
     assert torch.equal(seq.anc, fus.anc)
     assert torch.equal(seq.child, fus.child)
     assert torch.equal(seq.depth, fus.depth)
-    w = seq.w
     ok = seq.status.cpu().numpy() == 0         # (a bad block id leaves the output unspecified)
-    if int(w.prefix_len.max()) + w.N <= 6 * 32:
-        # at most 6 stages of 32 keys: the three groups' first two stages each,
-        # handed out statically, so both calls sum in the same order
-        assert np.array_equal(_raw(seq.out)[ok], _raw(fus.out)[ok])
-    else:
-        # later stages go to whichever group frees a buffer first, so the
-        # summation order (not the result beyond rounding) varies from run to run
-        so, fo = out_to_f64(seq.out)[ok], out_to_f64(fus.out)[ok]
-        assert np.all(np.abs(so - fo) <= 2e-3 + 8e-3 * np.abs(so)), float(np.abs(so - fo).max())
+    assert np.array_equal(_raw(seq.out)[ok], _raw(fus.out)[ok])
     zero = np.isin(seq.status.cpu().numpy(), (1, 6))
     assert np.all(out_to_f64(fus.out)[zero] == 0)
 
@@ -163,10 +152,23 @@ def test_fused_empty_tree():
     assert run.child.cpu().numpy().tolist() == [[0], [0], [0]]
 
 
-def test_fused_full_config2():
-    w = synth.make_config(2)
-    _case("mask+attn full config 2", _kernels(w))
-    assert _kernels(w) == "one kernel"
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_fused_full_config(cfg):
+    """The step's attention launch at full size: the same results as the two
+    calls, the same bits on repeated calls, masks equal to the oracle's,
+    sampled (request, head) outputs within the bar of the oracle."""
+    w = synth.make_config(cfg)
+    _case(f"mask+attn full config {cfg}", _kernels(w))
+    if cfg in (2, 4):
+        assert _kernels(w) == "one kernel"
     seq, fus = _both(w)
     _same(seq, fus)
-    _oracle(fus, pairs=[(0, 0), (3, 17), (7, 31)])
+    first = _raw(fus.out)
+    for _ in range(3):                       # repeated calls: the same bits
+        fus.mask_attn()
+        torch.cuda.synchronize()
+        assert np.array_equal(_raw(fus.out), first)
+    rng = np.random.default_rng(100 + cfg)
+    pairs = {(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(6)}
+    pairs |= {(0, 0), (w.B - 1, w.H - 1)}
+    _oracle(fus, pairs=sorted(pairs))

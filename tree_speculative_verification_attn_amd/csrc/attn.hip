@@ -20,8 +20,8 @@
 //
 // bf16 path (matrix cores): K/V stages of 32 keys go HBM -> LDS with
 // direct-to-LDS loads; three independent 4-wave groups per workgroup each
-// run a two-buffer ring (48 KB of loads in flight per CU) and claim stages
-// of the chunk at run time.  Within a group, wave w < ceil(N/16) owns query
+// run a two-buffer ring (48 KB of loads in flight per CU) and take the
+// chunk's stages in turn, so every call sums in the same order.  Within a group, wave w < ceil(N/16) owns query
 // tile w and keeps its running max, sum and O in registers.  Per 32 keys:
 //   S^T[key][query] = K . Q^T     on v_mfma_f32_16x16x32_bf16
 //     (A = 16 keys x 32 dims of K from LDS, B = 32 dims x 16 queries of Q)
@@ -171,8 +171,8 @@ __device__ __forceinline__ int tile_off(int r, int c16) {   // byte offset
 }
 
 // One workgroup per (request b, head h, key chunk s), made of kGroups groups of 4
-// waves.  The chunk is cut into stages of 32 keys, which the groups claim
-// as they go (see the loop below); each group runs as if it were a workgroup of its own: a
+// waves.  The chunk is cut into stages of 32 keys, dealt to the groups in
+// turn (see the loop below); each group runs as if it were a workgroup of its own: a
 // two-buffer ring of K/V stages filled HBM -> LDS with direct-to-LDS loads
 // (no registers), one stage in flight while the other is read, and its own
 // barrier (an LDS counter), so the groups drift independently and one
@@ -227,8 +227,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   __shared__ int s_hung;
   __shared__ int s_wflag[kAttnThreads / 64];      // per wave: 1 = request skipped, 2 = bad block id
   __shared__ int s_gbar[kGroups];
-  __shared__ int s_next;                    // next stage of the chunk not yet claimed
-  __shared__ int s_sel[kGroups][2];         // stage a group's wave 0 claimed for the group
   __shared__ int s_blk[kMaxChunkBlocks];
 
   // Every load that depends on nothing goes out first, in every thread:
@@ -348,11 +346,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     if (i < nblk && (raw[r] < 0 || raw[r] >= a.num_blocks)) bad = 1;
   }
   if (threadIdx.x < kGroups) s_gbar[threadIdx.x] = 0;
-  if (threadIdx.x < 2 * kGroups) s_sel[threadIdx.x >> 1][threadIdx.x & 1] = INT_MAX;
-  if (threadIdx.x == 0) {
-    s_hung = 0;
-    s_next = kGroups * kRing;               // the ones before are handed out statically below
-  }
+  if (threadIdx.x == 0) s_hung = 0;
   // The workgroup agrees on the status (another workgroup of the request
   // may flag a bad block meanwhile) and on the bad-block flag with one
   // barrier: each wave leaves its flags in a slot of its own.
@@ -563,21 +557,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
-  // Stages are handed to the groups at run time.  Group g starts with
-  // stages g, g + kGroups, ... (one per ring buffer, all loading now); after
-  // that, whenever a buffer frees up, the group claims the next unclaimed
-  // stage of the chunk from an LDS counter.  A group whose loads land late
-  // thus takes fewer stages, and the groups finish close together (with a
-  // fixed share, the group that started last decides when the workgroup
-  // ends).  Wave 0 of the group claims just before it arrives at the
-  // barrier and leaves the index in s_sel; the other waves read it after
-  // the barrier.  held[0] is the stage being computed, held[1..] the ones in
-  // flight; claims only grow, so once held[0] is past the chunk every later
-  // one is too.
+  // Stages are dealt in turn: group g takes stages g, g + kGroups,
+  // g + 2 kGroups, ... in that order, the first kRing of them loading now,
+  // the next one whenever a buffer frees up.  Each group thus sums a fixed
+  // set of stages in a fixed order, and the groups merge in group order, so
+  // the result does not depend on timing: repeated calls give the same bits.
+  // (Handing each freed buffer the next unclaimed stage instead balances
+  // the groups a little better but makes the summation order, and so the
+  // last bits of bf16 outputs, vary from call to call.)  held[0] is the
+  // stage being computed, held[1..] the ones in flight; they only grow, so
+  // once held[0] is past the chunk every later one is too.
   //
   // In the loop, one barrier per stage: after it, the stage's loads have
   // landed for every wave, and every wave has finished reading the buffer
-  // of the stage before, which is then refilled with the newly claimed
+  // of the stage before, which is then refilled with the group's next
   // stage, in flight during this stage's compute.
   int held[kRing];
   issue_q();
@@ -595,11 +588,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     for (int r = 1; r < kRing; ++r)
       if ((it == 0 || r < kRing - 1) && held[r] < nst) ++later;
     wait_stage(later);
-    if (it >= 1 && gw == 0 && lane == 0)
-      s_sel[grp][it & 1] = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     group_barrier();
     if (it >= 1) {
-      const int nx = s_sel[grp][it & 1];
+      const int nx = grp + kGroups * (it + kRing - 1);
       held[kRing - 1] = nx;
       if (nx >= 0 && nx < nst) issue(nx, gring + ((it + kRing - 1) % kRing) * 2 * TILE);
     }
@@ -613,7 +604,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
     if (computes) compute(held[0], gring + (it % kRing) * 2 * TILE);
 #pragma unroll
     for (int r = 0; r + 1 < kRing; ++r) held[r] = held[r + 1];
-    held[kRing - 1] = INT_MAX;                // claimed at the next iteration
+    held[kRing - 1] = INT_MAX;                // set at the next iteration
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lrun += __shfl_xor(lrun, 16, 64);
