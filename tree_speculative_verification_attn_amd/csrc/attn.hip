@@ -12,7 +12,9 @@
 // key K/V row is read from HBM exactly once and reused by all N tree queries
 // of that (b, h), which is what makes the tree pass cheaper than per-path
 // decoding.  The pass is bound by HBM bandwidth, so the bf16 kernel runs one
-// workgroup per CU that streams its chunk through LDS.  The number of chunks
+// workgroup per CU that streams its chunk through LDS (or, when a launch has
+// at least three rounds of items, three single-group workgroups per CU that
+// take the requests longest first).  The number of chunks
 // per (b, h) comes from a small cost
 // model: as few as keep every CU busy, because each extra chunk leaves an
 // unnormalised partial (O, max, sum) that a second kernel reads back and
@@ -53,6 +55,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
 constexpr int kMaxSplits = 64;                      // chunks per (request, head)
 constexpr int kMaxChunkKeys = 32768;                // keys per workgroup chunk (bf16 path)
+constexpr int kMaxChunkKeysG1 = 8192;               //   the same for single-group workgroups
+constexpr int kRankMaxB = 256;                      // requests the single-group kernel ranks
 constexpr int kMaxChunkBlocks = kMaxChunkKeys / TV_BLOCK + 1;
 
 struct AttnArgs {
@@ -79,6 +83,7 @@ struct AttnArgs {
   int chunk;                 // keys per chunk (multiple of 128)
   int splits;                // S
   int npad;                  // queries padded to a multiple of 16
+  int rank;                  // single-group bf16 kernel: take requests longest first
 };
 
 // Request-level checks done by every workgroup of request b.  Returns
@@ -186,7 +191,15 @@ __device__ __forceinline__ int tile_off(int r, int c16) {   // byte offset
 // At the end the groups' softmax states are merged through LDS; with several
 // chunks per (b, h) the merged state is written as an unnormalised partial
 // that attn_merge_kernel combines.
-constexpr int kGroups = 3;                  // 4-wave groups per workgroup
+//
+// G = 1 (the plan's `single`): one group per workgroup and three workgroups
+// per CU.  Each item then takes three times as long, but the start and end of
+// one workgroup (block ids, status, Q, the first stage's trip; the output)
+// overlap the other two's streaming instead of leaving the CU idle.  With
+// many rounds the launch's end would then be set by the long items that
+// happen to start last, so these workgroups rank the requests by prefix
+// length and blockIdx.z = r takes the request of rank r, longest first.
+constexpr int kGroups = 3;                  // 4-wave groups per workgroup (G of the default kernel)
 constexpr int kRing = 2;                    // stage buffers per group
 constexpr int kGroupThreads = 256;
 constexpr int kAttnThreads = kGroups * kGroupThreads;
@@ -199,8 +212,12 @@ constexpr unsigned kGroupSpinLimit = 1u << 26;
 // status (device-scope stores) and the mask outputs of tree_build_mask, so no
 // two workgroups write the same word, except a timeout (which comes only after
 // a workgroup's spin limit, long after the first workgroup's setup).
-template <int D, int NQT, bool MASK>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) {
+template <int D, int NQT, bool MASK, int G>
+__global__ __launch_bounds__(G * kGroupThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void attn_mfma_kernel(AttnArgs a) {
+  constexpr int kGroups = G;
+  constexpr int kAttnThreads = G * kGroupThreads;
+  constexpr int kMaxChunkBlocks = (G == 1 ? kMaxChunkKeysG1 : kMaxChunkKeys) / TV_BLOCK + 1;
   constexpr int KC = D / 32;               // contraction steps over D
   constexpr int DT = D / 16;               // output dim tiles
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
@@ -212,7 +229,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   static_assert((kGroups - 1) * NQT * SLOT * 4 <= kGroups * kRing * 2 * TILE, "merge area");
   static_assert(kRing >= 2 && kRing <= 4, "ring depth");
 
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s = blockIdx.x, h = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = wave >> 2, gw = wave & 3;          // group, wave within the group
   const int lr = lane & 15, lg = lane >> 4;
@@ -228,6 +245,33 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(AttnArgs a) 
   __shared__ int s_wflag[kAttnThreads / 64];      // per wave: 1 = request skipped, 2 = bad block id
   __shared__ int s_gbar[kGroups];
   __shared__ int s_blk[kMaxChunkBlocks];
+
+  // The request of this workgroup: blockIdx.z, or with a.rank the request of
+  // that rank when requests are ordered by prefix length, longest first (ties
+  // by index).  Workgroups are dispatched in blockIdx order, so the longest
+  // items start first and the launch ends on short ones.  The ranking uses
+  // the stage ring, which nothing has written yet.
+  int b = blockIdx.z;
+  if constexpr (G == 1) {
+    if (a.rank) {
+      int* s_pl = reinterpret_cast<int*>(ring + 1024);    // clear of the mask builder's child words
+      int* s_rb = reinterpret_cast<int*>(ring + 2048);
+      const int t = threadIdx.x;
+      if (t < a.B) s_pl[t] = a.prefix_len[t];
+      __syncthreads();
+      if (t < a.B) {
+        const int mine = s_pl[t];
+        int r = 0;
+        for (int i = 0; i < a.B; ++i) {
+          const int v = s_pl[i];
+          r += (v > mine) | ((v == mine) & (i < t));
+        }
+        if (r == static_cast<int>(blockIdx.z)) *s_rb = t;
+      }
+      __syncthreads();
+      b = __builtin_amdgcn_readfirstlane(*s_rb);
+    }
+  }
 
   // Every load that depends on nothing goes out first, in every thread:
   // the request's status and prefix length (same address in all threads),
@@ -910,6 +954,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
 // ===========================================================================
 struct Plan {
   int chunk, splits, npad;
+  bool single;               // bf16: single-group workgroups, requests longest first
   size_t off_ml, ws_bytes;
 };
 
@@ -931,8 +976,8 @@ int attn_slots(int D) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
-  const void* fn = D == 128 ? reinterpret_cast<const void*>(attn_mfma_kernel<128, 4, false>)
-                            : reinterpret_cast<const void*>(attn_mfma_kernel<64, 4, false>);
+  const void* fn = D == 128 ? reinterpret_cast<const void*>(attn_mfma_kernel<128, 4, false, kGroups>)
+                            : reinterpret_cast<const void*>(attn_mfma_kernel<64, 4, false, kGroups>);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kAttnThreads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const int slots = cus * per_cu;
@@ -979,6 +1024,12 @@ Plan make_plan(tv_dtype dt, int B, int N, int H, int D, int max_blocks) {
   }
   p.chunk = static_cast<int>(c);
   p.splits = static_cast<int>((keys_max + c - 1) / c);
+  // With one chunk per (request, head) and at least three rounds of
+  // workgroups, three single-group workgroups share each CU and the requests
+  // are taken longest first: one workgroup's start and end then overlap the
+  // other two's streaming, and the launch ends on its shortest items.
+  p.single = dt == TV_BF16 && p.splits == 1 && p.chunk <= kMaxChunkKeysG1 && B <= kRankMaxB &&
+             pairs >= 3L * attn_slots(D);
   if (p.splits > 1) {
     const size_t rows = static_cast<size_t>(B) * H * p.splits * p.npad;
     p.off_ml = align256(rows * D * sizeof(float));
@@ -999,7 +1050,10 @@ extern "C" size_t tree_attn_verify_workspace(tv_dtype dt, int B, int N, int H, i
 
 template <int D, int NQT, bool MASK = false>
 static void launch_mfma(dim3 grid, hipStream_t st, const AttnArgs& a) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NQT, MASK>), grid, dim3(kAttnThreads), 0, st, a);
+  if (a.rank)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NQT, MASK, 1>), grid, dim3(kGroupThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NQT, MASK, kGroups>), grid, dim3(kAttnThreads), 0, st, a);
 }
 
 // Argument checks shared by both entry points and the kernel arguments;
@@ -1031,6 +1085,7 @@ static tv_status attn_setup(tv_dtype dt, int B, int N, int H, int D, float scale
   a.part_o = p.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_ml = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
   a.chunk = p.chunk; a.splits = p.splits; a.npad = p.npad;
+  a.rank = p.single ? 1 : 0;
   return TV_OK;
 }
 
