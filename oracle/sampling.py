@@ -24,20 +24,47 @@ Outputs: kind "logits" gives the scaled logits where kept and -inf elsewhere
 (a softmax of them is the transformed distribution); kind "probs" gives the
 normalised kept probabilities and 0 elsewhere.
 
-Precision reading: the rows are fp32, so the scaled logit is the fp32 product
-l' = fp32(l * fp32(1 / T)) (exact for T = 1), and ranks, masses and outputs
-are taken from l'.  A consumer of the "logits" output then sees exactly these
-fp32 values.
+Precision reading: the scaled logit is l / T, exact in float64 (l is an fp32
+row, so the quotient is exact up to float64 rounding); ranks, masses and
+outputs are taken from it.  The output is an fp32 row, so a scaled value
+beyond the fp32 range acts as its fp32 rounding would: above it, +inf (the
+row is invalid); below minus it, -inf (the entry has probability 0 and is
+never kept).  A device that rounds the scaled logits to fp32 can then differ
+from this only at rounding-level ties: two entries whose fp32 scaled values
+coincide at the top-k cut, or a top-p target within rounding of a cumulative
+mass.
 """
 import numpy as np
 
 
+FP32_MAX = float(np.finfo(np.float32).max)
+FP32_HALF_ULP_AT_MAX = 2.0 ** 103          # values below FP32_MAX + this round to FP32_MAX
+
+
 def scaled(logits_row, temperature):
-    """l' = fp32(l * fp32(1/T)) as float64 (non-finite entries pass through)."""
-    l32 = np.asarray(logits_row, dtype=np.float32)
-    inv = np.float32(1.0) / np.float32(temperature)
+    """l / T in float64; non-finite entries pass through, and values beyond
+    the fp32 range become the infinity fp32 rounding would give."""
+    l = np.asarray(logits_row, dtype=np.float32).astype(np.float64)
     with np.errstate(invalid="ignore", over="ignore"):
-        return (l32 * inv).astype(np.float32).astype(np.float64)
+        x = l / float(temperature)
+    lim = FP32_MAX + FP32_HALF_ULP_AT_MAX
+    x = np.where(np.isfinite(x) & (x >= lim), np.inf, x)
+    x = np.where(np.isfinite(x) & (x <= -lim), -np.inf, x)
+    return x
+
+
+def rounding_tie_at_topk(logits_row, temperature, top_k):
+    """True when the k-th and (k+1)-th ranked scaled logits are within fp32
+    rounding of each other (relative 2^-22): the cut is then a tie that a
+    device rounding the scaled values to fp32 may settle either way."""
+    if top_k <= 0:
+        return False
+    l = scaled(logits_row, temperature)
+    fin = np.sort(l[np.isfinite(l)])[::-1]
+    if len(fin) <= top_k:
+        return False
+    a, b = fin[top_k - 1], fin[top_k]
+    return abs(a - b) <= 2.0 ** -22 * max(abs(a), abs(b))
 
 
 def kept_in_rank_order(logits_row, temperature=1.0, top_k=0, top_p=1.0):

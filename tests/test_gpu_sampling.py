@@ -1,10 +1,12 @@
 """Sampling transforms on the GPU (tree_logits_transform) against the oracle
 (oracle/sampling.py), and verification of transformed rows.
 
-Bars: the kept set exactly, except where the oracle's top-p cut lies within
-1e-6 (relative to the kept mass) of a cumulative mass, a tie that rounding
-may settle either way (counted); kept scaled logits bit-exact (both sides
-form the same fp32 product); probabilities within 1e-5 relative.  MSS on
+Bars: the kept set exactly, except at a tie that rounding may settle either
+way (counted): the oracle's top-p cut within 4e-6 (relative to the kept mass)
+of a cumulative mass, or its k-th and (k+1)-th scaled logits within fp32
+rounding of each other; kept scaled logits within 2.5e-7 relative of the
+oracle's exact l / T (the device forms fp32(l * fp32(1/T)), at most two
+roundings; exact at T = 1); probabilities within 1e-5 relative.  MSS on
 transformed rows follows the MSS parity bar; and with i.i.d. drafted children
 it samples the transformed target distribution (Theorem 4.2 for the sampling
 distributions, as the wiki's implementation sketch applies it)."""
@@ -57,11 +59,18 @@ def _check_rows(rows, T, k, p, label):
         assert set(np.nonzero(pr[i] > 0)[0].tolist()) <= got, label      # tiny masses may round to 0
         if got != set(keep):
             m = sampling.top_p_margin(row, T, k, p)
-            assert m < 1e-6, (label, i, sorted(got ^ set(keep))[:10], m)
+            tie_k = sampling.rounding_tie_at_topk(row, T, k)
+            assert m < 4e-6 or tie_k, (label, i, sorted(got ^ set(keep))[:10], m)
             near += 1
             continue
         ref_l = sampling.transform_row(row, T, k, p, "logits")
-        assert np.array_equal(lg[i].astype(np.float64), ref_l), label
+        fin = np.isfinite(ref_l)
+        assert np.array_equal(np.isfinite(lg[i]), fin), label
+        if T == 1.0:
+            assert np.array_equal(lg[i][fin].astype(np.float64), ref_l[fin]), label
+        else:
+            np.testing.assert_allclose(lg[i][fin].astype(np.float64), ref_l[fin], rtol=2.5e-7, atol=3e-45,
+                                       err_msg=label)
         ref_p = sampling.transform_row(row, T, k, p, "probs")
         np.testing.assert_allclose(pr[i], ref_p, rtol=1e-5, atol=1e-12, err_msg=label)
     return near
@@ -75,7 +84,7 @@ def test_transform_matches_oracle(V):
         for ties in (False, True):
             print(f"[case] transform V={V} T={T} k={k} p={p} ties={ties}", flush=True)
             near += _check_rows(_rows(V, n, 1000 * V + 10 * c + ties, ties), T, k, p, f"V={V} {T} {k} {p}")
-    print(f"V={V}: {near} rows with a top-p cut within 1e-6 of a cumulative mass")
+    print(f"V={V}: {near} rows with a cut at a rounding-level tie")
 
 
 def test_transform_fallback_paths():

@@ -27,7 +27,7 @@ def _beats(l, x):
 
 
 def _kept_by_rank(l, T, k, p):
-    l = sampling.scaled(l, T)          # ranks and masses on fp32(l * fp32(1/T))
+    l = np.asarray(l, dtype=np.float64) / T      # ranks and masses on l / T
     fin = [x for x in range(len(l)) if np.isfinite(l[x])]
     keep = [x for x in fin if k == 0 or len(_beats(l, x)) < k]
     if p < 1.0:
@@ -47,11 +47,9 @@ def test_plain_softmax_and_temperature():
         p = sampling.transform_row(l, temperature=T, kind="probs")
         i, j = 3, 17
         # the ratio of two probabilities is exp of the logit difference over T
-        # (up to the fp32 rounding of the scaled logits)
-        assert math.isclose(p[i] / p[j], math.exp((float(l[i]) - float(l[j])) / T), rel_tol=1e-6)
+        assert math.isclose(p[i] / p[j], math.exp((float(l[i]) - float(l[j])) / T), rel_tol=1e-12)
         lg = sampling.transform_row(l, temperature=T, kind="logits")
-        np.testing.assert_allclose(lg, l.astype(np.float64) / T, rtol=1.2e-7)
-        assert (lg.astype(np.float32).astype(np.float64) == lg).all()      # fp32 values
+        assert (lg == l.astype(np.float64) / T).all()
     assert (sampling.transform_row(l, kind="logits") == l.astype(np.float64)).all()
     # low temperature concentrates on the argmax, high temperature flattens
     assert sampling.transform_row(l, temperature=0.01, kind="probs")[int(np.argmax(l))] > 0.999
@@ -90,9 +88,18 @@ def test_ties_invalid_rows_and_extremes():
     assert lg.tolist() == [-np.inf, 2.5, 2.5, -np.inf, -np.inf]       # 5 * 0.5 is exact in fp32
     for bad in ([0.0, np.nan], [0.0, np.inf], [-np.inf, -np.inf]):
         assert np.isnan(sampling.transform_row(np.array(bad, dtype=np.float32), kind="probs")).all()
-    # scaling that overflows a finite logit makes the row invalid
+    # the output is fp32: a scaled logit past the fp32 range makes the row
+    # invalid (above) or drops the entry (below); up to FLT_MAX it is kept
     assert np.isnan(sampling.transform_row(np.array([3e38, 1.0], dtype=np.float32), 0.5)).all()
     assert sampling.kept_in_rank_order(np.array([-3e38, 1.0], dtype=np.float32), 0.5) == [1]
+    big = np.array([1.7e38, 1.0], dtype=np.float32)
+    assert sampling.kept_in_rank_order(big, 0.5) == [0, 1]
+    assert sampling.transform_row(big, 0.5)[0] == float(big[0]) * 2.0
+    # rounding-level ties at the top-k cut are recognised, others are not
+    one = np.float32(1.0)
+    assert sampling.rounding_tie_at_topk(np.array([one, np.nextafter(one, np.float32(2))]), 1.0, 1)
+    assert not sampling.rounding_tie_at_topk(np.array([1.0, 1.5], dtype=np.float32), 0.7, 1)
+    assert not sampling.rounding_tie_at_topk(np.array([1.0, 1.0], dtype=np.float32), 1.0, 0)
     # a tiny top-p keeps only the largest entry
     assert sampling.kept_in_rank_order(l2, 1.0, 0, 1e-9) == [1]
 
