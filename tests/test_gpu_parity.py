@@ -375,6 +375,34 @@ def test_verify_sliced_vocab(V):
         assert int(run.ws_v.count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("B", [6, 24])
+def test_verify_rows_with_empty_slices(B):
+    # Rows whose entries are -inf over whole workgroup slices (as top-k or
+    # top-p filtering leaves them): such a slice has no argmax, and its
+    # missing index must not be read as a NaN or +inf flag (2048-entry
+    # slices; the bands below hold several).
+    w = synth.make_workload(2, B=B, L=20, H=1, V=40000, seed=5)
+    w.token = (w.token % 4096).astype(w.token.dtype)     # tokens below 4096 stay finite
+    tl = w.target_logits.copy()
+    tl[:, :, 4096:12288] = -np.inf            # several whole slices at any width
+    tl[:, :, 20480:36864] = -np.inf
+    w.target_logits = tl
+    _print_case("verify rows with empty slices", B)
+    run = DeviceRun(w).mask().greedy()
+    torch.cuda.synchronize()
+    _check_greedy(run)
+    assert (run.status.cpu().numpy() == 0).all()
+    run = DeviceRun(w).mask().mss()
+    torch.cuda.synchronize()
+    _check_mss(run, f"empty slices B={B}")
+    assert (run.status.cpu().numpy() == 0).all()
+    run = DeviceRun(w).mask().naive()
+    torch.cuda.synchronize()
+    ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [0] * w.B, w.seed, w.offset)
+    exact, excused, bad = compare_naive(run, ref)
+    assert not bad, bad
+
+
 @pytest.mark.parametrize("V", [5003, 40003])
 def test_verify_workspace_reuse(V):
     # one workspace for every call, left all zero after each; V = 5003 takes

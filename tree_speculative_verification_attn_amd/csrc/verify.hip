@@ -632,13 +632,15 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         S = block_sum_or(acc, 0, s_red, s_redf, rs_no & 1, &unused);
         ++rs_no;
       }
-      // slice argmax < 2^20, flags in bits 24..26
+      // slice argmax in bits 0..23 (< 2^20; a slice of -inf entries has no
+      // index, 0x7FFFFFFF, cut to 0xFFFFFF so it cannot reach the flags),
+      // flags in bits 24..26
       if (t == 0) {
         uint64_t* p = bank + static_cast<size_t>(g) * kHdr;
         put_tagged(p + 0, tag, __float_as_uint(M));
         put_tagged(p + 1, tag, lo32(S));
         put_tagged(p + 2, tag, hi32(S));
-        put_tagged(p + 3, tag, static_cast<uint32_t>(A) | (static_cast<uint32_t>(F) << 24));
+        put_tagged(p + 3, tag, (static_cast<uint32_t>(A) & 0xFFFFFFu) | (static_cast<uint32_t>(F) << 24));
       }
     } else {
       // ---- residual after rejecting the child whose draft row is in qv ----
