@@ -202,8 +202,11 @@ tv_status tree_mask_attn_verify(tv_dtype dt, int B, int N, int H, int D, float s
  *                 counters and values the workgroups of one request exchange.
  *                 Calls that overlap in time must not share a workspace.
  * Work split: up to V = 16384 one workgroup walks a request.  Above, each
- * request is walked by ceil(V / 2048) workgroups that exchange values through
- * the workspace and so must be resident at the same time.  They are started
+ * request is walked by ceil(V / (256 E)) workgroups that exchange values
+ * through the workspace and so must be resident at the same time; E = 4, 8 or
+ * 16 vocabulary entries per thread (greedy: 8), chosen per call from B, V and
+ * the device's compute unit count (one workgroup per compute unit when it
+ * fits).  They are started
  * by ordinary launches in batches of requests sized so that every workgroup
  * of a batch fits on the device at once (by the occupancy the device reports
  * for the kernel); that residency is not guaranteed when other work occupies
@@ -280,8 +283,9 @@ tv_status tree_verify_mss(int B, int N, int V, int R, const float* target_logits
  * made while `stream` is being captured also records the fill in the graph,
  * and the next call outside a capture fills again.
  * Errors: those of tree_verify_mss (without TV_EWORKSPACE), TV_ESCRATCH when
- * tree_verify_workspace(B, N, V) exceeds TV_NOALLOC_SCRATCH_BYTES (about 1800
- * requests at V = 32000), TV_EHIP when the array's address cannot be found.
+ * tree_verify_workspace(B, N, V) exceeds TV_NOALLOC_SCRATCH_BYTES (1260
+ * requests at V = 32000, 123 at V = 2^20), TV_EHIP when the array's address
+ * cannot be found.
  */
 tv_status tree_verify_mss_noalloc(int B, int N, int V, int R, const float* target_logits,
                                   const float* ssm_probs, const int32_t* q_row, const int32_t* token,

@@ -109,10 +109,12 @@ def test_host_argument_checks(L):
     assert noalloc(N=65) == TV_ETOOBIG
     assert noalloc(logits=False) == TV_EINVAL
     assert noalloc(B=0) == TV_OK
-    # the fixed scratch holds 1820 requests' exchange words at V = 32000
-    assert L.tree_verify_workspace(1820, 5, 32000) <= tv_pkg.TV_NOALLOC_SCRATCH_BYTES
-    assert noalloc(B=1821, V=32000) == TV_ESCRATCH
-    assert noalloc(B=200, V=1 << 20) == TV_ESCRATCH
+    # the fixed scratch holds 1260 requests' exchange words at V = 32000, 123 at V = 2^20
+    assert L.tree_verify_workspace(1260, 5, 32000) <= tv_pkg.TV_NOALLOC_SCRATCH_BYTES
+    assert L.tree_verify_workspace(1261, 5, 32000) > tv_pkg.TV_NOALLOC_SCRATCH_BYTES
+    assert noalloc(B=1261, V=32000) == TV_ESCRATCH
+    assert L.tree_verify_workspace(123, 5, 1 << 20) <= tv_pkg.TV_NOALLOC_SCRATCH_BYTES
+    assert noalloc(B=124, V=1 << 20) == TV_ESCRATCH
     assert L.kv_commit_accepted(5, 2, 5, 2, 128, _p(), _p(), 10, 16, _p(), 4, _p(), _p(), _p(), _p(),
                                 None) == TV_EDTYPE
     assert L.kv_commit_accepted(1, 2, 65, 2, 128, _p(), _p(), 10, 16, _p(), 4, _p(), _p(), _p(), _p(),

@@ -375,12 +375,36 @@ def test_verify_sliced_vocab(V):
         assert int(run.ws_v.count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("B,V", [(6, 40000), (12, 40000), (24, 40000), (40, 40000), (24, 40001), (12, 33001)])
+def test_verify_slice_widths(B, V):
+    # The sliced MSS and naive walks pick 4, 8 or 16 entries per thread per
+    # call (greedy keeps 8): on a 256-CU device, B = 6, 12 and 24 at
+    # V = 40000 take 4, 8 and 16 (each the smallest width that gives every
+    # workgroup a CU of its own) and B = 40 takes 16 over two launches.
+    # V = 40001 and 33001 take the scalar loads.
+    w = synth.make_workload(2, B=B, L=20, H=1, V=V)
+    _print_case("verify slice widths", B, V)
+    run = DeviceRun(w).mask().greedy()
+    torch.cuda.synchronize()
+    _check_greedy(run)
+    run = DeviceRun(w).mask().mss()
+    torch.cuda.synchronize()
+    _check_mss(run, f"slice widths B={B} V={V}")
+    assert int(run.ws_v.count_nonzero()) == 0
+    run = DeviceRun(w).mask().naive()
+    torch.cuda.synchronize()
+    ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [0] * w.B, w.seed, w.offset)
+    exact, excused, bad = compare_naive(run, ref)
+    assert not bad, bad
+    assert int(run.ws_v.count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("B", [6, 24])
 def test_verify_rows_with_empty_slices(B):
     # Rows whose entries are -inf over whole workgroup slices (as top-k or
     # top-p filtering leaves them): such a slice has no argmax, and its
-    # missing index must not be read as a NaN or +inf flag (2048-entry
-    # slices; the bands below hold several).
+    # missing index must not be read as a NaN or +inf flag.  B = 6 takes 4
+    # entries per thread (1024-entry slices), B = 24 takes 16 (4096).
     w = synth.make_workload(2, B=B, L=20, H=1, V=40000, seed=5)
     w.token = (w.token % 4096).astype(w.token.dtype)     # tokens below 4096 stay finite
     tl = w.target_logits.copy()

@@ -84,7 +84,7 @@ def test_noalloc_after_a_timed_out_walk():
 
 def test_noalloc_rejects_more_than_the_scratch():
     _case("noalloc: oversize request count")
-    B, N, V = 1821, 4, 32000
+    B, N, V = 1261, 4, 32000
     assert tv.tree_verify_workspace(B, N, V) > tv.TV_NOALLOC_SCRATCH_BYTES
     tl = torch.zeros((B, N + 1, V), dtype=torch.float32, device=DEV)
     sp = torch.zeros((B, 1, V), dtype=torch.float32, device=DEV)

@@ -9,9 +9,10 @@
 // Work decomposition.  The walk over a request's tree is sequential, but each
 // of its steps touches a whole vocabulary row (32K-50K floats): the target
 // statistics of the node reached, the residual after a rejection, the final
-// inverse-CDF sample.  One request therefore gets G = ceil(V / 2048)
-// workgroups that run at the same time; workgroup g owns the vocabulary slice
-// [2048 g, 2048 g + 2048) and keeps its slice of the current distribution in
+// inverse-CDF sample.  One request therefore gets G = ceil(V / (256 E))
+// workgroups that run at the same time (E = 4, 8 or 16 entries per thread,
+// chosen per launch); workgroup g owns the vocabulary slice
+// [256 E g, 256 E (g + 1)) and keeps its slice of the current distribution in
 // registers.  Every workgroup of a request makes the same decisions (random
 // child, ratio test) from the same data, so only a few scalars per step cross
 // workgroups: slice max / sum / argmax when a node is entered, slice residual
@@ -50,9 +51,7 @@ namespace {
 constexpr int kOwnThreads = 256;                   // threads that own vocabulary entries
 constexpr int kCoThreads = kOwnThreads + 64;       // threads per workgroup: the owners and the poll wave
 constexpr int kPollWave = kOwnThreads / 64;        // stages the request and polls the exchanges
-constexpr int kElem = 8;                           // vocabulary entries per owner thread
-constexpr int kSlice = kOwnThreads * kElem;        // entries per workgroup
-constexpr int kMaxG = (1 << 20) / kSlice;          // workgroups per request at V = 2^20
+constexpr int kMaxG = 512;                         // workgroups per request (LDS arrays)
 constexpr int kHdr = 4;                            // header words per workgroup per exchange
 constexpr unsigned kSpinLimit = 1u << 22;          // polls of one word before giving up
 
@@ -73,8 +72,27 @@ struct WsLayout {
   size_t off_hdr, off_kid, total;
 };
 
+// Vocabulary entries per owner thread of the sliced MSS and naive walks (E =
+// 4, 8 or 16; greedy keeps 8) are chosen per launch in launch_walk: the
+// smallest E that puts every workgroup of the call on a compute unit of its
+// own, else the E that needs the fewest launches (ties: the larger E, fewer
+// workgroups per CU).  Two workgroups of a walk sharing a CU slow every pass
+// of their requests at least as much as twice the entries per thread do, and
+// fewer entries per thread shorten each pass.  G = slice_groups(V, E) <=
+// kMaxG is required (V <= 2^20 keeps E = 16 at most 256 workgroups per
+// request).
+int slice_groups(int V, int E) { return (V + kOwnThreads * E - 1) / (kOwnThreads * E); }
+
+// Workgroups per request the workspace is laid out for: the most any choice
+// above can give.
+int ws_groups(int V) {
+  for (int E = 4; E <= 16; E *= 2)
+    if (slice_groups(V, E) <= kMaxG) return slice_groups(V, E);
+  return slice_groups(V, 16);
+}
+
 WsLayout ws_layout(int B, int V) {
-  const size_t G = (static_cast<size_t>(V) + kSlice - 1) / kSlice;
+  const size_t G = static_cast<size_t>(ws_groups(V));
   WsLayout w;
   w.off_hdr = align256(static_cast<size_t>(B) * 64 * sizeof(uint32_t));
   w.off_kid = w.off_hdr + align256(static_cast<size_t>(B) * 2 * G * kHdr * sizeof(uint64_t));
@@ -250,8 +268,10 @@ __device__ SlotStage stage_slots(const WalkArgs& a, int b, int N, uint64_t cm, i
 // walk state lives in registers and a pass needs no barrier beyond those of
 // its workgroup reductions.
 // ---------------------------------------------------------------------------
-template <int MODE, bool VEC, bool COMMIT, bool MULTI = false>
+template <int MODE, bool VEC, bool COMMIT, bool MULTI, int E>
 __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
+  constexpr int kElem = E;                           // vocabulary entries per owner thread
+  constexpr int kSlice = kOwnThreads * kElem;        // entries per workgroup
   constexpr int NW = kCoThreads / 64;
   const int G = a.G;
   const int b = a.b0 + static_cast<int>(blockIdx.x) / G;
@@ -292,8 +312,8 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   __shared__ float own_s[kElem];
 
   static_assert(kElem % 4 == 0, "entries per thread");
-  // VEC (V a multiple of 4, rows 16-byte aligned): a thread owns 0, 4 or 8
-  // entries and loads them as float4s.  The choice is made at compile time: a
+  // VEC (V a multiple of 4, rows 16-byte aligned): a thread owns a multiple
+  // of 4 entries (up to kElem) and loads them as float4s.  The choice is made at compile time: a
   // run-time choice leaves both paths writing the same registers, and the
   // compiler then drains every load in flight before the float4 ones.
   // Entries past the vocabulary (and all of the poll wave's) get a neutral
@@ -1522,54 +1542,73 @@ tv_status check_verify_args(int B, int N, int V) {
   return TV_OK;
 }
 
-// Workgroups of the walk kernel that fit on the device at once (cached per
-// device and mode: it depends only on the kernel and the device).
 // kernel variant: 0 greedy, 1 MSS, 2 naive, 3 MSS + commit, 4 MSS over proposals
-template <bool VEC>
+template <bool VEC, int E>
 const void* walk_kernel_of(int variant) {
-  if (variant == 4) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, false, true>);
-  if (variant == 3) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, true>);
-  if (variant == MODE_MSS) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, false>);
-  if (variant == MODE_NAIVE) return reinterpret_cast<const void*>(walk_kernel<MODE_NAIVE, VEC, false>);
-  return reinterpret_cast<const void*>(walk_kernel<MODE_GREEDY, VEC, false>);
+  if (variant == 4) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, false, true, E>);
+  if (variant == 3) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, true, false, E>);
+  if (variant == MODE_MSS) return reinterpret_cast<const void*>(walk_kernel<MODE_MSS, VEC, false, false, E>);
+  if (variant == MODE_NAIVE) return reinterpret_cast<const void*>(walk_kernel<MODE_NAIVE, VEC, false, false, E>);
+  return reinterpret_cast<const void*>(walk_kernel<MODE_GREEDY, VEC, false, false, E>);
+}
+
+int elem_index(int E) { return E == 4 ? 0 : (E == 8 ? 1 : 2); }
+
+// Compute units of device dev (cached per device).
+int device_cus(int dev) {
+  static std::atomic<int> cache[64];
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
+  if (cached) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 // Workgroups of a walk variant resident at once on device dev (cached per
-// device; every thread that fills an entry computes the same value, so
-// relaxed atomics suffice).
-int walk_capacity(int dev, int variant, bool vec) {
-  static std::atomic<int> cache[2][5][64];
+// device, variant and slice width; every thread that fills an entry computes
+// the same value, so relaxed atomics suffice).
+int walk_capacity(int dev, int variant, bool vec, int E) {
+  static std::atomic<int> cache[2][5][3][64];
+  const int ei = elem_index(E);
   const bool cached = dev >= 0 && dev < 64 && variant >= 0 && variant < 5;
   if (cached) {
-    const int c = cache[vec][variant][dev].load(std::memory_order_relaxed);
+    const int c = cache[vec][variant][ei][dev].load(std::memory_order_relaxed);
     if (c > 0) return c;
   }
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const void* fn = vec ? walk_kernel_of<true>(variant) : walk_kernel_of<false>(variant);
+  const int cus = device_cus(dev);
+  if (cus <= 0) return 0;
+  const void* fn = ei == 0 ? (vec ? walk_kernel_of<true, 4>(variant) : walk_kernel_of<false, 4>(variant))
+                 : ei == 1 ? (vec ? walk_kernel_of<true, 8>(variant) : walk_kernel_of<false, 8>(variant))
+                           : (vec ? walk_kernel_of<true, 16>(variant) : walk_kernel_of<false, 16>(variant));
+  int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kCoThreads, 0) != hipSuccess) return 0;
   const int cap = cus * std::max(1, per_cu);
-  if (cached) cache[vec][variant][dev].store(cap, std::memory_order_relaxed);
+  if (cached) cache[vec][variant][ei][dev].store(cap, std::memory_order_relaxed);
   return cap;
 }
 
-template <bool VEC>
-void launch_sliced_vec(const WalkArgs& a, int grid, hipStream_t stream) {
+template <bool VEC, int E>
+void launch_sliced_ve(const WalkArgs& a, int grid, hipStream_t stream) {
   if (a.mode == MODE_MSS && a.multi)
-    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, false, true>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, false, true, E>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else if (a.mode == MODE_MSS && a.commit)
-    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, true>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, true, false, E>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else if (a.mode == MODE_MSS)
-    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, false>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_MSS, VEC, false, false, E>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else if (a.mode == MODE_NAIVE)
-    hipLaunchKernelGGL((walk_kernel<MODE_NAIVE, VEC, false>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_NAIVE, VEC, false, false, E>), dim3(grid), dim3(kCoThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((walk_kernel<MODE_GREEDY, VEC, false>), dim3(grid), dim3(kCoThreads), 0, stream, a);
+    hipLaunchKernelGGL((walk_kernel<MODE_GREEDY, VEC, false, false, E>), dim3(grid), dim3(kCoThreads), 0, stream, a);
 }
 
-void launch_sliced(const WalkArgs& a, int grid, bool vec, hipStream_t stream) {
-  if (vec) launch_sliced_vec<true>(a, grid, stream);
-  else launch_sliced_vec<false>(a, grid, stream);
+void launch_sliced(const WalkArgs& a, int grid, bool vec, int E, hipStream_t stream) {
+  if (E == 4) vec ? launch_sliced_ve<true, 4>(a, grid, stream) : launch_sliced_ve<false, 4>(a, grid, stream);
+  else if (E == 8) vec ? launch_sliced_ve<true, 8>(a, grid, stream) : launch_sliced_ve<false, 8>(a, grid, stream);
+  else vec ? launch_sliced_ve<true, 16>(a, grid, stream) : launch_sliced_ve<false, 16>(a, grid, stream);
 }
 
 template <int E, int MODE, bool COMMIT = false, bool MULTI = false>
@@ -1601,18 +1640,43 @@ tv_status launch_walk(WalkArgs a, int B, hipStream_t stream) {
     else launch_row<32>(a, B, vec, stream);
     return tv::launch_status();
   }
-  const int G = a.G;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TV_EHIP;
+  const int cus = device_cus(dev);
+  if (cus <= 0) return TV_EHIP;
   const int variant = a.mode != MODE_MSS ? a.mode : (a.multi ? 4 : (a.commit ? 3 : MODE_MSS));
-  const int capacity = walk_capacity(dev, variant, vec);
+  // Greedy passes are light (a max and an argmax, no normaliser), so its
+  // walk keeps 8 entries per thread: measured, 4 or 16 only made it slower.
+  int E = a.mode == MODE_GREEDY ? 8 : 0;
+  for (int e = 4; e <= 16 && !E; e *= 2) {
+    const int g = slice_groups(a.V, e);
+    if (g <= kMaxG && static_cast<long>(B) * g <= cus) E = e;
+  }
+  if (!E) {
+    long best = 0;
+    for (int e = 16; e >= 4; e /= 2) {
+      const int g = slice_groups(a.V, e);
+      const int cap = walk_capacity(dev, variant, vec, e);
+      if (cap <= 0) return TV_EHIP;
+      if (g > kMaxG || g > cap) continue;
+      const long per = cap / g, launches = (B + per - 1) / per;
+      if (!E || launches < best) {
+        E = e;
+        best = launches;
+      }
+    }
+    if (!E) return TV_EINVAL;
+  }
+  const int G = slice_groups(a.V, E);            // <= ws_groups(V): the workspace holds it
+  a.G = G;
+  const int capacity = walk_capacity(dev, variant, vec, E);
   if (capacity <= 0) return TV_EHIP;
   if (G > capacity) return TV_EINVAL;
   const int per_launch = capacity / G;
   for (int b0 = 0; b0 < B; b0 += per_launch) {
     const int nb = std::min(per_launch, B - b0);
     a.b0 = b0;
-    launch_sliced(a, nb * G, vec, stream);
+    launch_sliced(a, nb * G, vec, E, stream);
     if (hipGetLastError() != hipSuccess) return TV_EHIP;
   }
   return TV_OK;
@@ -1638,7 +1702,7 @@ WalkArgs make_args(int mode, int N, int V, int R, void* workspace, int B) {
   a.N = N;
   a.V = V;
   a.R = R;
-  a.G = (V + kSlice - 1) / kSlice;
+  a.G = 0;                  // set by launch_walk with the slice width
   const WsLayout w = ws_layout(B, V);
   uint8_t* p = static_cast<uint8_t*>(workspace);
   a.done = reinterpret_cast<uint32_t*>(p);
