@@ -10,7 +10,9 @@ The headline workload is the LLaMA-65B-shaped layer, the largest of the
 five that runs on one GPU (bf16, 32 requests x 64 heads x 128 dims, ragged
 prefixes of 512..4096 tokens in a paged cache, random 64-node trees, fp32
 logits over a 32000-token vocabulary).  The LLaMA-7B, OPT-30B and
-long-context layers are measured the same way and reported beside it.
+long-context layers are measured the same way and reported beside it, and so
+is one GPU's share of the LLaMA-65B layer under 8-way tensor parallelism
+over heads (8 of the 64 heads, every request).
 
 Inputs stay resident in HBM.  The timed loop rotates over several copies of
 the inputs whose total exceeds twice the 256 MB Infinity Cache, so each step
@@ -122,6 +124,13 @@ def main():
             note(f"measured {wc.name}")
             del wc
             torch.cuda.empty_cache()
+        # one GPU's share of the LLaMA-65B layer under 8-way tensor
+        # parallelism over heads: every request, 8 of the 64 heads
+        wc = synth.make_workload(4, H=8)
+        others["llama65b_layer_tp8_shard"] = run_workload(torch, tv, wc, args, full=False)
+        note("measured llama65b_layer_tp8_shard")
+        del wc
+        torch.cuda.empty_cache()
         res["other_workloads"] = others
     if cpu is not None:
         for leg in ("one_core", "all_cores"):
