@@ -132,8 +132,8 @@ tv_status tree_build_mask(int B, int N, const int32_t* parent, uint64_t* anc,
  *                 the call may set TV_REQ_KV_CAPACITY or TV_REQ_BAD_BLOCK
  *                 (then that request's output is unspecified)
  *   out           [B][N][H][D]; every key is summed in an order fixed by
- *                 the shapes alone, so repeated calls on the same inputs give
- *                 the same bits
+ *                 the shapes and the device (never by timing), so repeated
+ *                 calls on the same inputs and device give the same bits
  *   workspace     ws_bytes >= tree_attn_verify_workspace(...) bytes of device
  *                 memory for per-chunk partial results (may be null when that
  *                 size is 0); contents on entry do not matter.  Calls that
