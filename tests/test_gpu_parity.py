@@ -399,6 +399,26 @@ def test_verify_slice_widths(B, V):
     assert int(run.ws_v.count_nonzero()) == 0
 
 
+def test_verify_largest_vocabulary():
+    # V = 2^20, the largest vocabulary the boundary accepts: 512 workgroups
+    # of 8 entries per thread (greedy) or 256 of 16 (MSS, naive) per request,
+    # one request per launch
+    w = synth.make_workload(2, B=2, L=20, H=1, V=1 << 20)
+    _print_case("verify largest vocabulary", w.V)
+    run = DeviceRun(w).mask().greedy()
+    torch.cuda.synchronize()
+    _check_greedy(run)
+    run = DeviceRun(w).mask().mss()
+    torch.cuda.synchronize()
+    _check_mss(run, "V = 2^20")
+    assert int(run.ws_v.count_nonzero()) == 0
+    run = DeviceRun(w).mask().naive()
+    torch.cuda.synchronize()
+    ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [0] * w.B, w.seed, w.offset)
+    exact, excused, bad = compare_naive(run, ref)
+    assert not bad, bad
+
+
 @pytest.mark.parametrize("B", [6, 24])
 def test_verify_rows_with_empty_slices(B):
     # Rows whose entries are -inf over whole workgroup slices (as top-k or
