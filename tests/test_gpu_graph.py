@@ -85,7 +85,10 @@ def _same(name, got, ref, w):
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("cfg,kw", [(2, dict(B=4, L=300, H=8, V=32000)),
                                     (3, dict(B=3, L=77, H=3, V=50272)),
-                                    (4, dict(B=6, H=2, V=20000))])
+                                    (4, dict(B=6, H=2, V=20000)),
+                                    # 960 (request, head) items: the single-group attention
+                                    # kernel that ranks requests by prefix length
+                                    (4, dict(B=40, H=24, V=20000))])
 def test_graph_replay_matches_eager(cfg, kw, fused):
     w = synth.make_workload(cfg, **kw)
     print("[case] graph replay", cfg, kw, "three launches" if fused else "five calls", flush=True)
