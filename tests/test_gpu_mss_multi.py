@@ -19,6 +19,9 @@ SHAPES = {
     "row_c1": (1, dict()),
     "sliced_c3": (3, dict(B=3, L=20, H=1, V=20000)),
     "sliced_c3_scalar": (3, dict(B=3, L=20, H=1, V=17003)),
+    # on a 256-CU device these take 8 and 16 vocabulary entries per thread
+    "sliced_c3_w8": (3, dict(B=12, L=20, H=1, V=40000)),
+    "sliced_c3_w16": (3, dict(B=24, L=20, H=1, V=40000)),
 }
 
 

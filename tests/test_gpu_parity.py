@@ -391,6 +391,13 @@ def test_verify_slice_widths(B, V):
     torch.cuda.synchronize()
     _check_mss(run, f"slice widths B={B} V={V}")
     assert int(run.ws_v.count_nonzero()) == 0
+    # MSS with the compaction: the same path, and the prefix grown by it
+    fused = DeviceRun(w).mask().mss_commit()
+    torch.cuda.synchronize()
+    for name in ("m_acc", "m_num", "m_bonus", "m_rounds", "status"):
+        assert torch.equal(getattr(fused, name), getattr(run, name)), name
+    num = run.m_num.cpu().numpy()
+    assert np.array_equal(fused.pl.cpu().numpy(), w.prefix_len + np.maximum(num, 0))
     run = DeviceRun(w).mask().naive()
     torch.cuda.synchronize()
     ref = o_verify.verify_naive(w.parent, w.token, w.target_logits, [0] * w.B, w.seed, w.offset)
