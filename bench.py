@@ -115,12 +115,16 @@ def main():
     if res is None:                       # --profile-only
         return
     note(f"measured {w.name}")
-    mss_out = res.pop("_mss_out")
+    replays = {w.name: (w, res.pop("_mss_out"))} if cpu is not None else {}
+    res.pop("_mss_out", None)
     if not args.no_others and args.config is None:
         others = {}
         for c in (2, 3, 5):
             wc = synth.make_config(c)
             others[wc.name] = run_workload(torch, tv, wc, args, full=False)
+            out = others[wc.name].pop("_mss_out")
+            if cpu is not None:
+                replays[wc.name] = (wc, out)
             note(f"measured {wc.name}")
             del wc
             torch.cuda.empty_cache()
@@ -128,14 +132,19 @@ def main():
         # parallelism over heads: every request, 8 of the 64 heads
         wc = synth.make_workload(4, H=8)
         others["llama65b_layer_tp8_shard"] = run_workload(torch, tv, wc, args, full=False)
+        others["llama65b_layer_tp8_shard"].pop("_mss_out")
         note("measured llama65b_layer_tp8_shard")
         del wc
         torch.cuda.empty_cache()
         res["other_workloads"] = others
+    res["roofline"]["measured_copy_ceiling_GBps"] = copy_ceiling(torch)
+    res["roofline"]["frac_of_copy_ceiling"] = round(res["roofline"]["achieved"] /
+                                                    res["roofline"]["measured_copy_ceiling_GBps"], 4)
     if cpu is not None:
         for leg in ("one_core", "all_cores"):
             cpu[leg]["gpu_over_cpu"] = round(res["value"] / cpu[leg]["value"], 1)
-        cpu["mss_replay"] = mss_replay(w, mss_out)
+        # the oracle replays each workload's MSS call (after every GPU timing)
+        cpu["mss_replay"] = {name: mss_replay(wr, out) for name, (wr, out) in replays.items()}
         res["cpu_baseline"] = cpu
     print(json.dumps(res))
 
@@ -308,6 +317,14 @@ def run_workload(torch, tv, w, args, full):
     mss_gbs = l_bytes / (t_mss * 1e-3) / 1e9
     value = B * N / (ms_per_step * 1e-3)
 
+    # the MSS call the oracle replays: input copy 0, the workload's own
+    # Philox key and offset, every request live
+    st0 = torch.zeros((B,), dtype=torch.int32, device=dev)
+    tv.tree_verify_mss(copies[0]["tl"], copies[0]["sp"], qr, token, child, st0, w.seed, w.offset, m_acc, m_num,
+                       m_bonus, m_rounds, ws_v)
+    torch.cuda.synchronize()
+    mss_out = {k: t.cpu().numpy() for k, t in (("accepted", m_acc), ("num_accepted", m_num), ("bonus", m_bonus),
+                                               ("rounds", m_rounds), ("status", st0))}
     if not full:
         del copies
         return {"workload": f"{w.name}: B={B} H={H} D={D} L={_lens(w)} N={N} V={V}",
@@ -321,7 +338,7 @@ def run_workload(torch, tv, w, args, full):
                         "frac": round(mss_gbs / HBM_PEAK_GBS, 4), "logit_bytes": l_bytes},
                 "greedy_ms_per_launch": round(t_greedy, 5),
                 "tree_attn_plus_mss_tokens_per_s": round(B * N / ((t_attn + t_mss) * 1e-3), 1),
-                "input_copies_rotated": n_copies}
+                "input_copies_rotated": n_copies, "_mss_out": mss_out}
 
     res = {
         "metric": METRIC,
@@ -361,14 +378,7 @@ def run_workload(torch, tv, w, args, full):
                                         token, qr, bt, m_acc, m_num, m_bonus, m_rounds, ws_v, t_attn, t_attn_only,
                                         t_mss, variants)
     res["tree_vs_sequence"] = tree_vs_sequence(torch, tv, w, copies, bt, t_attn_only, stream)
-    # the MSS call the oracle replays: input copy 0, the workload's own
-    # Philox key and offset, every request live
-    st0 = torch.zeros((B,), dtype=torch.int32, device=dev)
-    tv.tree_verify_mss(copies[0]["tl"], copies[0]["sp"], qr, token, child, st0, w.seed, w.offset, m_acc, m_num,
-                       m_bonus, m_rounds, ws_v)
-    torch.cuda.synchronize()
-    res["_mss_out"] = {k: t.cpu().numpy() for k, t in (("accepted", m_acc), ("num_accepted", m_num),
-                                                        ("bonus", m_bonus), ("rounds", m_rounds), ("status", st0))}
+    res["_mss_out"] = mss_out
     del copies
     torch.cuda.empty_cache()
     return res
@@ -546,6 +556,29 @@ def tree_vs_sequence(torch, tv, w, copies, bt, t_tree, stream, reps=10):
             "tree_speedup": round(t_seq / t_tree, 3), "tree_kv_bytes": tree_kv,
             "sequence_kv_bytes": sbs[0].kv_bytes,
             "kernel": "tree_attn_verify for both; paths share the physical prefix blocks"}
+
+
+def copy_ceiling(torch, mib=1024, reps=20):
+    """GB/s of a plain device-to-device copy of `mib` MiB (bytes read plus
+    bytes written over the time), timed with HIP events on the current
+    stream: the practical HBM ceiling the roofline fraction is read against."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
 
 
 def copy_calibration(torch, mib):
