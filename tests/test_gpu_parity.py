@@ -172,18 +172,21 @@ def test_attention_status_paths():
     assert run2.status.cpu().numpy()[2] == 7
 
 
-@pytest.mark.parametrize("B,H", [(40, 2), (70, 2), (40, 24), (70, 12), (300, 3)])
+@pytest.mark.parametrize("B,H,D", [(40, 2, 128), (70, 2, 128), (40, 24, 128), (70, 12, 128), (300, 3, 128),
+                                   (256, 3, 128), (64, 24, 64)])
 @pytest.mark.parametrize("fused", [False, True])
-def test_attention_ragged_order(B, H, fused):
+def test_attention_ragged_order(B, H, D, fused):
     """Ragged prefixes in one batch (B on both sides of 64), with equal
     lengths, an empty prefix, the longest prefix repeated, a request skipped
     upstream and one past the cache's capacity; every (request, head) output
-    is checked.  On a 256-CU device, 40 x 24 and 70 x 12 (request, head)
-    items are at least three rounds of workgroups, which runs the
-    single-group kernel that takes requests longest first (ties by index);
-    300 requests are more than it ranks, and the others fewer items."""
-    _print_case("attention ragged order", B, H, "fused" if fused else "plain")
-    w = synth.make_workload(dict(name="ragged", B=B, H=H, D=128, V=50, dtype="bf16", tree=("expand", (2, 2, 1)),
+    is checked.  On a 256-CU device, 40 x 24, 70 x 12 and 256 x 3 (request,
+    head) items at head dim 128, and 64 x 24 at head dim 64 (two default
+    workgroups per CU there), are at least three rounds of workgroups, which
+    runs the single-group kernel that takes requests longest first (ties by
+    index; 256 requests is the most it ranks); 300 requests are more than it
+    ranks, and the others fewer items."""
+    _print_case("attention ragged order", B, H, D, "fused" if fused else "plain")
+    w = synth.make_workload(dict(name="ragged", B=B, H=H, D=D, V=50, dtype="bf16", tree=("expand", (2, 2, 1)),
                                  L=("uniform", 0, 300), sig_t=1.0, sig_s=1.0), 91)
     pl = w.prefix_len.copy()
     pl[3] = pl[7] = pl[11] = pl[5]          # ties: rank by request index
