@@ -363,8 +363,15 @@ tv_status tree_verify_mss_multi(int B, int N, int S, int V, int R, const float* 
  *                      block_size, block_table, max_blocks, prefix_len,
  *                      accepted, num_accepted, status, stream);
  * on the same arguments (outputs, status codes, cache contents, prefix
- * lengths).  The workgroup of a request that writes the accepted path also
- * moves its rows, which saves the second launch and its start-up round trips.
+ * lengths).  The workgroups that walk a request also move its rows, each a
+ * block of heads (all of them when one workgroup walks the request), which
+ * saves the second launch and its start-up round trips.  With several
+ * workgroups per request, the one that writes the request's outputs decides
+ * whether the move is made and grows the prefix length only after every
+ * other workgroup has reported its heads moved; if a report does not come
+ * within the wait bound, the request ends as TV_REQ_TIMEOUT with its prefix
+ * length unchanged, and only then may the K/V rows of its tree's slots
+ * [L, L + N) be partly compacted (rows outside them never change).
  * The first 18 arguments are tree_verify_mss's, the rest kv_commit_accepted's
  * (N, B and accepted / num_accepted / status are shared); ownership,
  * workspace rules and errors are the union of theirs.

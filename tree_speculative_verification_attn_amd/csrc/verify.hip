@@ -116,7 +116,9 @@ struct WalkArgs {
   int32_t* bonus;
   int32_t* rounds;
   uint32_t* done;            // [B][64]: word 0 counts the workgroups that left; words 2-3 hold
-                            // MSS's sampled token, tagged, from the slice that found it
+                            // MSS's sampled token, tagged, from the slice that found it;
+                            // with the commit, words 4-5 workgroup 0's tagged decision to
+                            // move and word 6 the other workgroups' reports
   uint64_t* hdr;
   uint64_t* kid;
   bool commit;              // MSS: also compact the accepted path in the KV cache
@@ -306,6 +308,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   __shared__ double s_gt[NW][kMaxG];             // slice totals of the current distribution (per wave)
   __shared__ double s_scan[NW];
   __shared__ int s_status0, s_timeout, s_found, s_last, s_xs;
+  __shared__ int s_dec, s_acks;                  // COMMIT: workgroup 0's decision / the others' reports
   __shared__ int s_L;                            // COMMIT: the request's prefix length
   __shared__ tv::CommitLds s_mv;                 // COMMIT: the move's block offsets
   __shared__ int s_tblk[tv::kMaxTreeBlocks];     // COMMIT: block ids covering the tree's slots
@@ -367,17 +370,17 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
       s_status0 = st;
       s_timeout = 0;
       // nothing writes the prefix length before the move at the end
-      if constexpr (COMMIT) s_L = g == 0 ? a.kv.prefix_len[b] : 0;
+      // nothing writes the prefix length before every workgroup has moved its heads
+      if constexpr (COMMIT) s_L = a.kv.prefix_len[b];
     }
   }
   __syncthreads();
 
-  // COMMIT: the poll wave of workgroup 0 fetches the block ids of the tree's
-  // slots now; the loads land long before its first poll waits (in issue
-  // order) for anything
+  // COMMIT: the poll wave fetches the block ids of the tree's slots now; the
+  // loads land long before its first poll waits (in issue order) for anything
   int tblk = 0;
   if constexpr (COMMIT)
-    if (g == 0 && wave == kPollWave && lane < tv::kMaxTreeBlocks) tblk = tv::tree_block_id(a.kv, b, N, s_L, lane);
+    if (wave == kPollWave && lane < tv::kMaxTreeBlocks) tblk = tv::tree_block_id(a.kv, b, N, s_L, lane);
 
   // ---- walk state: registers, identical in every thread of the request ----
   int status = s_status0;
@@ -884,7 +887,7 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     }
   }
   if constexpr (COMMIT)
-    if (g == 0 && wave == kPollWave && lane < tv::kMaxTreeBlocks) s_tblk[lane] = tblk;
+    if (wave == kPollWave && lane < tv::kMaxTreeBlocks) s_tblk[lane] = tblk;
   __syncthreads();
   const bool ok = status == TV_REQ_OK && !s_timeout;
 
@@ -903,39 +906,95 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
   int stt = status;
   if (stt == TV_REQ_OK && s_timeout) stt = TV_REQ_TIMEOUT;
 
-  // ---- verify + commit: workgroup 0 also compacts the accepted path,
-  // exactly as kv_commit_accepted would after this call.  Its checks and the
-  // first batch of row loads go out now, so the loads are in flight while
-  // the results are written and the workgroups sign off below. ----
+  // ---- verify + commit: every workgroup compacts the accepted path of its
+  // own block of heads, [g H / G, (g + 1) H / G), exactly as
+  // kv_commit_accepted would after this call.  Heads occupy disjoint rows,
+  // so the workgroups' moves never meet; within one, the batches keep the
+  // order kv_move.h describes.  Workgroup 0 decides whether the move is made
+  // (its walk, the checks and the final token's hand-over) and posts the
+  // decision; the others move only on it and report, and workgroup 0 grows
+  // the prefix length only when every report says moved.  Otherwise the
+  // request times out with its prefix length unchanged (the rows of its
+  // tree's slots may then be partly compacted).  Each workgroup's checks and
+  // first batch of row loads go out now, so the loads are in flight during
+  // the hand-over. ----
   tv::MovePlan plan;
   int mres = -1;                   // TV_REQ_OK: move; -1: nothing to do; else the status to store
+  int mv_begin = 0;                // this workgroup's first item of the move
   uint4 mbuf[kMoveChunks];
+  uint64_t* const dword = reinterpret_cast<uint64_t*>(done + 4);   // COMMIT: the decision
+  uint32_t* const acks = done + 6;                                  // COMMIT: the reports
   if constexpr (COMMIT) {
-    if (g == 0) {
-      mres = tv::move_prepare<kCoThreads, kMoveChunks, true>(a.kv, b, N, stt, s_L, ok ? k : -1, s_acc, false, s_mv,
-                                                              s_tblk, plan);
-      if (mres == TV_REQ_OK) tv::move_load<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, 0, mbuf);
+    mres = tv::move_prepare<kCoThreads, kMoveChunks, true>(a.kv, b, N, stt, s_L, ok ? k : -1, s_acc, false, s_mv,
+                                                            s_tblk, plan);
+    if (mres == TV_REQ_OK) {
+      mv_begin = (g * a.kv.H) / G * plan.per_head;
+      plan.total = ((g + 1) * a.kv.H) / G * plan.per_head;
+      if (mv_begin < plan.total) tv::move_load<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, mv_begin, mbuf);
     }
   }
 
-  // ---- results: workgroup 0 writes the path, the bonus and the status.
-  // MSS's token from another slice arrives in the tagged word; if it does not
-  // within the wait bound, the request times out like any other wait (no
-  // output, no move), so the outputs always come from one decision. ----
-  if (g == 0) {
-    if (final_draw && owner != 0) {
-      if (t == 0) {
+  // ---- MSS's token from another slice arrives in the tagged word; if it
+  // does not within the wait bound, the request times out like any other
+  // wait (no output, no move), so the outputs always come from one
+  // decision. ----
+  if (g == 0 && final_draw && owner != 0) {
+    if (t == 0) {
+      uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
+      s_xs = take_tagged<1>(xword, 1u, v, a.spin_limit) ? static_cast<int>(v[0]) : -1;
+    }
+    __syncthreads();
+    if (s_xs >= 0) {
+      bonus = s_xs;
+    } else {
+      stt = TV_REQ_TIMEOUT;
+      mres = -1;
+    }
+  }
+
+  if constexpr (COMMIT) {
+    if (g == 0 && t == 0) put_tagged(dword, 1u, mres == TV_REQ_OK ? 1u : 0u);
+    if (g != 0 && t == 0) {
+      int dec = 0;
+      if (mres == TV_REQ_OK) {
         uint32_t v[kHdr] = {0u, 0u, 0u, 0u};
-        s_xs = take_tagged<1>(xword, 1u, v, a.spin_limit) ? static_cast<int>(v[0]) : -1;
+        dec = take_tagged<1>(dword, 1u, v, a.spin_limit) ? static_cast<int>(v[0]) : 0;
+      }
+      s_dec = dec;
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the first batch have completed
+    __syncthreads();
+    const bool go = mres == TV_REQ_OK && (g == 0 || s_dec == 1);
+    if (go && mv_begin < plan.total) {
+      tv::move_store<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, mv_begin, mbuf);
+      tv::move_rest<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, mv_begin + plan.step);
+    }
+    if (g != 0) {
+      if (t == 0) __hip_atomic_fetch_add(acks, go ? 1u : 0x10000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (go) {
+      // every other workgroup's report: low half moved, high half not
+      if (t == 0) {
+        int all = 0;
+        for (unsigned polls = 0; polls < a.spin_limit; ++polls) {
+          const uint32_t x = __hip_atomic_load(acks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (static_cast<int>((x & 0xFFFFu) + (x >> 16)) >= G - 1) {
+            all = (x >> 16) == 0u ? 1 : 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        s_acks = all;
       }
       __syncthreads();
-      if (s_xs >= 0) {
-        bonus = s_xs;
-      } else {
+      if (!s_acks) {
         stt = TV_REQ_TIMEOUT;
         mres = -1;
       }
     }
+  }
+
+  // ---- results: workgroup 0 writes the path, the bonus and the status ----
+  if (g == 0) {
     if (t == 0) {
       if (stt != TV_REQ_OK) {
         a.status[b] = stt;
@@ -947,29 +1006,20 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
         a.bonus[b] = bonus;
         if (a.rounds) a.rounds[b] = rounds;
       }
+      if constexpr (COMMIT) {
+        if (mres == TV_REQ_OK) a.kv.prefix_len[b] = s_L + k;
+        else if (mres >= 0 && mres != stt) a.status[b] = mres;
+      }
     }
     const int kk = stt == TV_REQ_OK ? k : 0;
     for (int i = t; i < N; i += kCoThreads) a.accepted[static_cast<size_t>(b) * N + i] = i < kk ? s_acc[i] : -1;
   }
 
   // ---- leave the workspace zeroed: the last workgroup out clears it ----
-  __builtin_amdgcn_s_waitcnt(0);     // this thread's stores (and the move's first loads) have completed
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have completed
   __syncthreads();
   uint32_t prev = 0;
   if (t == 0) prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if constexpr (COMMIT) {
-    if (g == 0) {
-      if (mres == TV_REQ_OK) {
-        // every load of the first batch, in every thread, completed before
-        // the barrier above
-        tv::move_store<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, 0, mbuf);
-        tv::move_rest<kCoThreads, kMoveChunks>(a.kv, plan, s_mv, plan.step);
-        if (t == 0) a.kv.prefix_len[b] = s_L + k;
-      } else if (mres >= 0 && mres != stt && t == 0) {
-        a.status[b] = mres;
-      }
-    }
-  }
   if (t == 0) s_last = prev == static_cast<uint32_t>(G - 1);
   __syncthreads();
   if (s_last) {          // every workgroup has finished reading
@@ -978,6 +1028,10 @@ __global__ __launch_bounds__(kCoThreads) void walk_kernel(WalkArgs a) {
     if (t == 0) {
       st_u32(done, 0u);
       st_u64(xword, 0ull);
+      if constexpr (COMMIT) {
+        st_u64(dword, 0ull);
+        st_u32(acks, 0u);
+      }
     }
   }
 }
