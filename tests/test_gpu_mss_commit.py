@@ -66,6 +66,11 @@ CASES = {
     "sliced_c2_bf16": (2, dict(B=3, L=20, H=2, V=40000)),
     "sliced_c4_scalar_loads": (4, dict(B=2, H=2, V=33001)),
     "sliced_c3_f32": (3, dict(B=2, L=40, H=2, V=20000, dtype="f32")),
+    # the walking workgroups share the move by head: 13 heads over the 40
+    # workgroups of a request (most move none), and 37 heads over 10 (uneven
+    # blocks; 40 requests do not fit one workgroup per CU)
+    "sliced_heads_fewer_than_groups": (2, dict(B=3, L=30, H=13, V=40000)),
+    "sliced_heads_uneven_blocks": (2, dict(B=40, L=20, H=37, V=40000)),
 }
 
 
