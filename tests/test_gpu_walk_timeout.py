@@ -79,3 +79,44 @@ def test_normal_bound_after_timeouts():
     exact, excused, bad = compare_mss(run, ref)
     assert not bad and exact + excused == w.B
     assert int(run.ws_v.count_nonzero()) == 0
+
+
+def test_commit_without_every_report_times_out():
+    """The fused MSS + commit grows a request's prefix length only when every
+    walking workgroup reports its block of heads moved.  A report of "not
+    moved" is planted from the host for requests 0 and 2 (the reports word is
+    word 6 of the request's 256-byte line at the start of the workspace), so
+    workgroup 0 of those requests gives up once the count is complete, while
+    requests 1 and 3 commit as usual.  Checked: the planted requests report
+    TV_REQ_TIMEOUT with a skipped request's outputs and their prefix lengths
+    unchanged; every row of the caches is either as before or as the normal
+    call leaves it; the other requests equal the normal call; the workspace is
+    left all zero."""
+    _case("commit reports incomplete")
+    w = synth.make_workload(2, B=4, L=40, H=5, V=40000)
+    ref = DeviceRun(w).mask()
+    ref.mss_commit()
+    run = DeviceRun(w).mask()
+    torch.cuda.synchronize()
+    k0, v0, pl0 = _raw(run.k), _raw(run.v), run.pl.cpu().numpy()
+    words = run._ws_verify().view(torch.int32)
+    for b in (0, 2):
+        words[b * 64 + 6] = 0x10000
+    run.mss_commit()
+    torch.cuda.synchronize()
+    st_ref = ref.status.cpu().numpy()
+    assert list(st_ref) == [0] * 4
+    assert list(run.status.cpu().numpy()) == [TIMEOUT, 0, TIMEOUT, 0]
+    pl_ref = ref.pl.cpu().numpy()
+    assert (pl_ref[[0, 2]] > pl0[[0, 2]]).any(), "the case should grow a planted request's prefix"
+    assert np.array_equal(run.pl.cpu().numpy(), [pl0[0], pl_ref[1], pl0[2], pl_ref[3]])
+    for name in ("m_num", "m_bonus", "m_rounds"):
+        got, exp = getattr(run, name).cpu().numpy(), getattr(ref, name).cpu().numpy()
+        assert np.all(got[[0, 2]] == -1) and np.array_equal(got[[1, 3]], exp[[1, 3]]), name
+    acc, acc_ref = run.m_acc.cpu().numpy(), ref.m_acc.cpu().numpy()
+    assert np.all(acc[[0, 2]] == -1) and np.array_equal(acc[[1, 3]], acc_ref[[1, 3]])
+    for got, pre, exp in ((_raw(run.k), k0, _raw(ref.k)), (_raw(run.v), v0, _raw(ref.v))):
+        same_pre = np.all(got == pre, axis=(2, 3))
+        same_ref = np.all(got == exp, axis=(2, 3))
+        assert np.all(same_pre | same_ref), "a (block, head) slab is neither as before nor committed"
+    assert int(run.ws_v.count_nonzero()) == 0, "workspace not left zero"
