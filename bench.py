@@ -658,14 +658,23 @@ def _cpu_verify(reqs):
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family, model and
+    stepping numbers and clock (a virtual machine may report only a brand)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                       # the first processor's block is enough
+                key, _, val = line.partition(":")
+                info[key.strip()] = val.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    if "cpu MHz" in info:
+        ids.append(f"{float(info['cpu MHz']):.0f} MHz")
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def cpu_baseline(w, budget_s):
