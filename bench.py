@@ -87,7 +87,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the verification step shards by request with no exchange; see the design notes)",
+              "(this benchmark measures one GPU; attention shards by head and verification by request)",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration_mb or args.compare_sequence:
