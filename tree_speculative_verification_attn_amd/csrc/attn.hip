@@ -453,8 +453,11 @@ void attn_mfma_kernel(AttnArgs a) {
       const uint8_t* src = (which ? vg : kg) + static_cast<size_t>(blk) * blk_bytes + h * head_bytes +
                            static_cast<size_t>(row) * D * 2 + c16 * 16;
       const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + which * TILE + lt * 1024));
-      // lane i's 16 bytes land at M0 + 16 * i
-      asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds_addr) : "memory");
+      // lane i's 16 bytes land at M0 + 16 * i.  The K/V stream is read once:
+      // the non-temporal hint (nt) keeps it from displacing cached lines,
+      // which measured 5-11% faster launches than default caching (sc0 or
+      // sc1 alone changed nothing).
+      asm volatile("global_load_lds_dwordx4 %0, off nt" :: "v"(src), "{m0}"(lds_addr) : "memory");
     }
   };
 
