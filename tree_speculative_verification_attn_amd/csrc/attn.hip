@@ -729,7 +729,9 @@ void attn_mfma_kernel(AttnArgs a) {
   if (n_q < N) {
     float* po = a.part_o + (pbase + n_q) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lg) = o[dt];
+    // (written once and read once by the merge: non-temporal both ways, measured 1-4% faster
+    // launches on the split plans)
+    for (int dt = 0; dt < DT; ++dt) __builtin_nontemporal_store(o[dt], reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lg));
     if (lg == 0) {
       a.part_ml[(pbase + n_q) * 2 + 0] = M;
       a.part_ml[(pbase + n_q) * 2 + 1] = lsum;
@@ -945,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
     const size_t row = (bh + s) * a.npad + n;
     const float w = tv::exp2_fast(a.part_ml[row * 2] - Mu);
     l += w * a.part_ml[row * 2 + 1];
-    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + row * a.D + 4 * d4);
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.part_o + row * a.D + 4 * d4));
     acc[0] += w * x[0]; acc[1] += w * x[1]; acc[2] += w * x[2]; acc[3] += w * x[3];
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
