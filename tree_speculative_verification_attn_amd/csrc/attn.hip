@@ -21,7 +21,8 @@
 // merges with log-sum-exp weights.
 //
 // bf16 path (matrix cores): K/V stages of 32 keys go HBM -> LDS with
-// direct-to-LDS loads; three independent 4-wave groups per workgroup each
+// direct-to-LDS loads that carry the non-temporal hint (each K/V byte is read
+// once, so it should not displace cached lines); three independent 4-wave groups per workgroup each
 // run a two-buffer ring (48 KB of loads in flight per CU) and take the
 // chunk's stages in turn, so every call sums in the same order.  Within a group, wave w < ceil(N/16) owns query
 // tile w and keeps its running max, sum and O in registers.  Per 32 keys:
